@@ -1,0 +1,251 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = the whole path on the two workloads the metric is quoted on:
+  chunk: one 4,096-row prompt chunk on a 65,536-token cached prefix (69,632
+         keys), 4 key heads x 16 query heads: index scores -> block
+         selection -> msa_prefill;
+  long:  one decode row at 262,144 keys, 4 key heads x 16 query heads:
+         index scores -> block selection -> msa_decode (split-K + combine).
+value = rows per second of the step (4,097 rows).  Inputs are resident in HBM
+before timing; the timed region enqueues K steps back to back, bracketed by a
+device synchronisation on both sides.  Inputs rotate over replicas so the
+256 MB Infinity Cache cannot hold a whole step's working set.
+
+Every library call is bracketed by HIP events recorded on the stream the
+library launches on (torch's current stream), so per-kernel average durations
+come from the same timed region; the dominant kernel's duration gives the
+roofline entry.  The oracle (CPU) is timed on a bounded sample of the same
+workloads as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA prefill rows/s + decode rows/s at 64K–256K ctx; % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def algorithmic_work(case):
+    """Per-launch algorithmic FLOPs and bytes of each step for one workload."""
+    import numpy as np
+    H, G, D, dI, B, k = case.n_kv_heads, case.group, case.head_dim, case.index_dim, case.block, case.top_k
+    pairs = 0           # causal (row, key) pairs per key head
+    kept = 0            # kept visible keys per key head
+    for L, n in zip(case.seq_lens, case.rows):
+        p = np.arange(L - n, L, dtype=np.int64)
+        pairs += int((p + 1).sum())
+        nb = p // B + 1
+        full = np.minimum(nb, k) - 1                         # kept blocks other than the local one
+        kept += int((full * B + (p % B) + 1).sum())
+    rows = case.total_rows
+    nbk = -(-case.max_seq_len // B)
+    keys = case.total_keys
+    ik_heads = case.ik.shape[1]
+    w = {}
+    w["index_scores"] = dict(
+        flops=2 * dI * pairs * H,
+        bytes=keys * ik_heads * dI * 2 + rows * H * dI * 2 + rows * H * nbk * 4)
+    w["select_blocks"] = dict(flops=0, bytes=rows * H * nbk * 4 + rows * H * k * 4)
+    attn_bytes = rows * H * G * D * 2 * 2 + rows * H * k * 4     # q in, out
+    # kept K/V blocks, counted once per distinct (sequence, key head, block)
+    attn_bytes += kept_kv_bytes(case)
+    w["attention"] = dict(flops=4 * D * kept * H * G, bytes=attn_bytes)
+    return w
+
+
+def kept_kv_bytes(case):
+    """Distinct K/V bytes a perfect cache would read: for the chunk every
+    block below its last row is kept by some row, so K and V are read whole;
+    for a single row, its 16 blocks."""
+    total = 0
+    B, k = case.block, case.top_k
+    for L, n in zip(case.seq_lens, case.rows):
+        nb_last = (L - 1) // B + 1
+        blocks = nb_last if n >= 64 else min(nb_last, k * n)
+        total += blocks * B * case.head_dim * 2 * 2 * case.n_kv_heads
+    return total
+
+
+class Timed:
+    """Collects HIP-event pairs around library calls on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.ev.setdefault(name, []).append((a, b))
+
+    def mean_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.ev.items()}
+
+
+def cpu_baseline(cases, threads):
+    """Time the oracle as it stands on a bounded sample: 96 rows of the chunk
+    and the decode row; scale to rows/s of the full step."""
+    import numpy as np
+    import oracle
+    chunk, long_ = cases["chunk"], cases["long"]
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(chunk.total_rows, 96, replace=False))
+    t0 = time.perf_counter()
+    oracle.run(chunk, rows=sample, threads=threads)
+    t_chunk_row = (time.perf_counter() - t0) / len(sample)
+    t0 = time.perf_counter()
+    oracle.run(long_, threads=threads)
+    t_long = time.perf_counter() - t0
+    step = t_chunk_row * chunk.total_rows + t_long
+    return {"value": (chunk.total_rows + long_.total_rows) / step, "unit": "rows/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"96 random rows of the 4,096-row chunk ({t_chunk_row * 1e3:.1f} ms/row) and the "
+                      f"262,144-key decode row ({t_long * 1e3:.0f} ms); step time extrapolated to "
+                      f"4,096 + 1 rows = {step:.1f} s",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding by key head is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_04_amd as msa
+    from workloads import config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    cases = {"chunk": config("chunk"), "long": config("long")}
+    reps = {"chunk": 2, "long": 4}       # replicas: >= 512 MB rotated per workload
+    modes = {"chunk": "prefill", "long": "decode"}
+    state = {}
+    for name, case in cases.items():
+        base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(reps[name] - 1)]
+        shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
+        batch = msa.Batch(case.seq_lens, case.rows, device=dev)
+        outs = msa.run_path(shape, batch, inputs[0], modes[name])
+        state[name] = (shape, batch, inputs, outs)
+    torch.cuda.synchronize()
+
+    timer = Timed(torch)
+
+    def step(i, timed):
+        for name in ("chunk", "long"):
+            shape, batch, inputs, o = state[name]
+            t = inputs[i % len(inputs)]
+            calls = [
+                ("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])),
+                ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"])),
+            ]
+            if modes[name] == "prefill":
+                calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"],
+                                                                   o["block_idx"], o["out"], o["lse"])))
+            else:
+                calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"],
+                                                                  o["block_idx"], o["out"], o["lse"],
+                                                                  o["workspace"])))
+            for kname, fn in calls:
+                if timed:
+                    timer.run(f"{name}/{kname}", fn)
+                else:
+                    fn()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    rows = sum(c.total_rows for c in cases.values())
+    kms = timer.mean_ms()
+
+    kernels = []
+    for name, case in cases.items():
+        work = algorithmic_work(case)
+        for kname in ("index_scores", "select_blocks", "attention"):
+            ms = kms[f"{name}/{kname}"]
+            wk = work[kname]
+            bound = "mfma" if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm"
+            if bound == "mfma":
+                ach = wk["flops"] / (ms * 1e-3) / 1e12
+                ent = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+            else:
+                ach = wk["bytes"] / (ms * 1e-3) / 1e9
+                ent = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s")
+            ent["frac"] = ent["achieved"] / ent["peak"]
+            ent.update(kernel=f"{name}/{kname}", ms=ms, algorithmic_flops=wk["flops"],
+                       algorithmic_bytes=wk["bytes"])
+            kernels.append(ent)
+    dom = max(kernels, key=lambda e: e["ms"])
+    roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline.update(kernel=dom["kernel"], traffic=None)
+
+    t_chunk = sum(kms[f"chunk/{k}"] for k in ("index_scores", "select_blocks", "attention"))
+    t_long = sum(kms[f"long/{k}"] for k in ("index_scores", "select_blocks", "attention"))
+    res = {
+        "metric": METRIC,
+        "value": rows / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunked prefill (1 seq, 4,096 rows on a 65,536-key prefix, 69,632 keys) "
+                               "+ long decode (1 row at 262,144 keys); 4 key heads x 16 query heads, "
+                               "head_dim 128, index_dim 64, block 64, top-16 incl. local block",
+                   "rows_per_step": rows, "kv_heads": 4, "q_heads": 64},
+        "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
+        "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cases, args.cpu_threads)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+"""Python binding of libmsa.so, the MI355X block-sparse attention (MSA) library.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  The
+functions carry the C ABI's names (include/msa.h) and take torch tensors for
+device memory; PyTorch supplies memory and the current stream.  If the
+library is not built, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # loads the HIP runtime the library binds to
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsa.so")
+
+GROUP, HEAD_DIM, INDEX_DIM, BLOCK = 16, 128, 64, 64
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"msa status {status}: {detail}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _BatchC(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("total_rows", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("cu_rows", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("kv_start", ctypes.c_void_p)]
+
+
+EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode",
+           "msa_decode_workspace_bytes", "msa_status_string", "msa_last_error", "msa_version")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            SP, BP = ctypes.POINTER(Shape), ctypes.POINTER(_BatchC)
+            L.msa_index_scores.argtypes = [SP, BP, vp, vp, i64, i64, vp, i32, vp]
+            L.msa_select_blocks.argtypes = [SP, BP, vp, i32, vp, vp]
+            L.msa_prefill.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp]
+            L.msa_decode.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            for n in ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode"):
+                getattr(L, n).restype = ctypes.c_int
+            L.msa_decode_workspace_bytes.argtypes = [SP, i32]
+            L.msa_decode_workspace_bytes.restype = ctypes.c_size_t
+            L.msa_status_string.argtypes = [ctypes.c_int]
+            L.msa_status_string.restype = ctypes.c_char_p
+            L.msa_last_error.argtypes = []
+            L.msa_last_error.restype = ctypes.c_char_p
+            L.msa_version.argtypes = []
+            L.msa_version.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def make_shape(n_kv_heads: int, top_k: int = 16, scale: float | None = None) -> Shape:
+    return Shape(n_kv_heads, GROUP, HEAD_DIM, INDEX_DIM, BLOCK, top_k,
+                 (1.0 / HEAD_DIM ** 0.5) if scale is None else scale)
+
+
+class Batch:
+    """A ragged batch: host sizes plus device arrays (kept alive here).
+    Sequence s has seq_lens[s] keys and rows[s] query rows, its last positions;
+    its keys start at token kv_start[s] (default: packed back to back)."""
+
+    def __init__(self, seq_lens, rows, device="cuda", kv_start=None):
+        seq_lens = [int(x) for x in seq_lens]
+        rows = [int(x) for x in rows]
+        cu = [0]
+        for n in rows:
+            cu.append(cu[-1] + n)
+        if kv_start is None:
+            kv_start, acc = [], 0
+            for n in seq_lens:
+                kv_start.append(acc)
+                acc += n
+        self.seq_lens, self.rows, self.kv_start_host = seq_lens, rows, list(kv_start)
+        self.n_seqs, self.total_rows = len(seq_lens), cu[-1]
+        self.max_rows = max(rows) if rows else 0
+        self.max_seq_len = max(seq_lens) if seq_lens else 0
+        self.cu_rows = torch.tensor(cu, dtype=torch.int32, device=device)
+        self.seq_lens_d = torch.tensor(seq_lens or [0], dtype=torch.int32, device=device)
+        self.kv_start = torch.tensor(list(kv_start) or [0], dtype=torch.int64, device=device)
+        self.c = _BatchC(self.n_seqs, self.total_rows, self.max_rows, self.max_seq_len,
+                         self.cu_rows.data_ptr(), self.seq_lens_d.data_ptr(), self.kv_start.data_ptr())
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.max_seq_len // BLOCK)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc: int):
+    if rc != 0:
+        L = lib()
+        raise MsaError(rc, f"{L.msa_status_string(rc).decode()}: {L.msa_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name, contiguous=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _strides_tok_head(t, name):
+    """(token stride, head stride) of a [tokens, heads, dim] view; a single
+    head (or a stride-0 broadcast) gives head stride 0 (shared)."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [tokens, heads, dim] with a contiguous dim axis")
+    head = 0 if t.shape[1] == 1 else t.stride(1)
+    return t.stride(0), head
+
+
+def msa_index_scores(shape: Shape, batch: Batch, iq, ik, block_scores, stream=None):
+    _need(iq, torch.bfloat16, "iq")
+    _need(ik, torch.bfloat16, "ik", contiguous=False)
+    _need(block_scores, torch.float32, "block_scores")
+    tok, head = _strides_tok_head(ik, "ik")
+    _check(lib().msa_index_scores(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(iq), _ptr(ik),
+                                  tok, head, _ptr(block_scores), block_scores.shape[-1],
+                                  _stream(stream)))
+
+
+def msa_select_blocks(shape: Shape, batch: Batch, block_scores, block_idx, stream=None):
+    _need(block_scores, torch.float32, "block_scores")
+    _need(block_idx, torch.int32, "block_idx")
+    _check(lib().msa_select_blocks(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(block_scores),
+                                   block_scores.shape[-1], _ptr(block_idx), _stream(stream)))
+
+
+def msa_prefill(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(v, torch.bfloat16, "v", contiguous=False)
+    tok, head = _strides_tok_head(k, "k")
+    if _strides_tok_head(v, "v") != (tok, head):
+        raise ValueError("k and v must share strides")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().msa_prefill(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), _ptr(k), _ptr(v),
+                             tok, head, _ptr(block_idx), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def msa_decode_workspace_bytes(shape: Shape, total_rows: int) -> int:
+    return int(lib().msa_decode_workspace_bytes(ctypes.byref(shape), int(total_rows)))
+
+
+def msa_decode(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, workspace=None,
+               stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(v, torch.bfloat16, "v", contiguous=False)
+    tok, head = _strides_tok_head(k, "k")
+    if _strides_tok_head(v, "v") != (tok, head):
+        raise ValueError("k and v must share strides")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    nbytes = msa_decode_workspace_bytes(shape, batch.total_rows)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), _ptr(k), _ptr(v),
+                            tok, head, _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: dict | None = None,
+             stream=None) -> dict:
+    """Enqueue the whole path -- index scores, selection, attention -- on
+    device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
+    Output buffers are allocated unless given in `out`."""
+    out = {} if out is None else out
+    dev = t["q"].device
+    H, rows, nb = shape.n_kv_heads, batch.total_rows, batch.n_blocks
+    if "block_scores" not in out:
+        out["block_scores"] = torch.empty(rows, H, nb, dtype=torch.float32, device=dev)
+    if "block_idx" not in out:
+        out["block_idx"] = torch.empty(rows, H, shape.top_k, dtype=torch.int32, device=dev)
+    if "out" not in out:
+        out["out"] = torch.empty_like(t["q"])
+    if "lse" not in out:
+        out["lse"] = torch.empty(rows, H * GROUP, dtype=torch.float32, device=dev)
+    msa_index_scores(shape, batch, t["iq"], t["ik"], out["block_scores"], stream)
+    msa_select_blocks(shape, batch, out["block_scores"], out["block_idx"], stream)
+    if mode == "prefill":
+        msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
+    elif mode == "decode":
+        if "workspace" not in out:
+            out["workspace"] = torch.empty(max(msa_decode_workspace_bytes(shape, rows), 16),
+                                           dtype=torch.uint8, device=dev)
+        msa_decode(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"],
+                   out["workspace"], stream)
+    else:
+        raise ValueError(mode)
+    return out

@@ -1,0 +1,237 @@
+// api.hip -- the library's C ABI (include/msa.h): host-side validation, then
+// one launch sequence per entry point on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "msa.h"
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return MSA_OK;
+}
+
+int check_shape(const msa_shape *sh) {
+    if (!sh) return fail(MSA_ERR_INVALID, "shape is NULL");
+    if (sh->n_kv_heads < 1) return fail(MSA_ERR_INVALID, "n_kv_heads=%d must be >= 1", sh->n_kv_heads);
+    if (sh->n_kv_heads > 4096) return fail(MSA_ERR_UNSUPPORTED, "n_kv_heads=%d > 4096", sh->n_kv_heads);
+    if (sh->group != msa::kGroup || sh->head_dim != msa::kHeadDim || sh->index_dim != msa::kIndexDim ||
+        sh->block != msa::kBlock)
+        return fail(MSA_ERR_UNSUPPORTED,
+                    "group=%d head_dim=%d index_dim=%d block=%d: only 16/128/64/64 are built",
+                    sh->group, sh->head_dim, sh->index_dim, sh->block);
+    if (sh->top_k < 1 || sh->top_k > msa::kMaxTopK)
+        return fail(MSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", sh->top_k, msa::kMaxTopK);
+    if (!(sh->scale > 0.f) || !isfinite(sh->scale))
+        return fail(MSA_ERR_INVALID, "scale must be finite and > 0");
+    return MSA_OK;
+}
+
+// Returns MSA_OK with *empty set when there is nothing to do.
+int check_batch(const msa_batch *b, const msa_shape *sh, bool *empty) {
+    if (!b) return fail(MSA_ERR_INVALID, "batch is NULL");
+    if (b->n_seqs < 0 || b->total_rows < 0 || b->max_rows < 0 || b->max_seq_len < 0)
+        return fail(MSA_ERR_INVALID, "negative batch size field");
+    *empty = b->n_seqs == 0;
+    if (*empty) {
+        if (b->total_rows != 0) return fail(MSA_ERR_INVALID, "n_seqs=0 but total_rows=%d", b->total_rows);
+        return MSA_OK;
+    }
+    if (!b->cu_rows || !b->seq_lens || !b->kv_start)
+        return fail(MSA_ERR_INVALID, "batch device arrays must not be NULL");
+    if (b->max_rows < 1 || b->max_seq_len < 1 || b->total_rows < b->n_seqs)
+        return fail(MSA_ERR_INVALID, "every sequence needs >= 1 row and >= 1 key");
+    if (b->max_rows > b->max_seq_len)
+        return fail(MSA_ERR_INVALID, "max_rows=%d > max_seq_len=%d", b->max_rows, b->max_seq_len);
+    if ((int64_t)b->max_rows * b->n_seqs < b->total_rows)
+        return fail(MSA_ERR_INVALID, "total_rows exceeds n_seqs * max_rows");
+    if ((int64_t)b->n_seqs * sh->n_kv_heads > 65535)
+        return fail(MSA_ERR_UNSUPPORTED, "n_seqs * n_kv_heads > 65535");
+    if ((int64_t)b->total_rows * sh->n_kv_heads * 8 > 0x7fffffffLL)
+        return fail(MSA_ERR_UNSUPPORTED, "total_rows * n_kv_heads too large for one launch");
+    return MSA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MSA_ERR_HIP, "no usable HIP device: %s", hipGetErrorString(e));
+    return MSA_OK;
+}
+
+msa::BatchDev to_dev(const msa_batch *b) {
+    msa::BatchDev d;
+    d.n_seqs = b->n_seqs;
+    d.total_rows = b->total_rows;
+    d.max_rows = b->max_rows;
+    d.max_seq_len = b->max_seq_len;
+    d.cu_rows = b->cu_rows;
+    d.seq_lens = b->seq_lens;
+    d.kv_start = b->kv_start;
+    return d;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MSA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int check_kv(const void *k, const void *v, int64_t tok, int64_t head, int n_kv_heads) {
+    if (!k || !v) return fail(MSA_ERR_INVALID, "k/v must not be NULL");
+    if (tok < msa::kHeadDim || head < 0 || (n_kv_heads > 1 && head < msa::kHeadDim))
+        return fail(MSA_ERR_INVALID, "kv strides (%lld, %lld) overlap a %d-element row",
+                    (long long)tok, (long long)head, msa::kHeadDim);
+    if (!aligned16(k) || !aligned16(v) || (tok * 2) % 16 || (head * 2) % 16)
+        return fail(MSA_ERR_INVALID, "k/v rows must be 16-byte aligned");
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_version(void) { return "msa-mi355x 0.1 (gfx950)"; }
+
+const char *msa_last_error(void) { return g_last_error; }
+
+const char *msa_status_string(int status) {
+    switch (status) {
+        case MSA_OK: return "ok";
+        case MSA_ERR_INVALID: return "invalid argument";
+        case MSA_ERR_UNSUPPORTED: return "unsupported shape";
+        case MSA_ERR_WORKSPACE: return "workspace too small";
+        case MSA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int msa_index_scores(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
+                     int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores,
+                     int32_t bs_stride, void *stream) {
+    int rc;
+    bool empty;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
+    if (empty) return ok();
+    if (!iq || !ik || !block_scores) return fail(MSA_ERR_INVALID, "iq/ik/block_scores must not be NULL");
+    if (ik_tok_stride < msa::kIndexDim || ik_head_stride < 0 ||
+        (ik_head_stride > 0 && ik_head_stride < msa::kIndexDim))
+        return fail(MSA_ERR_INVALID, "ik strides (%lld, %lld) overlap a %d-element row",
+                    (long long)ik_tok_stride, (long long)ik_head_stride, msa::kIndexDim);
+    if (!aligned16(iq) || !aligned16(ik) || (ik_tok_stride * 2) % 16 || (ik_head_stride * 2) % 16)
+        return fail(MSA_ERR_INVALID, "iq/ik rows must be 16-byte aligned");
+    const int64_t need = ((int64_t)batch->max_seq_len + msa::kBlock - 1) / msa::kBlock;
+    if (bs_stride < need)
+        return fail(MSA_ERR_INVALID, "bs_stride=%d < ceil(max_seq_len/64)=%lld", bs_stride, (long long)need);
+    if ((rc = check_device())) return rc;
+    msa::IndexArgs a;
+    a.b = to_dev(batch);
+    a.H = shape->n_kv_heads;
+    a.iq = static_cast<const uint16_t *>(iq);
+    a.ik = static_cast<const uint16_t *>(ik);
+    a.ik_tok = ik_tok_stride;
+    a.ik_head = ik_head_stride;
+    a.scores = block_scores;
+    a.bs_stride = bs_stride;
+    return launched(msa::launch_index_scores(a, static_cast<hipStream_t>(stream)), "index_scores");
+}
+
+int msa_select_blocks(const msa_shape *shape, const msa_batch *batch, const float *block_scores,
+                      int32_t bs_stride, int32_t *block_idx, void *stream) {
+    int rc;
+    bool empty;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
+    if (empty) return ok();
+    if (!block_scores || !block_idx) return fail(MSA_ERR_INVALID, "block_scores/block_idx must not be NULL");
+    const int64_t need = ((int64_t)batch->max_seq_len + msa::kBlock - 1) / msa::kBlock;
+    if (bs_stride < need)
+        return fail(MSA_ERR_INVALID, "bs_stride=%d < ceil(max_seq_len/64)=%lld", bs_stride, (long long)need);
+    if ((rc = check_device())) return rc;
+    msa::SelectArgs a;
+    a.b = to_dev(batch);
+    a.H = shape->n_kv_heads;
+    a.top_k = shape->top_k;
+    a.scores = block_scores;
+    a.bs_stride = bs_stride;
+    a.idx = block_idx;
+    return launched(msa::launch_select_blocks(a, static_cast<hipStream_t>(stream)), "select_blocks");
+}
+
+static int attn_common(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
+                       const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
+                       const int32_t *block_idx, void *out, float *lse, msa::AttnArgs *a, bool *empty) {
+    int rc;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, empty))) return rc;
+    if (*empty) return MSA_OK;
+    if (!q || !block_idx || !out) return fail(MSA_ERR_INVALID, "q/block_idx/out must not be NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(MSA_ERR_INVALID, "q/out must be 16-byte aligned");
+    if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, shape->n_kv_heads))) return rc;
+    a->b = to_dev(batch);
+    a->H = shape->n_kv_heads;
+    a->top_k = shape->top_k;
+    a->scale_log2 = shape->scale * msa::kLog2e;
+    a->q = static_cast<const uint16_t *>(q);
+    a->k = static_cast<const uint16_t *>(k);
+    a->v = static_cast<const uint16_t *>(v);
+    a->kv_tok = kv_tok_stride;
+    a->kv_head = kv_head_stride;
+    a->idx = block_idx;
+    a->out = static_cast<uint16_t *>(out);
+    a->lse = lse;
+    a->ws = nullptr;
+    return MSA_OK;
+}
+
+int msa_prefill(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
+                const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
+                void *out, float *lse, void *stream) {
+    msa::AttnArgs a;
+    bool empty = false;
+    int rc = attn_common(shape, batch, q, k, v, kv_tok_stride, kv_head_stride, block_idx, out, lse, &a,
+                         &empty);
+    if (rc) return rc;
+    if (empty) return ok();
+    if ((rc = check_device())) return rc;
+    return launched(msa::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill");
+}
+
+size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows) {
+    if (!shape || check_shape(shape) || total_rows < 0) return 0;
+    return (size_t)total_rows * shape->n_kv_heads * msa::decode_splits(shape->top_k) *
+           msa::kPartialFloats * sizeof(float);
+}
+
+int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
+               const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
+               void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    msa::AttnArgs a;
+    bool empty = false;
+    int rc = attn_common(shape, batch, q, k, v, kv_tok_stride, kv_head_stride, block_idx, out, lse, &a,
+                         &empty);
+    if (rc) return rc;
+    if (empty) return ok();
+    const size_t need = msa_decode_workspace_bytes(shape, batch->total_rows);
+    if (!workspace || workspace_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(MSA_ERR_INVALID, "workspace must be 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    a.ws = static_cast<float *>(workspace);
+    return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+}  // extern "C"

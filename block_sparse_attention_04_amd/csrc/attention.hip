@@ -1,0 +1,345 @@
+// attention.hip -- exact softmax attention over the kept blocks.
+//
+// For query head h of key head g = h / 16 and a row at position p:
+//   out[h] = sum_j softmax_j(scale * q[h].k[j]) v[j]  over the kept blocks'
+//   keys j <= p;  lse[h] = log sum_j exp(scale * q[h].k[j]).
+// The 16 query heads of a key head share the row's selection, so a wave holds
+// all 16 heads of one (row, key head) and reads every kept key/value once for
+// all of them (TensorFold pull request 1388, commit on 4,096-row prompt
+// chunks).  Decode splits the kept keys into 32-key partials merged by a
+// log-sum-exp combine (same pull request, commit adding the minimax_m3
+// family).
+//
+// Per 32-key chunk, on v_mfma_f32_16x16x32_bf16:
+//   S^T[key][head] = K Q^T      2 key tiles x 4 k-steps over the 128 dims
+//   O^T[d][head]  += V^T P^T    8 d-tiles x one 32-key k-step
+// With S^T, a lane holds one head's scores for 8 keys, which is exactly the
+// P^T operand layout of the second product, so probabilities go from the
+// softmax straight into the MFMA without leaving registers, and the running
+// max / sum / rescale of a head stay inside its 4 lanes.  V is written to LDS
+// transposed (d-major, keys permuted to the lanes' k-slot order, 16-byte
+// groups XOR-swizzled) so each V^T operand is one conflict-free 16-byte read.
+// Softmax runs in base 2 on scale*log2(e)-prescaled scores.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+struct Softmax {
+    floatx4 o[8];   // O^T: head (lane % 16), d = 16*dt + 4*(lane/16) + i
+    float m;        // running max (log2 units); equal on the 4 lanes of a head
+    float l;        // this lane's share of the running sum
+};
+
+__device__ __forceinline__ void softmax_init(Softmax &st) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+}
+
+// Byte offset of 16-byte group `grp` (of 4) in row d of the transposed V tile.
+__device__ __forceinline__ int vt_offset(int d, int grp) {
+    return d * 64 + ((grp ^ (((d >> 2) ^ (d >> 4)) & 3)) << 4);
+}
+
+// Query B operand: head (lane % 16), dims 32*(lane/16) + 8*s + (0..7).
+__device__ __forceinline__ void load_q(u32x4 (&qb)[4], const uint16_t *qrow_head0) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t *src = qrow_head0 + (lane & 15) * kHeadDim + 32 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[s] = load16(src + 8 * s);
+}
+
+// Fold the 32 keys [kbase, kbase + 32) of one sequence (those <= p) into st.
+// kseq/vseq point at key 0 of the sequence for this key head; vt is this
+// wave's 8 KiB LDS tile.
+__device__ __forceinline__ void attend_chunk32(Softmax &st, const u32x4 (&qb)[4],
+                                               const uint16_t *kseq, const uint16_t *vseq,
+                                               int64_t tok, int kbase, int p, float scale_log2,
+                                               uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+
+    // K operands: key kbase + 16*mt + lr, dims 32*lg + 8*s.
+    u32x4 ka[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int key = kbase + 16 * mt + lr;
+        if (key <= p) {
+            const uint16_t *src = kseq + (int64_t)key * tok + 32 * lg;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ka[mt][s] = load16(src + 8 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ka[mt][s] = zero16();
+        }
+    }
+    // V rows: keys kbase + 4*kg + (0..3), dims 16*dc + (0..15).
+    const int kg = lane >> 3, dc = lane & 7;
+    u32x4 vr[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int key = kbase + 4 * kg + kk;
+        if (key <= p) {
+            const uint16_t *src = vseq + (int64_t)key * tok + 16 * dc;
+            vr[kk][0] = load16(src);
+            vr[kk][1] = load16(src + 8);
+        } else {
+            vr[kk][0] = zero16();
+            vr[kk][1] = zero16();
+        }
+    }
+
+    floatx4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c = mfma_16x16x32(ka[mt][s], qb[s], c);
+        sacc[mt] = c;
+    }
+
+    // V^T into LDS.  Key k of the chunk goes to slot 8*((k%16)/4) + 4*(k/16) + k%4,
+    // so lane group lg's k-slots (keys 4lg..4lg+3 and 16+4lg..16+4lg+3) are
+    // the 8 contiguous slots of group lg.  Keys 4kg..4kg+3 share one 8-byte
+    // word per dim.
+    const int grp = kg & 3, half = kg >> 2;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int reg = t >> 3, dw = (t & 7) >> 1;
+        uint32_t w0, w1;
+        if (t & 1) {
+            w0 = (vr[0][reg][dw] >> 16) | (vr[1][reg][dw] & 0xffff0000u);
+            w1 = (vr[2][reg][dw] >> 16) | (vr[3][reg][dw] & 0xffff0000u);
+        } else {
+            w0 = (vr[0][reg][dw] & 0xffffu) | (vr[1][reg][dw] << 16);
+            w1 = (vr[2][reg][dw] & 0xffffu) | (vr[3][reg][dw] << 16);
+        }
+        const int d = 16 * dc + t;
+        *reinterpret_cast<uint2 *>(vt + vt_offset(d, grp) + 8 * half) = make_uint2(w0, w1);
+    }
+
+    // Online softmax over this lane's 8 keys of head lr.
+    float z[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = sacc[mt][i] * scale_log2;
+            if (kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
+            z[mt][i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = max_over_lane_groups(mx);
+    const float m_new = fmaxf(st.m, mx);        // finite: key kbase <= p is visible
+    const float alpha = exp2f(st.m - m_new);    // 0 on the first chunk
+    float pr[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[mt][i] = exp2f(z[mt][i] - m_new);
+            psum += pr[mt][i];
+        }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                      pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const u32x4 va = *reinterpret_cast<const u32x4 *>(vt + vt_offset(16 * dt + lr, lg));
+        st.o[dt] = mfma_16x16x32(va, pb, st.o[dt]);
+    }
+    wave_lds_sync();   // reads finish before the next chunk overwrites the tile
+}
+
+// Unit (row r, key head g) of a head-major enumeration: consecutive units are
+// consecutive rows of one key head, so neighbouring waves share local blocks.
+struct Unit {
+    int r, g, s, p;
+    bool ok;
+};
+
+__device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
+    Unit u;
+    u.g = (int)(unit / a.b.total_rows);
+    u.r = (int)(unit % a.b.total_rows);
+    u.s = locate_seq(a.b.cu_rows, a.b.n_seqs, u.r);
+    const int rows_s = a.b.cu_rows[u.s + 1] - a.b.cu_rows[u.s];
+    const int L = a.b.seq_lens[u.s];
+    u.ok = rows_s > 0 && rows_s <= L && L <= a.b.max_seq_len;
+    u.p = L - rows_s + (u.r - a.b.cu_rows[u.s]);
+    return u;
+}
+
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
+    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+    const Unit u = make_unit(a, unit);
+    if (!u.ok) return;
+
+    const int hq = a.H * kGroup;
+    const int64_t kv0 = a.b.kv_start[u.s];
+    const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+    const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+    u32x4 qb[4];
+    load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+    const int32_t *sel = a.idx + ((int64_t)u.r * a.H + u.g) * a.top_k;
+    const int my_b = lane < a.top_k ? sel[lane] : -1;
+
+    Softmax st;
+    softmax_init(st);
+    for (int t = 0; t < a.top_k; ++t) {
+        const int b = __builtin_amdgcn_readlane(my_b, t);
+        if (b < 0 || b * kBlock > u.p) continue;
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {
+            const int kbase = b * kBlock + 32 * half;
+            if (kbase > u.p) break;
+            attend_chunk32(st, qb, kseq, vseq, a.kv_tok, kbase, u.p, a.scale_log2, vt_all[wave]);
+        }
+    }
+
+    const float l = sum_over_lane_groups(st.l);
+    const int h = u.g * kGroup + lr;
+    uint16_t *dst = a.out + ((int64_t)u.r * hq + h) * kHeadDim + 4 * lg;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const uint2 w = make_uint2(pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv),
+                                   pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv));
+        *reinterpret_cast<uint2 *>(dst + 16 * dt) = w;
+    }
+    if (a.lse && lg == 0) a.lse[(int64_t)u.r * hq + h] = l > 0.f ? (st.m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Decode: workgroup (unit, split) = 4 waves; wave w folds 32-key chunk
+// 4*split + w of the unit's kept list (block slot chunk/2, half chunk%2); the
+// workgroup merges its 4 pieces in LDS in wave order and writes one partial.
+__global__ __launch_bounds__(256) void decode_partial_kernel(AttnArgs a, int n_split) {
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    __shared__ float mrg[kDecodeWaves][34][kWave];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int64_t unit = blockIdx.x / n_split;
+    const int split = blockIdx.x % n_split;
+    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+    const Unit u = make_unit(a, unit);
+
+    Softmax st;
+    softmax_init(st);
+    const int chunk = split * kDecodeWaves + wave;
+    const int slot = chunk >> 1, half = chunk & 1;
+    if (u.ok && slot < a.top_k) {
+        const int b = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
+        const int kbase = b * kBlock + 32 * half;
+        if (b >= 0 && kbase <= u.p) {
+            const int64_t kv0 = a.b.kv_start[u.s];
+            u32x4 qb[4];
+            load_q(qb, a.q + ((int64_t)u.r * a.H * kGroup + u.g * kGroup) * kHeadDim);
+            attend_chunk32(st, qb, a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head,
+                           a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head, a.kv_tok, kbase, u.p,
+                           a.scale_log2, vt_all[wave]);
+        }
+    }
+    const float l = sum_over_lane_groups(st.l);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mrg[wave][4 * dt + i][lane] = st.o[dt][i];
+    mrg[wave][32][lane] = st.m;
+    mrg[wave][33][lane] = l;
+    __syncthreads();
+    if (wave != 0) return;
+
+    float mw[kDecodeWaves], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+        mw[w] = mrg[w][32][lane];
+        M = fmaxf(M, mw[w]);
+    }
+    float scl[kDecodeWaves], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+        scl[w] = M == -INFINITY ? 0.f : exp2f(mw[w] - M);
+        Ls += scl[w] * mrg[w][33][lane];
+    }
+    float *part = a.ws + (unit * n_split + split) * (int64_t)kPartialFloats;
+    if (lg == 0) {
+        part[lr] = M;
+        part[16 + lr] = Ls;
+    }
+    float *acc = part + 32 + lr * kHeadDim + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] += scl[w] * mrg[w][4 * dt + i][lane];
+        *reinterpret_cast<floatx4 *>(acc + 16 * dt) = o;
+    }
+}
+
+// Combine the n_split partials of a unit: 256 threads, thread = (head, 8 dims).
+__global__ __launch_bounds__(256) void decode_combine_kernel(AttnArgs a, int n_split) {
+    const int64_t unit = blockIdx.x;
+    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+    const int g = (int)(unit / a.b.total_rows), r = (int)(unit % a.b.total_rows);
+    const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+    const float *part = a.ws + unit * n_split * (int64_t)kPartialFloats;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[s * kPartialFloats + h]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < n_split; ++s) {
+            const float *ps = part + s * kPartialFloats;
+            const float w = exp2f(ps[h] - M);
+            Ls += w * ps[16 + h];
+            const floatx4 x0 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0);
+            const floatx4 x1 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0 + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += w * x0[i];
+                acc[4 + i] += w * x1[i];
+            }
+        }
+    }
+    const int hq = a.H * kGroup;
+    const int hh = g * kGroup + h;
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *reinterpret_cast<u32x4 *>(a.out + ((int64_t)r * hq + hh) * kHeadDim + d0) = w;
+    if (a.lse && d0 == 0) a.lse[(int64_t)r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
+    const int64_t units = (int64_t)a.b.total_rows * a.H;
+    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
+    const int64_t units = (int64_t)a.b.total_rows * a.H;
+    const int n_split = decode_splits(a.top_k);
+    hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)(units * n_split)), dim3(256), 0, st, a,
+                       n_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)units), dim3(256), 0, st, a, n_split);
+    return hipGetLastError();
+}
+
+}  // namespace msa

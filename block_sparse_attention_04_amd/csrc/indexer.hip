@@ -1,0 +1,255 @@
+// indexer.hip -- lightning-indexer scores max-pooled per 64-key block.
+//
+// S[r, g, b] = max over the causally visible keys j of block b of
+//              sum_d iq[r, g, d] * ik[j, g, d]
+// (TensorFold pull request 1388, commit adding the minimax_m3 family: index
+// scores per row and key head; "minimax-m3-sm120", What this fixes: blocks
+// are scored by max-pooling.  The plain dot product is this library's
+// reading of the unspecified score form.)
+//
+// The contraction runs on v_mfma_f32_16x16x32_bf16 with keys on the M axis and
+// query rows on the N axis (S^T = IK * IQ^T): each lane's accumulator then
+// holds 4 keys of one row, so the 64-key max-pool is 15 in-lane maxima and
+// two cross-lane steps, and no score ever leaves the registers.
+//
+// Two tilings of the same computation:
+//   index_scores_tiled  prompt chunks: a workgroup owns 256 rows x a key range;
+//                       each 64-key tile of ik is staged once in LDS (double
+//                       buffered) and reused by the 4 waves' 64 rows each.
+//   index_scores_window decode steps and windows (<= 16 rows per sequence):
+//                       the 16-row tile is the wave's whole row set, so ik is
+//                       streamed straight from HBM into MFMA operand registers
+//                       and the key axis is spread over the whole chip.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// k-assignment shared by both operands: k-step s, lane group lg -> index dims
+// 16*lg + 8*s + (0..7), i.e. each lane reads 32 contiguous bytes of a vector.
+
+// Block max of one 16-row x 64-key MFMA result (4 M-tiles), causal-masked
+// against the lane's row position when the block reaches past the wave's
+// first row.
+__device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0, int p_row,
+                                              bool need_mask) {
+    const int lg = (threadIdx.x & 63) >> 4;
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = acc[mt][i];
+            if (need_mask && key0 + 16 * mt + 4 * lg + i > p_row) v = -INFINITY;
+            m = fmaxf(m, v);
+        }
+    }
+    return max_over_lane_groups(m);
+}
+
+constexpr int kTiledWaves = 4;
+constexpr int kLdsRow = 144;   // bytes per staged key (128 + 16 pad: conflict-free b128 reads)
+
+template <int NT>
+__global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int blocks_per_wg) {
+    constexpr int kRowsWave = 16 * NT;
+    constexpr int kRowsWg = kRowsWave * kTiledWaves;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * kLdsRow];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
+    if (s >= a.b.n_seqs) return;
+    const int row0 = a.b.cu_rows[s];
+    const int rows_s = a.b.cu_rows[s + 1] - row0;
+    const int L = a.b.seq_lens[s];
+    if (rows_s <= 0 || rows_s > L || L > a.b.max_seq_len) return;
+    const int tile0 = blockIdx.y * kRowsWg;
+    if (tile0 >= rows_s) return;
+    const int tile_rows = min(kRowsWg, rows_s - tile0);
+    const int p_base = L - rows_s;                       // position of row 0 of the sequence
+    const int nb_tile = (p_base + tile0 + tile_rows - 1) / kBlock + 1;
+    const int b_begin = blockIdx.x * blocks_per_wg;
+    const int b_end = min(b_begin + blocks_per_wg, a.bs_stride);
+    if (b_begin >= b_end) return;
+    const int b_cmp_end = min(b_end, nb_tile);
+    const int64_t kv0 = a.b.kv_start[s];
+
+    // This wave's rows and their indexer queries (the B operand, kept in VGPRs).
+    const int wrow0 = tile0 + wave * kRowsWave;
+    u32x4 bq[NT][2];
+    int prow[NT];
+    bool rvalid[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rl = wrow0 + nt * 16 + lr;
+        rvalid[nt] = rl < rows_s;
+        prow[nt] = p_base + rl;
+        if (rvalid[nt]) {
+            const uint16_t *src = a.iq + ((int64_t)(row0 + rl) * a.H + g) * kIndexDim + 16 * lg;
+            bq[nt][0] = load16(src);
+            bq[nt][1] = load16(src + 8);
+        } else {
+            bq[nt][0] = zero16();
+            bq[nt][1] = zero16();
+        }
+    }
+    const int wave_p_min = p_base + wrow0;
+
+    // Staging: thread t copies 32 bytes (piece t&3) of key t>>2 of the tile.
+    const int st_key = threadIdx.x >> 2, st_piece = threadIdx.x & 3;
+    const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * st_piece;
+    u32x4 x0 = zero16(), x1 = zero16();
+    auto gload = [&](int b) {
+        const int j = b * kBlock + st_key;
+        if (j < L) {
+            const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
+            x0 = load16(src);
+            x1 = load16(src + 8);
+        } else {
+            x0 = zero16();
+            x1 = zero16();
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint8_t *dst = &lds[buf][st_key * kLdsRow + 32 * st_piece];
+        *reinterpret_cast<u32x4 *>(dst) = x0;
+        *reinterpret_cast<u32x4 *>(dst + 16) = x1;
+    };
+
+    if (b_begin < b_cmp_end) {
+        gload(b_begin);
+        sstore(0);
+    }
+    __syncthreads();
+
+    float held[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) held[nt] = -INFINITY;
+
+    for (int b = b_begin; b < b_end; ++b) {
+        float m[NT];
+        if (b < b_cmp_end) {
+            const int buf = (b - b_begin) & 1;
+            const bool more = b + 1 < b_cmp_end;
+            if (more) gload(b + 1);
+            floatx4 acc[NT][4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint8_t *src = &lds[buf][(16 * mt + lr) * kLdsRow + 32 * lg];
+                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(src);
+                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(src + 16);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                    c = mfma_16x16x32(a0, bq[nt][0], c);
+                    acc[nt][mt] = mfma_16x16x32(a1, bq[nt][1], c);
+                }
+            }
+            const bool need_mask = b * kBlock + kBlock - 1 > wave_p_min;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) m[nt] = block_max_64(acc[nt], b * kBlock, prow[nt], need_mask);
+            if (more) sstore(buf ^ 1);
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) m[nt] = -INFINITY;
+        }
+        // Lane group lg keeps the blocks with b % 4 == lg; every 4 blocks the
+        // wave writes 16 contiguous bytes per row.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            if (lg == (b & 3)) held[nt] = m[nt];
+        if ((b & 3) == 3 || b == b_end - 1) {
+            const int blk = (b & ~3) + lg;
+            if (blk >= b_begin && blk <= b) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (rvalid[nt])
+                        a.scores[((int64_t)(row0 + wrow0 + nt * 16 + lr) * a.H + g) * a.bs_stride + blk] =
+                            held[nt];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int blocks_per_wave) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
+    if (s >= a.b.n_seqs) return;
+    const int row0 = a.b.cu_rows[s];
+    const int rows_s = a.b.cu_rows[s + 1] - row0;
+    const int L = a.b.seq_lens[s];
+    if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;
+    const int b_begin = (blockIdx.x * 4 + wave) * blocks_per_wave;
+    const int b_end = min(b_begin + blocks_per_wave, a.bs_stride);
+    if (b_begin >= b_end) return;
+    const int nb_seq = (L - 1) / kBlock + 1;
+    const int b_cmp_end = min(b_end, nb_seq);
+    const int64_t kv0 = a.b.kv_start[s];
+
+    const bool rvalid = lr < rows_s;
+    const int p_first = L - rows_s;
+    const int prow = p_first + lr;
+    u32x4 bq0 = zero16(), bq1 = zero16();
+    if (rvalid) {
+        const uint16_t *src = a.iq + ((int64_t)(row0 + lr) * a.H + g) * kIndexDim + 16 * lg;
+        bq0 = load16(src);
+        bq1 = load16(src + 8);
+    }
+    const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
+
+    float held = -INFINITY;
+    for (int b = b_begin; b < b_end; ++b) {
+        float m = -INFINITY;
+        if (b < b_cmp_end) {
+            u32x4 av[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int j = b * kBlock + 16 * mt + lr;
+                if (j < L) {
+                    const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
+                    av[mt][0] = load16(src);
+                    av[mt][1] = load16(src + 8);
+                } else {
+                    av[mt][0] = zero16();
+                    av[mt][1] = zero16();
+                }
+            }
+            floatx4 acc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma_16x16x32(av[mt][0], bq0, c);
+                acc[mt] = mfma_16x16x32(av[mt][1], bq1, c);
+            }
+            m = block_max_64(acc, b * kBlock, prow, b * kBlock + kBlock - 1 > p_first);
+        }
+        if (lg == (b & 3)) held = m;
+        if ((b & 3) == 3 || b == b_end - 1) {
+            const int blk = (b & ~3) + lg;
+            if (rvalid && blk >= b_begin && blk <= b)
+                a.scores[((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk] = held;
+        }
+    }
+}
+
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
+    const int gz = a.b.n_seqs * a.H;
+    if (a.b.max_rows <= 16) {
+        const int bpw = 8;                       // blocks per wave (multiple of 4)
+        const int per_wg = bpw * 4;
+        dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, gz);
+        hipLaunchKernelGGL(index_scores_window, grid, dim3(256), 0, st, a, bpw);
+    } else {
+        constexpr int NT = 4;
+        const int rows_wg = 16 * NT * kTiledWaves;
+        const int bpwg = 16;                     // blocks per workgroup (multiple of 4)
+        dim3 grid((a.bs_stride + bpwg - 1) / bpwg, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
+        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, bpwg);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace msa

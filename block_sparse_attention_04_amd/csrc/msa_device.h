@@ -1,0 +1,91 @@
+// msa_device.h -- device-side helpers shared by the library's kernels
+// (gfx950 / CDNA4, wave64).  Library-internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace msa {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 16;      // query heads per key head
+constexpr int kHeadDim = 128;   // q/k/v head dim
+constexpr int kIndexDim = 64;   // indexer dim
+constexpr int kBlock = 64;      // keys per block
+constexpr int kMaxTopK = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// D = A * B + C on one 16x16x32 bf16 MFMA.
+// Lane layout (wave64): A supplies row (lane % 16) and the 8 k-values of
+// lane group (lane / 16); B supplies column (lane % 16) and the same 8
+// k-values of its lane group; D lane holds column (lane % 16), rows
+// 4*(lane/16) + 0..3.  A and B share the k assignment, so any consistent
+// relabelling of k across the two operands computes the same contraction.
+__device__ __forceinline__ floatx4 mfma_16x16x32(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ u32x4 zero16() {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return z;
+}
+
+// Sequence owning global row r: the last s with cu_rows[s] <= r.
+__device__ __forceinline__ int locate_seq(const int32_t *cu_rows, int n_seqs, int r) {
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu_rows[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Wave-wide reductions across the four lanes l, l^16, l^32, l^48 that share
+// a column of an MFMA result.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Make LDS writes of this wave visible to its own later LDS reads (and keep
+// the compiler from moving LDS accesses across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace msa

@@ -1,0 +1,59 @@
+// msa_launch.h -- library-internal kernel argument blocks and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct BatchDev {
+    int n_seqs, total_rows, max_rows, max_seq_len;
+    const int32_t *cu_rows;
+    const int32_t *seq_lens;
+    const int64_t *kv_start;
+};
+
+struct IndexArgs {
+    BatchDev b;
+    int H;                       // key heads
+    const uint16_t *iq;          // [total_rows, H, 64]
+    const uint16_t *ik;          // strided, dims contiguous
+    int64_t ik_tok, ik_head;     // element strides
+    float *scores;               // [total_rows, H, bs_stride]
+    int bs_stride;
+};
+
+struct SelectArgs {
+    BatchDev b;
+    int H, top_k;
+    const float *scores;
+    int bs_stride;
+    int32_t *idx;                // [total_rows, H, top_k]
+};
+
+struct AttnArgs {
+    BatchDev b;
+    int H, top_k;
+    float scale_log2;            // softmax scale * log2(e)
+    const uint16_t *q;           // [total_rows, H*16, 128]
+    const uint16_t *k, *v;       // strided, dims contiguous
+    int64_t kv_tok, kv_head;
+    const int32_t *idx;          // [total_rows, H, top_k]
+    uint16_t *out;               // [total_rows, H*16, 128]
+    float *lse;                  // [total_rows, H*16] or null
+    float *ws;                   // decode partials
+};
+
+// Decode split-K geometry: every wave owns 32 keys, a workgroup of 4 waves
+// merges its pieces into one partial; a partial is m[16], l[16], acc[16][128].
+constexpr int kDecodeWaves = 4;
+constexpr int kPartialFloats = 16 + 16 + 16 * 128;
+inline int decode_splits(int top_k) { return (top_k * 2 + kDecodeWaves - 1) / kDecodeWaves; }
+
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
+hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t st);
+hipError_t launch_decode(const AttnArgs &a, hipStream_t st);
+
+}  // namespace msa

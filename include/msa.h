@@ -1,0 +1,180 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax-M3 block-sparse attention
+ * (MSA) library, libmsa.so.
+ *
+ * The method, as the pages describe it in prose (no formulas are given):
+ *   - "minimax-m3-sm120" README, section "What this fixes": the MSA model
+ *     selects the top-16 blocks per GQA group, scores blocks by max-pooling
+ *     and always keeps the local block.
+ *   - TensorFold pull request 1388, commit adding the minimax_m3 family: the
+ *     lightning indexer produces index scores and a top-16 block selection
+ *     per row and key head; decode attends over the kept blocks in 32-key
+ *     partials; prompt chunks attend over each tile's kept blocks.
+ *   - same pull request, commit on 4,096-row prompt chunks: the 16 query heads
+ *     of one key head share that key head's selection, so each kept key/value
+ *     block is read once for all of them.
+ *
+ * Notation.  A ragged batch holds n_seqs sequences.  Sequence s has
+ * seq_lens[s] keys (every key visible to its last row, the rows' own keys
+ * included) and rows_s = cu_rows[s+1] - cu_rows[s] query rows, which are its
+ * LAST rows_s positions: row i sits at p = seq_lens[s] - rows_s + i.  Key j of
+ * the sequence (0-based) lives at token kv_start[s] + j of the key tensors and
+ * is visible to the row at p iff j <= p.  Blocks are `block` consecutive keys;
+ * the row's causal block count is nb = floor(p / block) + 1 and its local
+ * block is nb - 1.  Query head h belongs to key head floor(h / group).
+ *
+ * Steps (one entry point each, enqueued on the caller's stream):
+ *   msa_index_scores  S[r,g,b] = max_{j in block b, j <= p} sum_d iq[r,g,d]*ik[j,g,d]
+ *   msa_select_blocks the local block + the top_k-1 best other blocks by S
+ *                     (ties: lower block index), ascending, -1 padded
+ *   msa_prefill       exact softmax attention of the group's query heads over
+ *                     the kept blocks' visible keys (one pass per row)
+ *   msa_decode        the same result, split into 32-key partials that are
+ *                     merged with a log-sum-exp combine (for few rows)
+ *
+ * Dtypes: bf16 tensors are passed as raw 16-bit patterns (void*); scores and
+ * lse are fp32; indices int32.  Every pointer argument is DEVICE memory unless
+ * marked host.  Element strides are in elements, not bytes.
+ *
+ * Ownership and threading: the caller allocates and owns every buffer,
+ * including the decode workspace.  The library allocates nothing, keeps no
+ * state between calls, never synchronises the device and only enqueues work
+ * on `stream` (a hipStream_t; NULL is the default stream).  Calls are
+ * thread-safe.
+ *
+ * Errors: all host-visible arguments are validated before anything is
+ * enqueued; a failure returns a negative msa_status, enqueues nothing and sets
+ * the calling thread's msa_last_error() text.  A launch failure returns
+ * MSA_ERR_HIP.  Device-array contents are preconditions and are not checked
+ * on the host: 1 <= rows_s <= seq_lens[s] <= max_seq_len, rows_s <= max_rows,
+ * cu_rows non-decreasing with cu_rows[n_seqs] == total_rows, key ranges in
+ * bounds of the key tensors, and block_idx entries either -1 or a causal block
+ * of their row.  Kernels skip (do not fault on) rows and blocks that violate
+ * the row/length preconditions; their outputs are then unspecified.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_INVALID = -1,      /* null pointer, negative size, inconsistent sizes */
+    MSA_ERR_UNSUPPORTED = -2,  /* a shape this build has no kernel for */
+    MSA_ERR_WORKSPACE = -3,    /* decode workspace smaller than required */
+    MSA_ERR_HIP = -4           /* HIP runtime error (no device, launch failure) */
+} msa_status;
+
+/* Fixed per-model shape.  Supported: group 16, head_dim 128, index_dim 64,
+ * block 64, 1 <= top_k <= 32, n_kv_heads >= 1, scale finite and > 0. */
+typedef struct msa_shape {
+    int32_t n_kv_heads;   /* H_kv: key heads (query heads = H_kv * group) */
+    int32_t group;        /* query heads per key head */
+    int32_t head_dim;     /* D of q, k, v */
+    int32_t index_dim;    /* d_I of iq, ik */
+    int32_t block;        /* keys per block */
+    int32_t top_k;        /* blocks kept per (row, key head), local block included */
+    float scale;          /* softmax scale applied to q.k (1/sqrt(head_dim) usually) */
+} msa_shape;
+
+/* Ragged batch.  The four integers are host values; the arrays are device
+ * arrays.  No device-to-host copy is ever made. */
+typedef struct msa_batch {
+    int32_t n_seqs;            /* >= 0; 0 means nothing to do */
+    int32_t total_rows;        /* == cu_rows[n_seqs] */
+    int32_t max_rows;          /* >= every rows_s */
+    int32_t max_seq_len;       /* >= every seq_lens[s] */
+    const int32_t *cu_rows;    /* device [n_seqs + 1], prefix sums of rows_s, cu_rows[0] = 0 */
+    const int32_t *seq_lens;   /* device [n_seqs] */
+    const int64_t *kv_start;   /* device [n_seqs], first token of each sequence in k/v/ik */
+} msa_batch;
+
+/*
+ * Steps 1-2: lightning-indexer scores, max-pooled per block.
+ *   iq           bf16 [total_rows, n_kv_heads, index_dim], contiguous
+ *   ik           bf16, element (token t, key head g, dim d) at
+ *                ik[t*ik_tok_stride + g*ik_head_stride + d]; the dim axis is
+ *                contiguous; ik_head_stride == 0 means one index key shared by
+ *                every key head.  Rows of 128 bytes must be 16-byte aligned.
+ *   block_scores fp32 [total_rows, n_kv_heads, bs_stride], written in full:
+ *                S[r,g,b] for b < nb(r), -INFINITY for nb(r) <= b < bs_stride.
+ *   bs_stride    >= ceil(max_seq_len / block)
+ * Cost: reads every causally visible index key once per row tile; the
+ * contraction runs on bf16 MFMA with fp32 accumulation.
+ */
+int msa_index_scores(const msa_shape *shape, const msa_batch *batch,
+                     const void *iq, const void *ik,
+                     int64_t ik_tok_stride, int64_t ik_head_stride,
+                     float *block_scores, int32_t bs_stride, void *stream);
+
+/*
+ * Step 3: per (row, key head), keep the local block and the top_k-1 highest
+ * block scores among the earlier blocks; equal scores prefer the lower block
+ * index (-0.0 and +0.0 are equal).  Rows with nb <= top_k keep blocks
+ * 0..nb-1.  Output is ascending and padded with -1.
+ *   block_scores fp32 [total_rows, n_kv_heads, bs_stride] (as written above)
+ *   block_idx    int32 [total_rows, n_kv_heads, top_k]
+ * Scores must not be NaN.
+ */
+int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
+                      const float *block_scores, int32_t bs_stride,
+                      int32_t *block_idx, void *stream);
+
+/*
+ * Step 4 for prompt chunks: out[r, h, :] = softmax over the kept, visible keys
+ * of scale * q[r,h,:].k[j,g,:], applied to v[j,g,:], g = h / group.  One pass
+ * per row; the group's query heads share the row's selection, so each kept
+ * block is read once for all of them.  Keys are walked in ascending block
+ * order, so a row's bits do not depend on the other rows in the batch.
+ *   q, out    bf16 [total_rows, n_kv_heads*group, head_dim], contiguous
+ *   k, v      bf16, element (token t, key head g, dim d) at
+ *             k[t*kv_tok_stride + g*kv_head_stride + d]; 16-byte aligned rows
+ *   block_idx int32 [total_rows, n_kv_heads, top_k] (from msa_select_blocks)
+ *   lse       fp32 [total_rows, n_kv_heads*group] natural-log log-sum-exp of
+ *             the scaled scores, or NULL.  A row with no kept visible key gets
+ *             out = 0 and lse = -INFINITY.
+ */
+int msa_prefill(const msa_shape *shape, const msa_batch *batch,
+                const void *q, const void *k, const void *v,
+                int64_t kv_tok_stride, int64_t kv_head_stride,
+                const int32_t *block_idx, void *out, float *lse, void *stream);
+
+/* Bytes of workspace msa_decode needs for total_rows rows (host function). */
+size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
+
+/*
+ * Step 4 for decode steps and verify windows: the same result as msa_prefill
+ * (within rounding), computed as split-K over the kept keys: each wave owns a
+ * 32-key piece, a workgroup merges its pieces, the partials
+ * (max, sum, weighted values) go to `workspace` and a combine pass merges
+ * them with log-sum-exp weights.  The split depends only on top_k and block,
+ * never on the batch, so a row's bits do not depend on the other rows.
+ *   workspace        device scratch of >= msa_decode_workspace_bytes() bytes;
+ *                    contents on entry are ignored, on return unspecified.
+ * Other arguments as msa_prefill.
+ */
+int msa_decode(const msa_shape *shape, const msa_batch *batch,
+               const void *q, const void *k, const void *v,
+               int64_t kv_tok_stride, int64_t kv_head_stride,
+               const int32_t *block_idx, void *out, float *lse,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *msa_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none). */
+const char *msa_last_error(void);
+
+/* Library version string (static). */
+const char *msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/msa.h declares, and validates arguments before anything reaches the
+device.  No kernel is launched by these tests."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_attention_04_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH), reason="libmsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for n in ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = msa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(msa.EXPORTS)
+
+
+def test_version_and_status_strings():
+    L = msa.lib()
+    assert b"gfx950" in L.msa_version()
+    assert L.msa_status_string(0) == b"ok"
+    assert L.msa_status_string(-3) == b"workspace too small"
+    assert L.msa_status_string(12345) == b"unknown status"
+
+
+class FakeBatch:
+    """A batch whose device pointers are never dereferenced: each test below
+    fails validation before any device call."""
+
+    def __init__(self, n_seqs=1, total_rows=4, max_rows=4, max_seq_len=100):
+        self.c = msa._BatchC(n_seqs, total_rows, max_rows, max_seq_len, 256, 512, 768)
+
+
+def _call_index(shape, batch, iq=4096, ik=8192, tok=64, head=0, scores=12288, bs=2):
+    L = msa.lib()
+    return L.msa_index_scores(ctypes.byref(shape) if shape is not None else None,
+                              ctypes.byref(batch.c) if batch is not None else None,
+                              ctypes.c_void_p(iq), ctypes.c_void_p(ik), tok, head,
+                              ctypes.c_void_p(scores), bs, None)
+
+
+def _err():
+    return msa.lib().msa_last_error().decode()
+
+
+def test_null_shape_and_batch():
+    assert _call_index(None, FakeBatch()) == -1
+    assert "shape" in _err()
+    assert _call_index(msa.make_shape(1), None) == -1
+    assert "batch" in _err()
+
+
+@pytest.mark.parametrize("field,value", [("group", 8), ("head_dim", 64), ("index_dim", 128),
+                                         ("block", 128), ("top_k", 0), ("top_k", 33)])
+def test_unsupported_shapes(field, value):
+    sh = msa.make_shape(2)
+    setattr(sh, field, value)
+    assert _call_index(sh, FakeBatch()) == -2
+
+
+def test_invalid_scale_and_heads():
+    sh = msa.make_shape(2)
+    sh.scale = 0.0
+    assert _call_index(sh, FakeBatch()) == -1
+    sh = msa.make_shape(2)
+    sh.scale = float("inf")
+    assert _call_index(sh, FakeBatch()) == -1
+    assert _call_index(msa.make_shape(0), FakeBatch()) == -1
+
+
+def test_invalid_batches():
+    sh = msa.make_shape(1)
+    assert _call_index(sh, FakeBatch(n_seqs=-1)) == -1
+    assert _call_index(sh, FakeBatch(max_rows=200, max_seq_len=100)) == -1   # rows > keys
+    assert _call_index(sh, FakeBatch(n_seqs=1, total_rows=9, max_rows=4)) == -1
+    assert _call_index(sh, FakeBatch(n_seqs=0, total_rows=3)) == -1
+
+
+def test_empty_batch_is_a_no_op():
+    # n_seqs == 0 returns OK without touching the device or the pointers
+    assert _call_index(msa.make_shape(1), FakeBatch(n_seqs=0, total_rows=0, max_rows=0,
+                                                    max_seq_len=0), iq=0, ik=0, scores=0) == 0
+
+
+def test_pointer_stride_and_alignment_checks():
+    sh = msa.make_shape(2)
+    assert _call_index(sh, FakeBatch(), iq=0) == -1                  # null iq
+    assert _call_index(sh, FakeBatch(), tok=32) == -1                # rows overlap
+    assert _call_index(sh, FakeBatch(), head=16) == -1               # heads overlap
+    assert _call_index(sh, FakeBatch(), iq=4098) == -1               # misaligned
+    assert _call_index(sh, FakeBatch(max_seq_len=200), bs=3) == -1   # stride < ceil(200/64)
+    assert "bs_stride" in _err()
+
+
+def test_decode_workspace_size_and_check():
+    L = msa.lib()
+    sh = msa.make_shape(4, top_k=16)
+    per_row = 4 * 8 * (16 + 16 + 16 * 128) * 4     # heads * splits * partial floats * 4 bytes
+    assert msa.msa_decode_workspace_bytes(sh, 3) == 3 * per_row
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 4 * 1 * 2080 * 4
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=40), 1) == 0
+    b = FakeBatch(total_rows=4)
+    rc = L.msa_decode(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096),
+                      ctypes.c_void_p(8192), ctypes.c_void_p(16384), 512, 128,
+                      ctypes.c_void_p(32768), ctypes.c_void_p(65536), None,
+                      ctypes.c_void_p(131072), 3 * per_row, None)
+    assert rc == -3 and "workspace" in _err()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
+def test_no_device_returns_hip_error():
+    # every argument is valid, so only the device check can fail here
+    rc = _call_index(msa.make_shape(1), FakeBatch())
+    assert rc == -4 and "device" in _err()
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(msa.MsaError) as ei:
+        msa._check(-2)
+    assert ei.value.status == -2

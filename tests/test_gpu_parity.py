@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs; plus the invariants the method implies (batch,
+window/one-row and rerun bit-identity) and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_04_amd as msa
+import oracle
+from gpu_helpers import device_tensors, full_check, gpu_run, say, shape_of
+from workloads import Case, config, make_case
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # > 16 rows: the LDS-tiled indexer; 300 rows span two 256-row tiles
+    "ragged_tiled": dict(seq_lens=[700, 1500, 300, 64], rows=[300, 5, 300, 64], n_kv_heads=2, seed=101),
+    # <= 16 rows per sequence: the streaming indexer; includes a 1-key sequence
+    "ragged_window": dict(seq_lens=[5000, 1, 64, 65, 3000], rows=[16, 1, 16, 7, 3], n_kv_heads=3, seed=102),
+    # one index key shared by the key heads (head stride 0)
+    "shared_ik": dict(seq_lens=[2000, 900], rows=[40, 8], n_kv_heads=4, seed=103, ik_shared=True),
+    # indexer inputs scaled by 1/8 (exact), as in the tiny configuration
+    "scaled_index": dict(seq_lens=[3000], rows=[100], n_kv_heads=1, seed=104, index_scale=0.125),
+    "top1": dict(seq_lens=[1200, 800], rows=[20, 3], n_kv_heads=2, seed=105, top_k=1),
+    "top5": dict(seq_lens=[1200, 800], rows=[20, 3], n_kv_heads=2, seed=106, top_k=5),
+    "top32": dict(seq_lens=[4000, 2100], rows=[30, 2], n_kv_heads=2, seed=107, top_k=32),
+}
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cases(name, mode):
+    kw = dict(SMALL[name])
+    case = make_case(name, **kw)
+    full_check(case, mode)
+
+
+FULL_ROWS = {
+    "tiny": lambda c: np.unique(np.r_[0, 1, 63, 64, 1023, 1024, 1025, 2047,
+                                      np.random.default_rng(1).choice(2048, 120, replace=False)]),
+    "decode": lambda c: np.arange(c.total_rows),
+    "chunk": lambda c: np.unique(np.r_[0, 1, 63, 64, 255, 256, 257, 1000, 2047, 2048, 4032, 4095,
+                                       np.random.default_rng(2).choice(4096, 20, replace=False)]),
+    "long": lambda c: np.arange(c.total_rows),
+    "windows": lambda c: np.arange(c.total_rows),
+}
+FULL_MODE = {"tiny": "prefill", "decode": "decode", "chunk": "prefill", "long": "decode",
+             "windows": "decode"}
+
+
+@pytest.mark.parametrize("name", list(FULL_ROWS))
+def test_full_configs(name):
+    """The five named workloads at full size, through the entry point the
+    benchmark uses for them; outputs compared on sampled rows."""
+    case = config(name)
+    m = full_check(case, FULL_MODE[name], rows=FULL_ROWS[name](case))
+    if name == "windows":
+        # the planted needle blocks are kept by every row and key head
+        g = gpu_run(case, "decode")
+        idx = g["block_idx"].numpy()
+        for s in range(case.n_seqs):
+            for r in range(case.cu_rows[s], case.cu_rows[s + 1]):
+                for h in range(case.n_kv_heads):
+                    assert set(case.needles[s]) <= set(idx[r, h].tolist())
+    assert m["excluded"] <= max(3, 0.05 * m["units"])
+
+
+def test_prefill_and_decode_agree():
+    case = make_case("cross", [3000, 700], [16, 9], 2, seed=111)
+    a = gpu_run(case, "prefill")
+    b = gpu_run(case, "decode")
+    assert np.array_equal(a["block_idx"].numpy(), b["block_idx"].numpy())
+    d = (a["out"].float() - b["out"].float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_reruns_are_bit_identical(mode):
+    case = make_case("rerun", [5000, 2000], [64, 16], 2, seed=112)
+    t = device_tensors(case)
+    runs = [gpu_run(case, mode, t=t) for _ in range(3)]
+    for r in runs[1:]:
+        for k in ("block_scores", "block_idx", "out", "lse"):
+            assert torch.equal(r[k], runs[0][k]), k
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_batch_invariance(mode):
+    """A sequence alone gives the same bits as inside a ragged batch."""
+    big = make_case("batch", [3000, 1700, 900], [20, 16, 5], 2, seed=113)
+    g = gpu_run(big, mode)
+    k0, L, r0, n = big.kv_start[1], big.seq_lens[1], big.cu_rows[1], big.rows[1]
+    solo = Case(name="solo", seq_lens=[L], rows=[n], n_kv_heads=2, q=big.q[r0:r0 + n],
+                k=big.k[k0:k0 + L], v=big.v[k0:k0 + L], iq=big.iq[r0:r0 + n], ik=big.ik[k0:k0 + L])
+    s = gpu_run(solo, mode)
+    nbk = s["block_scores"].shape[2]
+    assert torch.equal(g["block_scores"][r0:r0 + n, :, :nbk], s["block_scores"])
+    assert torch.equal(g["block_idx"][r0:r0 + n], s["block_idx"])
+    assert torch.equal(g["out"][r0:r0 + n], s["out"])
+
+
+def test_window_equals_one_row_steps():
+    """A 16-row verify window through msa_decode gives, row by row, the same
+    bits as 16 one-row decode steps on the growing cache."""
+    L, n = 9000, 16
+    win = make_case("win", [L], [n], 2, seed=114)
+    gw = gpu_run(win, "decode")
+    for i in range(n):
+        p = L - n + i
+        step = Case(name="step", seq_lens=[p + 1], rows=[1], n_kv_heads=2, q=win.q[i:i + 1],
+                    k=win.k[:p + 1], v=win.v[:p + 1], iq=win.iq[i:i + 1], ik=win.ik[:p + 1])
+        gs = gpu_run(step, "decode")
+        assert torch.equal(gw["block_idx"][i], gs["block_idx"][0])
+        assert torch.equal(gw["out"][i], gs["out"][0])
+        nbk = gs["block_scores"].shape[2]
+        assert torch.equal(gw["block_scores"][i, :, :nbk], gs["block_scores"][0])
+
+
+def test_equal_scores_take_lowest_blocks():
+    """All-zero indexer queries: every block scores 0, so the selection is the
+    15 lowest blocks plus the local one (ties go to the lower index); this also
+    drives the selection's many-ties path."""
+    case = make_case("zeros", [8000, 3000], [17, 2], 2, seed=115)
+    case.iq = torch.zeros_like(case.iq)
+    g = gpu_run(case, "prefill")
+    nb = oracle.causal_blocks(case)
+    idx = g["block_idx"].numpy()
+    for r in range(case.total_rows):
+        want = list(range(15)) + [int(nb[r]) - 1]
+        for h in range(2):
+            assert list(idx[r, h]) == want
+    full_check(case, "decode")
+
+
+def test_integer_ties_exact():
+    """Small-integer indexer inputs give exact scores on both sides, with many
+    exact ties at the cut: the selection must match bit for bit everywhere."""
+    case = make_case("ties", [6000, 2500], [24, 4], 2, seed=116)
+    gen = torch.Generator().manual_seed(5)
+    case.iq = torch.randint(-2, 3, case.iq.shape, generator=gen).to(torch.bfloat16)
+    case.ik = torch.randint(-2, 3, case.ik.shape, generator=gen).to(torch.bfloat16)
+    g = gpu_run(case, "decode")
+    ref = oracle.run(case)
+    assert np.array_equal(g["block_scores"].numpy().astype(np.float64), ref["scores64"])
+    assert np.array_equal(g["block_idx"].numpy(), ref["block_idx"])
+
+
+def test_constant_values_and_zero_keys():
+    case = make_case("const", [2500], [33], 2, seed=117)
+    case.v = torch.full_like(case.v, 0.75)
+    for mode in ("prefill", "decode"):
+        g = gpu_run(case, mode)
+        assert torch.all(g["out"].float() == 0.75)
+    case = make_case("zk", [2500], [33], 2, seed=118)
+    case.k = torch.zeros_like(case.k)
+    full_check(case, "prefill")
+
+
+def test_empty_batch_is_noop():
+    case = make_case("e", [100], [1], 1, seed=119)
+    shape = shape_of(case)
+    b = msa.Batch([], [])
+    t = device_tensors(case)
+    s = torch.full((1, 1, 2), 7.0, device="cuda")
+    msa.msa_index_scores(shape, b, t["iq"], t["ik"], s)
+    torch.cuda.synchronize()
+    assert torch.all(s == 7.0)
+
+
+def test_strided_kv_views():
+    """k/v as views into a wider [tokens, heads, 2*128] buffer (token stride
+    != heads*128) give the same result as contiguous copies."""
+    case = make_case("strided", [2000], [20], 2, seed=120)
+    t = device_tensors(case)
+    wide_k = torch.zeros(case.total_keys, 2, 256, dtype=torch.bfloat16, device="cuda")
+    wide_v = torch.zeros_like(wide_k)
+    wide_k[:, :, 64:192] = t["k"]
+    wide_v[:, :, 64:192] = t["v"]
+    t2 = dict(t, k=wide_k[:, :, 64:192], v=wide_v[:, :, 64:192])
+    for mode in ("prefill", "decode"):
+        a = gpu_run(case, mode, t=t)
+        b = gpu_run(case, mode, t=t2)
+        assert torch.equal(a["out"], b["out"])
