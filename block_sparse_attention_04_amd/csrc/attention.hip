@@ -51,69 +51,65 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[4], const uint16_t *qrow_head
     for (int s = 0; s < 4; ++s) qb[s] = load16(src + 8 * s);
 }
 
-// Fold the 32 keys [kbase, kbase + 32) of one sequence (those <= p) into st.
-// kseq/vseq point at key 0 of the sequence for this key head; vt is this
-// wave's 8 KiB LDS tile.
-__device__ __forceinline__ void attend_chunk32(Softmax &st, const u32x4 (&qb)[4],
-                                               const uint16_t *kseq, const uint16_t *vseq,
-                                               int64_t tok, int kbase, int p, float scale_log2,
-                                               uint8_t *vt) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-
-    // K operands: key kbase + 16*mt + lr, dims 32*lg + 8*s.
+// Registers of one 32-key chunk: K as MFMA A operands (key kbase + 16*mt +
+// lane%16, dims 32*(lane/16) + 8*s) and V rows (keys kbase + 4*(lane/8) +
+// 0..3, dims 16*(lane%8) + 0..15).  A key past p is read from key p instead
+// (always in bounds): its score is masked to -inf, so its weight is 0.
+struct ChunkRegs {
     u32x4 ka[2][4];
+    u32x4 vr[4][2];
+};
+
+__device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, const uint16_t *vseq,
+                                           int64_t tok, int kbase, int p) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const int key = kbase + 16 * mt + lr;
-        if (key <= p) {
-            const uint16_t *src = kseq + (int64_t)key * tok + 32 * lg;
+        const int key = min(kbase + 16 * mt + lr, p);
+        const uint16_t *src = kseq + (int64_t)key * tok + 32 * lg;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ka[mt][s] = load16(src + 8 * s);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) ka[mt][s] = zero16();
-        }
+        for (int s = 0; s < 4; ++s) c.ka[mt][s] = load16(src + 8 * s);
     }
-    // V rows: keys kbase + 4*kg + (0..3), dims 16*dc + (0..15).
     const int kg = lane >> 3, dc = lane & 7;
-    u32x4 vr[4][2];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const int key = kbase + 4 * kg + kk;
-        if (key <= p) {
-            const uint16_t *src = vseq + (int64_t)key * tok + 16 * dc;
-            vr[kk][0] = load16(src);
-            vr[kk][1] = load16(src + 8);
-        } else {
-            vr[kk][0] = zero16();
-            vr[kk][1] = zero16();
-        }
+        const int key = min(kbase + 4 * kg + kk, p);
+        const uint16_t *src = vseq + (int64_t)key * tok + 16 * dc;
+        c.vr[kk][0] = load16(src);
+        c.vr[kk][1] = load16(src + 8);
     }
+}
 
+// Fold one loaded 32-key chunk [kbase, kbase + 32) (keys <= p visible) into
+// st; vt is this wave's 8 KiB LDS tile.
+__device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
+                                           int kbase, int p, float scale_log2, uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     floatx4 sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) c = mfma_16x16x32(ka[mt][s], qb[s], c);
-        sacc[mt] = c;
+        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(c.ka[mt][s], qb[s], acc);
+        sacc[mt] = acc;
     }
 
     // V^T into LDS.  Key k of the chunk goes to slot 8*((k%16)/4) + 4*(k/16) + k%4,
     // so lane group lg's k-slots (keys 4lg..4lg+3 and 16+4lg..16+4lg+3) are
     // the 8 contiguous slots of group lg.  Keys 4kg..4kg+3 share one 8-byte
     // word per dim.
+    const int kg = lane >> 3, dc = lane & 7;
     const int grp = kg & 3, half = kg >> 2;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int reg = t >> 3, dw = (t & 7) >> 1;
         uint32_t w0, w1;
         if (t & 1) {
-            w0 = (vr[0][reg][dw] >> 16) | (vr[1][reg][dw] & 0xffff0000u);
-            w1 = (vr[2][reg][dw] >> 16) | (vr[3][reg][dw] & 0xffff0000u);
+            w0 = (c.vr[0][reg][dw] >> 16) | (c.vr[1][reg][dw] & 0xffff0000u);
+            w1 = (c.vr[2][reg][dw] >> 16) | (c.vr[3][reg][dw] & 0xffff0000u);
         } else {
-            w0 = (vr[0][reg][dw] & 0xffffu) | (vr[1][reg][dw] << 16);
-            w1 = (vr[2][reg][dw] & 0xffffu) | (vr[3][reg][dw] << 16);
+            w0 = (c.vr[0][reg][dw] & 0xffffu) | (c.vr[1][reg][dw] << 16);
+            w1 = (c.vr[2][reg][dw] & 0xffffu) | (c.vr[3][reg][dw] << 16);
         }
         const int d = 16 * dc + t;
         *reinterpret_cast<uint2 *>(vt + vt_offset(d, grp) + 8 * half) = make_uint2(w0, w1);
@@ -159,6 +155,15 @@ __device__ __forceinline__ void attend_chunk32(Softmax &st, const u32x4 (&qb)[4]
     wave_lds_sync();   // reads finish before the next chunk overwrites the tile
 }
 
+__device__ __forceinline__ void attend_chunk32(Softmax &st, const u32x4 (&qb)[4],
+                                               const uint16_t *kseq, const uint16_t *vseq,
+                                               int64_t tok, int kbase, int p, float scale_log2,
+                                               uint8_t *vt) {
+    ChunkRegs c;
+    load_chunk(c, kseq, vseq, tok, kbase, p);
+    fold_chunk(st, qb, c, kbase, p, scale_log2, vt);
+}
+
 // Unit (row r, key head g) of a head-major enumeration: consecutive units are
 // consecutive rows of one key head, so neighbouring waves share local blocks.
 struct Unit {
@@ -180,7 +185,7 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 
 __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
     const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
     if (unit >= (int64_t)a.b.total_rows * a.H) return;
@@ -193,20 +198,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
     u32x4 qb[4];
     load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+    // Lane t holds kept block t; read with v_readlane (loaded before the
+    // pipelined loop's explicit wait, so the loop never waits on it).
     const int32_t *sel = a.idx + ((int64_t)u.r * a.H + u.g) * a.top_k;
     const int my_b = lane < a.top_k ? sel[lane] : -1;
 
+    // Walk the kept blocks in list (ascending) order, 32 keys at a time, with
+    // the next chunk's K/V loads in flight while the current one is folded.
     Softmax st;
     softmax_init(st);
-    for (int t = 0; t < a.top_k; ++t) {
-        const int b = __builtin_amdgcn_readlane(my_b, t);
-        if (b < 0 || b * kBlock > u.p) continue;
-#pragma unroll 1
-        for (int half = 0; half < 2; ++half) {
-            const int kbase = b * kBlock + 32 * half;
-            if (kbase > u.p) break;
-            attend_chunk32(st, qb, kseq, vseq, a.kv_tok, kbase, u.p, a.scale_log2, vt_all[wave]);
+    int t = 0, half = 0;
+    auto chunk_base = [&](int tt, int hh) -> int {
+        const int b = __builtin_amdgcn_readlane(my_b, tt);
+        const int kb = b * kBlock + 32 * hh;
+        return (b < 0 || kb > u.p) ? -1 : kb;
+    };
+    auto next_chunk = [&]() -> int {     // advances (t, half) to the next visible chunk
+        for (;;) {
+            half ^= 1;
+            if (half == 0 && ++t >= a.top_k) return -1;
+            const int kb = chunk_base(t, half);
+            if (kb >= 0) return kb;
         }
+    };
+    force_ready(my_b);                   // the block list has arrived
+    int kb0 = chunk_base(0, 0);
+    if (kb0 < 0) kb0 = next_chunk();
+    ChunkRegs ca, cb;
+    uint8_t *vt = vt_all[wave];
+    if (kb0 >= 0) load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) force_ready(qb[s]);   // q complete before the loop
+    while (kb0 >= 0) {
+        const int kb1 = next_chunk();
+        if (kb1 >= 0) load_chunk(cb, kseq, vseq, a.kv_tok, kb1, u.p);
+        fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt);
+        if (kb1 < 0) break;
+        kb0 = next_chunk();
+        if (kb0 >= 0) load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
+        fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt);
     }
 
     const float l = sum_over_lane_groups(st.l);
@@ -297,14 +327,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(AttnArgs a, int n_s
     const int g = (int)(unit / a.b.total_rows), r = (int)(unit % a.b.total_rows);
     const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
     const float *part = a.ws + unit * n_split * (int64_t)kPartialFloats;
+    constexpr int kMaxSplit = (kMaxTopK * 2 + kDecodeWaves - 1) / kDecodeWaves;
+    float ms[kMaxSplit];
     float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[s * kPartialFloats + h]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+        ms[s] = s < n_split ? part[s * kPartialFloats + h] : -INFINITY;
+        M = fmaxf(M, ms[s]);
+    }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float Ls = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < n_split; ++s) {
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s) {
+            if (s >= n_split) break;
             const float *ps = part + s * kPartialFloats;
-            const float w = exp2f(ps[h] - M);
+            const float w = exp2f(ms[s] - M);
             Ls += w * ps[16 + h];
             const floatx4 x0 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0);
             const floatx4 x1 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0 + 4);

@@ -14,8 +14,9 @@
 //
 // Two tilings of the same computation:
 //   index_scores_tiled  prompt chunks: a workgroup owns 256 rows x a key range;
-//                       each 64-key tile of ik is staged once in LDS (double
-//                       buffered) and reused by the 4 waves' 64 rows each.
+//                       each 64-key tile of ik is staged once in LDS (a ring
+//                       of three, loads two tiles ahead) and reused by the 4
+//                       waves' 64 rows each.
 //   index_scores_window decode steps and windows (<= 16 rows per sequence):
 //                       the 16-row tile is the wave's whole row set, so ik is
 //                       streamed straight from HBM into MFMA operand registers
@@ -48,13 +49,15 @@ __device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0,
 }
 
 constexpr int kTiledWaves = 4;
+constexpr int kTiledBlocks = 16;   // blocks per workgroup key range
 constexpr int kLdsRow = 144;   // bytes per staged key (128 + 16 pad: conflict-free b128 reads)
 
 template <int NT>
 __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int blocks_per_wg) {
     constexpr int kRowsWave = 16 * NT;
     constexpr int kRowsWg = kRowsWave * kTiledWaves;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[3][kBlock * kLdsRow];
+    __shared__ float otile[kTiledWaves][kRowsWave * kTiledBlocks];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lg = lane >> 4, lr = lane & 15;
@@ -97,82 +100,131 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     const int wave_p_min = p_base + wrow0;
 
     // Staging: thread t copies 32 bytes (piece t&3) of key t>>2 of the tile.
+    // Three LDS buffers and two register sets: block i+3 is requested while
+    // block i is computed, so each load has two block-times to arrive.
     const int st_key = threadIdx.x >> 2, st_piece = threadIdx.x & 3;
     const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * st_piece;
-    u32x4 x0 = zero16(), x1 = zero16();
-    auto gload = [&](int b) {
-        const int j = b * kBlock + st_key;
-        if (j < L) {
-            const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
-            x0 = load16(src);
-            x1 = load16(src + 8);
-        } else {
-            x0 = zero16();
-            x1 = zero16();
-        }
+    struct Stage {
+        u32x4 x0, x1;
     };
-    auto sstore = [&](int buf) {
+    // Keys past the sequence end read its last key instead (always in
+    // bounds); they lie past every row's position, so the max-pool masks them.
+    auto gload = [&](int b, Stage &r) {
+        const int j = min(b * kBlock + st_key, L - 1);
+        const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
+        r.x0 = load16(src);
+        r.x1 = load16(src + 8);
+    };
+    auto sstore = [&](int buf, const Stage &r) {
         uint8_t *dst = &lds[buf][st_key * kLdsRow + 32 * st_piece];
-        *reinterpret_cast<u32x4 *>(dst) = x0;
-        *reinterpret_cast<u32x4 *>(dst + 16) = x1;
+        *reinterpret_cast<u32x4 *>(dst) = r.x0;
+        *reinterpret_cast<u32x4 *>(dst + 16) = r.x1;
     };
 
-    if (b_begin < b_cmp_end) {
-        gload(b_begin);
-        sstore(0);
-    }
-    __syncthreads();
-
-    float held[NT];
+    // Block maxima go to an LDS tile [wave rows][blocks of the range] and
+    // leave in one coalesced flush at the end, so no global store sits
+    // between the loop's prefetch loads.
+    float *out_tile = otile[wave];
+    auto emit = [&](int b, const float (&m)[NT]) {
+        if (lg == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) held[nt] = -INFINITY;
-
-    for (int b = b_begin; b < b_end; ++b) {
-        float m[NT];
-        if (b < b_cmp_end) {
-            const int buf = (b - b_begin) & 1;
-            const bool more = b + 1 < b_cmp_end;
-            if (more) gload(b + 1);
-            floatx4 acc[NT][4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint8_t *src = &lds[buf][(16 * mt + lr) * kLdsRow + 32 * lg];
-                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(src);
-                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(src + 16);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    floatx4 c = {0.f, 0.f, 0.f, 0.f};
-                    c = mfma_16x16x32(a0, bq[nt][0], c);
-                    acc[nt][mt] = mfma_16x16x32(a1, bq[nt][1], c);
-                }
-            }
-            const bool need_mask = b * kBlock + kBlock - 1 > wave_p_min;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) m[nt] = block_max_64(acc[nt], b * kBlock, prow[nt], need_mask);
-            if (more) sstore(buf ^ 1);
-            __syncthreads();
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) m[nt] = -INFINITY;
+            for (int nt = 0; nt < NT; ++nt) out_tile[(nt * 16 + lr) * kTiledBlocks + (b - b_begin)] = m[nt];
         }
-        // Lane group lg keeps the blocks with b % 4 == lg; every 4 blocks the
-        // wave writes 16 contiguous bytes per row.
+    };
+    const int nblk = b_cmp_end - b_begin;
+    auto step = [&](int i, Stage &r) {
+        const int b = b_begin + i;
+        const uint8_t *buf = lds[i % 3];
+        floatx4 acc[NT][4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            if (lg == (b & 3)) held[nt] = m[nt];
-        if ((b & 3) == 3 || b == b_end - 1) {
-            const int blk = (b & ~3) + lg;
-            if (blk >= b_begin && blk <= b) {
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint8_t *src = buf + (16 * mt + lr) * kLdsRow + 32 * lg;
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(src + 16);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    if (rvalid[nt])
-                        a.scores[((int64_t)(row0 + wrow0 + nt * 16 + lr) * a.H + g) * a.bs_stride + blk] =
-                            held[nt];
+            for (int nt = 0; nt < NT; ++nt) {
+                floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma_16x16x32(a0, bq[nt][0], c);
+                acc[nt][mt] = mfma_16x16x32(a1, bq[nt][1], c);
             }
+        }
+        // Unconditional (clamped) so every step issues the same two loads and
+        // the compiler can wait for exactly the older set: block i+1 was
+        // requested two steps ago; buffer (i+1)%3 is not read this step.
+        sstore((i + 1) % 3, r);
+        gload(min(b + 3, b_cmp_end - 1), r);
+        const bool need_mask = b * kBlock + kBlock - 1 > wave_p_min;
+        float m[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) m[nt] = block_max_64(acc[nt], b * kBlock, prow[nt], need_mask);
+        __syncthreads();
+        emit(b, m);
+    };
+
+    Stage r0, r1;
+    if (nblk > 0) gload(b_begin, r0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {  // iq operands complete before the loop
+        force_ready(bq[nt][0]);
+        force_ready(bq[nt][1]);
+    }
+    if (nblk > 0) sstore(0, r0);
+    gload(min(b_begin + 1, b_cmp_end - 1), r1);
+    gload(min(b_begin + 2, b_cmp_end - 1), r0);
+    __syncthreads();
+    for (int i = 0; i < nblk; i += 2) {
+        step(i, r1);
+        if (i + 1 < nblk) step(i + 1, r0);
+    }
+    for (int b = b_cmp_end; b < b_end; ++b) {
+        float m[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) m[nt] = -INFINITY;
+        emit(b, m);
+    }
+    wave_lds_sync();
+    // Flush: 4 lanes per row, 16 bytes each (blocks_per_wg == kTiledBlocks).
+    const int nb_here = b_end - b_begin;
+#pragma unroll
+    for (int it = 0; it < kRowsWave * kTiledBlocks / 4 / kWave; ++it) {
+        const int e = it * kWave + lane;              // float4 index within the wave tile
+        const int rr = e / (kTiledBlocks / 4), c4 = (e % (kTiledBlocks / 4)) * 4;
+        const int rl = wrow0 + rr;
+        if (rl < rows_s) {
+            float *dst = a.scores + ((int64_t)(row0 + rl) * a.H + g) * a.bs_stride + b_begin + c4;
+            const float *srcv = out_tile + rr * kTiledBlocks + c4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c4 + q < nb_here) dst[q] = srcv[q];
         }
     }
 }
 
+__device__ __forceinline__ void window_load_block(u32x4 (&av)[4][2], const uint16_t *ik_g, int64_t kv0,
+                                                  int64_t tok, int b, int L, int lr) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int j = min(b * kBlock + 16 * mt + lr, L - 1);   // past the end: masked
+        const uint16_t *src = ik_g + (kv0 + j) * tok;
+        av[mt][0] = load16(src);
+        av[mt][1] = load16(src + 8);
+    }
+}
+
+__device__ __forceinline__ float window_block_max(const u32x4 (&av)[4][2], u32x4 bq0, u32x4 bq1, int b,
+                                                 int prow, int p_first) {
+    floatx4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+        c = mfma_16x16x32(av[mt][0], bq0, c);
+        acc[mt] = mfma_16x16x32(av[mt][1], bq1, c);
+    }
+    return block_max_64(acc, b * kBlock, prow, b * kBlock + kBlock - 1 > p_first);
+}
+
+// Each wave streams a range of blocks_per_wave (a multiple of 4) blocks, two
+// at a time with both blocks' loads in flight before the first MFMA.
 __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int blocks_per_wave) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lg = lane >> 4, lr = lane & 15;
@@ -201,35 +253,27 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int bloc
     const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
 
     float held = -INFINITY;
-    for (int b = b_begin; b < b_end; ++b) {
-        float m = -INFINITY;
-        if (b < b_cmp_end) {
-            u32x4 av[4][2];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int j = b * kBlock + 16 * mt + lr;
-                if (j < L) {
-                    const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
-                    av[mt][0] = load16(src);
-                    av[mt][1] = load16(src + 8);
-                } else {
-                    av[mt][0] = zero16();
-                    av[mt][1] = zero16();
-                }
-            }
-            floatx4 acc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                floatx4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma_16x16x32(av[mt][0], bq0, c);
-                acc[mt] = mfma_16x16x32(av[mt][1], bq1, c);
-            }
-            m = block_max_64(acc, b * kBlock, prow, b * kBlock + kBlock - 1 > p_first);
+    for (int b = b_begin; b < b_end; b += 2) {
+        float m0 = -INFINITY, m1 = -INFINITY;
+        if (b + 1 < b_cmp_end) {
+            u32x4 av0[4][2], av1[4][2];
+            window_load_block(av0, ik_g, kv0, a.ik_tok, b, L, lr);
+            window_load_block(av1, ik_g, kv0, a.ik_tok, b + 1, L, lr);
+            m0 = window_block_max(av0, bq0, bq1, b, prow, p_first);
+            m1 = window_block_max(av1, bq0, bq1, b + 1, prow, p_first);
+        } else if (b < b_cmp_end) {
+            u32x4 av0[4][2];
+            window_load_block(av0, ik_g, kv0, a.ik_tok, b, L, lr);
+            m0 = window_block_max(av0, bq0, bq1, b, prow, p_first);
         }
-        if (lg == (b & 3)) held = m;
-        if ((b & 3) == 3 || b == b_end - 1) {
-            const int blk = (b & ~3) + lg;
-            if (rvalid && blk >= b_begin && blk <= b)
+        if (lg == (b & 3)) held = m0;
+        if (lg == ((b + 1) & 3)) held = m1;
+        // blocks come in pairs starting at a multiple of 4: store after the odd
+        // block of the second pair, or at the end of the range
+        const int last = min(b + 1, b_end - 1);
+        if ((last & 3) == 3 || last == b_end - 1) {
+            const int blk = (last & ~3) + lg;
+            if (rvalid && blk >= b_begin && blk <= last)
                 a.scores[((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk] = held;
         }
     }
@@ -238,16 +282,15 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int bloc
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
     const int gz = a.b.n_seqs * a.H;
     if (a.b.max_rows <= 16) {
-        const int bpw = 8;                       // blocks per wave (multiple of 4)
+        const int bpw = 4;                       // blocks per wave (multiple of 4)
         const int per_wg = bpw * 4;
         dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, gz);
         hipLaunchKernelGGL(index_scores_window, grid, dim3(256), 0, st, a, bpw);
     } else {
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
-        const int bpwg = 16;                     // blocks per workgroup (multiple of 4)
-        dim3 grid((a.bs_stride + bpwg - 1) / bpwg, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
-        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, bpwg);
+        dim3 grid((a.bs_stride + kTiledBlocks - 1) / kTiledBlocks, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
+        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, kTiledBlocks);
     }
     return hipGetLastError();
 }

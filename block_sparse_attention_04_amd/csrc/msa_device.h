@@ -66,19 +66,35 @@ __device__ __forceinline__ int locate_seq(const int32_t *cu_rows, int n_seqs, in
     return lo;
 }
 
-// Wave-wide reductions across the four lanes l, l^16, l^32, l^48 that share
-// a column of an MFMA result.
+// Reductions across the four lanes l, l^16, l^32, l^48 that share a column
+// of an MFMA result, on the VALU: v_permlane16_swap pairs lane rows (l, l^16)
+// and v_permlane32_swap pairs halves (l, l^32); with both operands equal, the
+// two results of each swap hold the pair's two values on every lane.
 __device__ __forceinline__ float max_over_lane_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float sum_over_lane_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// Make the compiler complete the loads that produced x here (an empty asm
+// that reads x): a software-pipelined loop that later uses x then never
+// waits on it, which would also wait for the loop's own prefetches.
+__device__ __forceinline__ void force_ready(const u32x4 &x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void force_ready(int x) { asm volatile("" ::"v"(x)); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Make LDS writes of this wave visible to its own later LDS reads (and keep
 // the compiler from moving LDS accesses across this point).

@@ -55,7 +55,73 @@ __device__ __forceinline__ uint32_t kth_largest_wave(uint32_t v, int k) {
     return t;
 }
 
-__global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
+// Scores of the unit live in LDS (one burst of independent loads) when they
+// fit the per-wave capacity `cap`; otherwise every pass reads them from global
+// memory (L2-resident after the first).
+template <bool kStaged>
+__device__ __forceinline__ void select_unit(const SelectArgs &a, const float *S, float *lds, int n,
+                                            int need, int32_t *out, uint32_t *cand) {
+    const int lane = threadIdx.x & 63;
+    auto key_at = [&](int b) -> uint32_t { return order_key(kStaged ? lds[b] : S[b]); };
+
+    uint32_t lmax = 0u;
+#pragma unroll 8
+    for (int b = lane; b < n; b += kWave) lmax = max(lmax, key_at(b));
+    const uint32_t t0 = kth_largest_wave(lmax, need);
+
+    int c = 0;
+    for (int b0 = 0; b0 < n; b0 += kWave) {
+        const int b = b0 + lane;
+        const uint32_t v = b < n ? key_at(b) : 0u;
+        const bool f = b < n && v >= t0;
+        const uint64_t mk = __ballot(f);
+        const int pos = c + lanes_below(mk);
+        if (f && pos < kWave) cand[pos] = v;
+        c += __popcll(mk);
+    }
+
+    uint32_t t;
+    int n_gt;
+    if (c <= kWave) {
+        wave_lds_sync();
+        const uint32_t cv = lane < c ? cand[lane] : 0u;
+        t = kth_largest_wave(cv, need);
+        n_gt = __popcll(__ballot(cv > t));
+    } else {
+        t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cb = t | (1u << bit);
+            int cnt = 0;
+#pragma unroll 8
+            for (int b = lane; b < n; b += kWave) cnt += key_at(b) >= cb;
+            if (wave_sum_int(cnt) >= need) t = cb;
+        }
+        int cnt = 0;
+#pragma unroll 8
+        for (int b = lane; b < n; b += kWave) cnt += key_at(b) > t;
+        n_gt = wave_sum_int(cnt);
+    }
+
+    const int need_eq = need - n_gt;
+    int taken = 0, eq_seen = 0;
+    for (int b0 = 0; b0 < n; b0 += kWave) {
+        const int b = b0 + lane;
+        const bool valid = b < n;
+        const uint32_t v = valid ? key_at(b) : 0u;
+        const bool gt = valid && v > t;
+        const bool eq = valid && v == t;
+        const uint64_t em = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + lanes_below(em) < need_eq);
+        const uint64_t tm = __ballot(take);
+        if (take) out[taken + lanes_below(tm)] = b;
+        taken += __popcll(tm);
+        eq_seen += __popcll(em);
+    }
+    if (lane == 0) out[need] = n;  // the local block, largest index, last
+}
+
+__global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a, int cap) {
+    extern __shared__ float dyn[];             // [4 waves][cap] staged scores
     __shared__ uint32_t cand[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
@@ -77,64 +143,24 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
     const float *S = a.scores + unit * a.bs_stride;
     const int n = nb - 1;          // candidates: blocks 0 .. nb-2
     const int need = a.top_k - 1;  // how many of them to keep
-
-    uint32_t lmax = 0u;
-    for (int b = lane; b < n; b += kWave) lmax = max(lmax, order_key(S[b]));
-    const uint32_t t0 = kth_largest_wave(lmax, need);
-
-    int c = 0;
-    for (int b0 = 0; b0 < n; b0 += kWave) {
-        const int b = b0 + lane;
-        const uint32_t v = b < n ? order_key(S[b]) : 0u;
-        const bool f = b < n && v >= t0;
-        const uint64_t mk = __ballot(f);
-        const int pos = c + lanes_below(mk);
-        if (f && pos < kWave) cand[wave][pos] = v;
-        c += __popcll(mk);
-    }
-
-    uint32_t t;
-    int n_gt;
-    if (c <= kWave) {
+    if (n <= cap) {
+        float *lds = dyn + wave * cap;
+#pragma unroll 8
+        for (int b = lane; b < n; b += kWave) lds[b] = S[b];
         wave_lds_sync();
-        const uint32_t cv = lane < c ? cand[wave][lane] : 0u;
-        t = kth_largest_wave(cv, need);
-        n_gt = __popcll(__ballot(cv > t));
+        select_unit<true>(a, S, lds, n, need, out, cand[wave]);
     } else {
-        t = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cb = t | (1u << bit);
-            int cnt = 0;
-            for (int b = lane; b < n; b += kWave) cnt += order_key(S[b]) >= cb;
-            if (wave_sum_int(cnt) >= need) t = cb;
-        }
-        int cnt = 0;
-        for (int b = lane; b < n; b += kWave) cnt += order_key(S[b]) > t;
-        n_gt = wave_sum_int(cnt);
+        select_unit<false>(a, S, nullptr, n, need, out, cand[wave]);
     }
-
-    const int need_eq = need - n_gt;
-    int taken = 0, eq_seen = 0;
-    for (int b0 = 0; b0 < n; b0 += kWave) {
-        const int b = b0 + lane;
-        const bool valid = b < n;
-        const uint32_t v = valid ? order_key(S[b]) : 0u;
-        const bool gt = valid && v > t;
-        const bool eq = valid && v == t;
-        const uint64_t em = __ballot(eq);
-        const bool take = gt || (eq && eq_seen + lanes_below(em) < need_eq);
-        const uint64_t tm = __ballot(take);
-        if (take) out[taken + lanes_below(tm)] = b;
-        taken += __popcll(tm);
-        eq_seen += __popcll(em);
-    }
-    if (lane == 0) out[need] = n;  // the local block, largest index, last
 }
 
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
+    // stage up to 4,096 candidate blocks (262,144 keys) per unit in LDS
+    const int need = (a.b.max_seq_len + kBlock - 1) / kBlock;
+    const int cap = ((min(need, 4096) + 63) / 64) * 64;
     dim3 grid((unsigned)((units + 3) / 4));
-    hipLaunchKernelGGL(select_blocks_kernel, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(select_blocks_kernel, grid, dim3(256), (size_t)4 * cap * sizeof(float), st, a, cap);
     return hipGetLastError();
 }
 
