@@ -5,7 +5,7 @@ One step = the whole path on the two workloads the metric is quoted on:
          keys), 4 key heads x 16 query heads: index scores -> block
          selection -> msa_prefill;
   long:  one decode row at 262,144 keys, 4 key heads x 16 query heads:
-         index scores -> block selection -> msa_decode (split-K + combine).
+         index scores -> block selection -> msa_decode (split-K, last-arriver combine).
 value = rows per second of the step (4,097 rows).  Inputs are resident in HBM
 before timing; the timed region enqueues K steps back to back, bracketed by a
 device synchronisation on both sides.  Inputs rotate over replicas so the

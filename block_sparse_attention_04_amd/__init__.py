@@ -181,6 +181,13 @@ def msa_decode_workspace_bytes(shape: Shape, total_rows: int) -> int:
     return int(lib().msa_decode_workspace_bytes(ctypes.byref(shape), int(total_rows)))
 
 
+def decode_workspace(shape: Shape, total_rows: int, device="cuda"):
+    """A zero-filled workspace for msa_decode (its counters must start at 0;
+    the library leaves them at 0 after every completed call)."""
+    n = max(msa_decode_workspace_bytes(shape, total_rows), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
 def msa_decode(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, workspace=None,
                stream=None):
     _need(q, torch.bfloat16, "q")
@@ -193,9 +200,8 @@ def msa_decode(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, wo
         raise ValueError("k and v must share strides")
     if lse is not None:
         _need(lse, torch.float32, "lse")
-    nbytes = msa_decode_workspace_bytes(shape, batch.total_rows)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(shape, batch.total_rows, q.device)
     _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), _ptr(k), _ptr(v),
                             tok, head, _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -223,8 +229,7 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
         msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
     elif mode == "decode":
         if "workspace" not in out:
-            out["workspace"] = torch.empty(max(msa_decode_workspace_bytes(shape, rows), 16),
-                                           dtype=torch.uint8, device=dev)
+            out["workspace"] = decode_workspace(shape, rows, dev)
         msa_decode(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"],
                    out["workspace"], stream)
     else:

@@ -16,6 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.hip", "indexer.hip", "select.hip", "attention.hip"]
+# Per-source extras.  indexer: MFMA accumulators in ordinary VGPRs, so the
+# max-pool reads them without v_accvgpr copies (measured faster; the
+# attention kernels measured slower with it).
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -32,7 +36,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -161,6 +161,9 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch, const floa
     const int64_t need = ((int64_t)batch->max_seq_len + msa::kBlock - 1) / msa::kBlock;
     if (bs_stride < need)
         return fail(MSA_ERR_INVALID, "bs_stride=%d < ceil(max_seq_len/64)=%lld", bs_stride, (long long)need);
+    if (need > msa::kMaxSelectBlocks)
+        return fail(MSA_ERR_UNSUPPORTED, "max_seq_len=%d: selection supports at most %d blocks (%d keys)",
+                    batch->max_seq_len, msa::kMaxSelectBlocks, msa::kMaxSelectBlocks * msa::kBlock);
     if ((rc = check_device())) return rc;
     msa::SelectArgs a;
     a.b = to_dev(batch);
@@ -193,7 +196,8 @@ static int attn_common(const msa_shape *shape, const msa_batch *batch, const voi
     a->idx = block_idx;
     a->out = static_cast<uint16_t *>(out);
     a->lse = lse;
-    a->ws = nullptr;
+    a->ws_count = nullptr;
+    a->ws_part = nullptr;
     return MSA_OK;
 }
 
@@ -212,8 +216,7 @@ int msa_prefill(const msa_shape *shape, const msa_batch *batch, const void *q, c
 
 size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows) {
     if (!shape || check_shape(shape) || total_rows < 0) return 0;
-    return (size_t)total_rows * shape->n_kv_heads * msa::decode_splits(shape->top_k) *
-           msa::kPartialFloats * sizeof(float);
+    return msa::decode_workspace_bytes((int64_t)total_rows * shape->n_kv_heads, shape->top_k);
 }
 
 int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
@@ -225,12 +228,14 @@ int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, co
                          &empty);
     if (rc) return rc;
     if (empty) return ok();
-    const size_t need = msa_decode_workspace_bytes(shape, batch->total_rows);
+    const int64_t units = (int64_t)batch->total_rows * shape->n_kv_heads;
+    const size_t need = msa::decode_workspace_bytes(units, shape->top_k);
     if (!workspace || workspace_bytes < need)
         return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(MSA_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
     if ((rc = check_device())) return rc;
-    a.ws = static_cast<float *>(workspace);
+    a.ws_count = static_cast<unsigned *>(workspace);
+    a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::decode_count_bytes(units));
     return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
 }
 

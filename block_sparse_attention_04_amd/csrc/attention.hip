@@ -6,8 +6,8 @@
 // The 16 query heads of a key head share the row's selection, so a wave holds
 // all 16 heads of one (row, key head) and reads every kept key/value once for
 // all of them (TensorFold pull request 1388, commit on 4,096-row prompt
-// chunks).  Decode splits the kept keys into 32-key partials merged by a
-// log-sum-exp combine (same pull request, commit adding the minimax_m3
+// chunks).  Decode splits the kept keys into partials of 32-key pieces merged
+// by a log-sum-exp combine (same pull request, commit adding the minimax_m3
 // family).
 //
 // Per 32-key chunk, on v_mfma_f32_16x16x32_bf16:
@@ -252,115 +252,118 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     if (a.lse && lg == 0) a.lse[(int64_t)u.r * hq + h] = l > 0.f ? (st.m + log2f(l)) * kLn2 : -INFINITY;
 }
 
-// Decode: workgroup (unit, split) = 4 waves; wave w folds 32-key chunk
-// 4*split + w of the unit's kept list (block slot chunk/2, half chunk%2); the
-// workgroup merges its 4 pieces in LDS in wave order and writes one partial.
-__global__ __launch_bounds__(256) void decode_partial_kernel(AttnArgs a, int n_split) {
+// Decode: the kept list of a (row, key head) is split into top_k partials of
+// one block (two 32-key chunks) each; wave `slot` folds partial `slot`, with
+// both chunks' loads in flight together, and writes (max, sum, weighted
+// values) to the workspace.  Workgroups of 4 waves take 4 consecutive slots;
+// the last workgroup of a unit to finish (a per-unit counter) merges all its
+// partials, in slot order, with log-sum-exp weights.  The partials and their
+// merge order depend only on top_k, so a row's bits never depend on the rest
+// of the batch or on which workgroup finished last.
+__global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
-    __shared__ float mrg[kDecodeWaves][34][kWave];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int is_last;
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
-    const int64_t unit = blockIdx.x / n_split;
-    const int split = blockIdx.x % n_split;
+    const int64_t unit = blockIdx.x / wg_per_unit;
+    const int split = blockIdx.x % wg_per_unit;
     if (unit >= (int64_t)a.b.total_rows * a.H) return;
     const Unit u = make_unit(a, unit);
+    const int hq = a.H * kGroup;
+    float *part_unit = a.ws_part + unit * a.top_k * (int64_t)kPartialFloats;
+    const int slot = split * 4 + wave;
 
-    Softmax st;
-    softmax_init(st);
-    const int chunk = split * kDecodeWaves + wave;
-    const int slot = chunk >> 1, half = chunk & 1;
-    if (u.ok && slot < a.top_k) {
-        const int b = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
-        const int kbase = b * kBlock + 32 * half;
-        if (b >= 0 && kbase <= u.p) {
+    if (slot < a.top_k) {
+        Softmax st;
+        softmax_init(st);
+        const int b = u.ok ? a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot] : -1;
+        const int kb0 = b * kBlock, kb1 = kb0 + 32;
+        if (b >= 0 && kb0 <= u.p) {
             const int64_t kv0 = a.b.kv_start[u.s];
+            const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+            const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
             u32x4 qb[4];
-            load_q(qb, a.q + ((int64_t)u.r * a.H * kGroup + u.g * kGroup) * kHeadDim);
-            attend_chunk32(st, qb, a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head,
-                           a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head, a.kv_tok, kbase, u.p,
-                           a.scale_log2, vt_all[wave]);
+            load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+            ChunkRegs ca, cb;
+            load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
+            if (kb1 <= u.p) load_chunk(cb, kseq, vseq, a.kv_tok, kb1, u.p);
+            fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave]);
+            if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave]);
         }
+        const float l = sum_over_lane_groups(st.l);
+        float *part = part_unit + slot * (int64_t)kPartialFloats;
+        if (lg == 0) {
+            part[lr] = st.m;
+            part[16 + lr] = l;
+        }
+        float *acc = part + 32 + lr * kHeadDim + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(acc + 16 * dt) = st.o[dt];
     }
-    const float l = sum_over_lane_groups(st.l);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mrg[wave][4 * dt + i][lane] = st.o[dt][i];
-    mrg[wave][32][lane] = st.m;
-    mrg[wave][33][lane] = l;
+    // Publish this workgroup's partials, count it in; the last one merges.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    if (wave != 0) return;
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.ws_count + unit, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == (unsigned)(wg_per_unit - 1);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (threadIdx.x == 0)   // leave the counter at zero for the next call
+        __hip_atomic_store(a.ws_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!u.ok) return;
 
-    float mw[kDecodeWaves], M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-        mw[w] = mrg[w][32][lane];
-        M = fmaxf(M, mw[w]);
-    }
-    float scl[kDecodeWaves], Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-        scl[w] = M == -INFINITY ? 0.f : exp2f(mw[w] - M);
-        Ls += scl[w] * mrg[w][33][lane];
-    }
-    float *part = a.ws + (unit * n_split + split) * (int64_t)kPartialFloats;
-    if (lg == 0) {
-        part[lr] = M;
-        part[16 + lr] = Ls;
-    }
-    float *acc = part + 32 + lr * kHeadDim + 4 * lg;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        floatx4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] += scl[w] * mrg[w][4 * dt + i][lane];
-        *reinterpret_cast<floatx4 *>(acc + 16 * dt) = o;
-    }
-}
-
-// Combine the n_split partials of a unit: 256 threads, thread = (head, 8 dims).
-__global__ __launch_bounds__(256) void decode_combine_kernel(AttnArgs a, int n_split) {
-    const int64_t unit = blockIdx.x;
-    if (unit >= (int64_t)a.b.total_rows * a.H) return;
-    const int g = (int)(unit / a.b.total_rows), r = (int)(unit % a.b.total_rows);
+    // Merge: thread = (head h, 8 dims), partials in slot order.  Loads go out
+    // in batches of 8 partials (no loop-carried load chains).
     const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-    const float *part = a.ws + unit * n_split * (int64_t)kPartialFloats;
-    constexpr int kMaxSplit = (kMaxTopK * 2 + kDecodeWaves - 1) / kDecodeWaves;
-    float ms[kMaxSplit];
+    float ms[kMaxTopK];
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-        ms[s] = s < n_split ? part[s * kPartialFloats + h] : -INFINITY;
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ms[s] = s < a.top_k ? part_unit[s * kPartialFloats + h] : -INFINITY;
         M = fmaxf(M, ms[s]);
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float accv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float Ls = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s) {
-            if (s >= n_split) break;
-            const float *ps = part + s * kPartialFloats;
-            const float w = exp2f(ms[s] - M);
-            Ls += w * ps[16 + h];
-            const floatx4 x0 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0);
-            const floatx4 x1 = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0 + 4);
+        for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
+            if (s0 >= a.top_k) break;
+            float lv[8];
+            floatx4 x0[8], x1[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] += w * x0[i];
-                acc[4 + i] += w * x1[i];
+            for (int q = 0; q < 8; ++q) {
+                // an empty partial (no visible key) or a slot past top_k has weight 0;
+                // read slot 0 instead so every load stays in bounds and finite
+                const bool use = s0 + q < a.top_k && ms[s0 + q] != -INFINITY;
+                const float *ps = part_unit + (use ? s0 + q : 0) * kPartialFloats;
+                lv[q] = ps[16 + h];
+                x0[q] = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0);
+                x1[q] = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0 + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool use = s0 + q < a.top_k && ms[s0 + q] != -INFINITY;
+                if (!use) continue;
+                const float w = exp2f(ms[s0 + q] - M);
+                Ls += w * lv[q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    accv[i] += w * x0[q][i];
+                    accv[4 + i] += w * x1[q][i];
+                }
             }
         }
     }
-    const int hq = a.H * kGroup;
-    const int hh = g * kGroup + h;
+    const int hh = u.g * kGroup + h;
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    u32x4 w;
+    u32x4 wv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-    *reinterpret_cast<u32x4 *>(a.out + ((int64_t)r * hq + hh) * kHeadDim + d0) = w;
-    if (a.lse && d0 == 0) a.lse[(int64_t)r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) wv[i] = pack_bf16x2(accv[2 * i] * inv, accv[2 * i + 1] * inv);
+    *reinterpret_cast<u32x4 *>(a.out + ((int64_t)u.r * hq + hh) * kHeadDim + d0) = wv;
+    if (a.lse && d0 == 0) a.lse[(int64_t)u.r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
@@ -371,12 +374,8 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
 
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
-    const int n_split = decode_splits(a.top_k);
-    hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)(units * n_split)), dim3(256), 0, st, a,
-                       n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)units), dim3(256), 0, st, a, n_split);
+    const int wg = decode_wg_per_unit(a.top_k);
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
     return hipGetLastError();
 }
 

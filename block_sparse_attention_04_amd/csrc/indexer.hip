@@ -31,19 +31,25 @@ namespace msa {
 
 // Block max of one 16-row x 64-key MFMA result (4 M-tiles), causal-masked
 // against the lane's row position when the block reaches past the wave's
-// first row.
+// first row.  need_mask is wave-uniform: blocks left of the diagonal take the
+// plain max tree.
 __device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0, int p_row,
                                               bool need_mask) {
-    const int lg = (threadIdx.x & 63) >> 4;
-    float m = -INFINITY;
+    float m;
+    if (__builtin_expect(need_mask, 0)) {
+        const int lg = (threadIdx.x & 63) >> 4;
+        m = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v = acc[mt][i];
-            if (need_mask && key0 + 16 * mt + 4 * lg + i > p_row) v = -INFINITY;
-            m = fmaxf(m, v);
-        }
+            for (int i = 0; i < 4; ++i)
+                m = fmaxf(m, key0 + 16 * mt + 4 * lg + i > p_row ? -INFINITY : acc[mt][i]);
+    } else {
+        float t[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            t[mt] = fmaxf(fmaxf(acc[mt][0], acc[mt][1]), fmaxf(acc[mt][2], acc[mt][3]));
+        m = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     }
     return max_over_lane_groups(m);
 }
@@ -223,9 +229,12 @@ __device__ __forceinline__ float window_block_max(const u32x4 (&av)[4][2], u32x4
     return block_max_64(acc, b * kBlock, prow, b * kBlock + kBlock - 1 > p_first);
 }
 
-// Each wave streams a range of blocks_per_wave (a multiple of 4) blocks, two
-// at a time with both blocks' loads in flight before the first MFMA.
-__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int blocks_per_wave) {
+// Each wave owns 4 consecutive blocks: all their loads go out before the
+// first MFMA (a block past the sequence re-reads its last computed block and
+// is discarded), and lane group lg ends up holding block b_begin + lg.
+constexpr int kWindowBlocks = 4;
+
+__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lg = lane >> 4, lr = lane & 15;
     const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
@@ -234,58 +243,47 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, int bloc
     const int rows_s = a.b.cu_rows[s + 1] - row0;
     const int L = a.b.seq_lens[s];
     if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;
-    const int b_begin = (blockIdx.x * 4 + wave) * blocks_per_wave;
-    const int b_end = min(b_begin + blocks_per_wave, a.bs_stride);
+    const int b_begin = (blockIdx.x * 4 + wave) * kWindowBlocks;
+    const int b_end = min(b_begin + kWindowBlocks, a.bs_stride);
     if (b_begin >= b_end) return;
     const int nb_seq = (L - 1) / kBlock + 1;
-    const int b_cmp_end = min(b_end, nb_seq);
+    const int nblk = min(b_end, nb_seq) - b_begin;    // blocks with visible keys
     const int64_t kv0 = a.b.kv_start[s];
 
     const bool rvalid = lr < rows_s;
     const int p_first = L - rows_s;
     const int prow = p_first + lr;
-    u32x4 bq0 = zero16(), bq1 = zero16();
-    if (rvalid) {
-        const uint16_t *src = a.iq + ((int64_t)(row0 + lr) * a.H + g) * kIndexDim + 16 * lg;
-        bq0 = load16(src);
-        bq1 = load16(src + 8);
-    }
-    const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
-
-    float held = -INFINITY;
-    for (int b = b_begin; b < b_end; b += 2) {
-        float m0 = -INFINITY, m1 = -INFINITY;
-        if (b + 1 < b_cmp_end) {
-            u32x4 av0[4][2], av1[4][2];
-            window_load_block(av0, ik_g, kv0, a.ik_tok, b, L, lr);
-            window_load_block(av1, ik_g, kv0, a.ik_tok, b + 1, L, lr);
-            m0 = window_block_max(av0, bq0, bq1, b, prow, p_first);
-            m1 = window_block_max(av1, bq0, bq1, b + 1, prow, p_first);
-        } else if (b < b_cmp_end) {
-            u32x4 av0[4][2];
-            window_load_block(av0, ik_g, kv0, a.ik_tok, b, L, lr);
-            m0 = window_block_max(av0, bq0, bq1, b, prow, p_first);
+    float mine = -INFINITY;
+    if (nblk > 0) {
+        u32x4 bq0 = zero16(), bq1 = zero16();
+        if (rvalid) {
+            const uint16_t *src = a.iq + ((int64_t)(row0 + lr) * a.H + g) * kIndexDim + 16 * lg;
+            bq0 = load16(src);
+            bq1 = load16(src + 8);
         }
-        if (lg == (b & 3)) held = m0;
-        if (lg == ((b + 1) & 3)) held = m1;
-        // blocks come in pairs starting at a multiple of 4: store after the odd
-        // block of the second pair, or at the end of the range
-        const int last = min(b + 1, b_end - 1);
-        if ((last & 3) == 3 || last == b_end - 1) {
-            const int blk = (last & ~3) + lg;
-            if (rvalid && blk >= b_begin && blk <= last)
-                a.scores[((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk] = held;
+        const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
+        u32x4 av[kWindowBlocks][4][2];
+#pragma unroll
+        for (int q = 0; q < kWindowBlocks; ++q)
+            window_load_block(av[q], ik_g, kv0, a.ik_tok, b_begin + min(q, nblk - 1), L, lr);
+#pragma unroll
+        for (int q = 0; q < kWindowBlocks; ++q) {
+            if (q < nblk) {
+                const float m = window_block_max(av[q], bq0, bq1, b_begin + q, prow, p_first);
+                if (lg == q) mine = m;
+            }
         }
     }
+    const int blk = b_begin + lg;
+    if (rvalid && blk < b_end) a.scores[((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk] = mine;
 }
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
     const int gz = a.b.n_seqs * a.H;
     if (a.b.max_rows <= 16) {
-        const int bpw = 4;                       // blocks per wave (multiple of 4)
-        const int per_wg = bpw * 4;
+        const int per_wg = kWindowBlocks * 4;
         dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, gz);
-        hipLaunchKernelGGL(index_scores_window, grid, dim3(256), 0, st, a, bpw);
+        hipLaunchKernelGGL(index_scores_window, grid, dim3(256), 0, st, a);
     } else {
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;

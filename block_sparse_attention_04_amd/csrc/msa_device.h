@@ -17,6 +17,7 @@ constexpr int kHeadDim = 128;   // q/k/v head dim
 constexpr int kIndexDim = 64;   // indexer dim
 constexpr int kBlock = 64;      // keys per block
 constexpr int kMaxTopK = 32;
+constexpr int kMaxSelectBlocks = 16384;  // selection stages a row's block scores in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -24,16 +25,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, on the
+// hardware converter (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const floatx2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // D = A * B + C on one 16x16x32 bf16 MFMA.

@@ -42,14 +42,18 @@ struct AttnArgs {
     const int32_t *idx;          // [total_rows, H, top_k]
     uint16_t *out;               // [total_rows, H*16, 128]
     float *lse;                  // [total_rows, H*16] or null
-    float *ws;                   // decode partials
+    unsigned *ws_count;          // decode: one arrival counter per (row, key head)
+    float *ws_part;              // decode: top_k partials per (row, key head)
 };
 
-// Decode split-K geometry: every wave owns 32 keys, a workgroup of 4 waves
-// merges its pieces into one partial; a partial is m[16], l[16], acc[16][128].
-constexpr int kDecodeWaves = 4;
+// Decode partial: m[16], l[16], acc[16][128] (fp32) for one kept block.
 constexpr int kPartialFloats = 16 + 16 + 16 * 128;
-inline int decode_splits(int top_k) { return (top_k * 2 + kDecodeWaves - 1) / kDecodeWaves; }
+inline int decode_wg_per_unit(int top_k) { return (top_k + 3) / 4; }
+// Workspace: counters (one uint32 per unit, region rounded to 256 bytes), then partials.
+inline size_t decode_count_bytes(int64_t units) { return (size_t)((units * 4 + 255) / 256 * 256); }
+inline size_t decode_workspace_bytes(int64_t units, int top_k) {
+    return decode_count_bytes(units) + (size_t)units * top_k * kPartialFloats * sizeof(float);
+}
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);

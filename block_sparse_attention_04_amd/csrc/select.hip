@@ -44,123 +44,199 @@ __device__ __forceinline__ int wave_sum_int(int x) {
     return x;
 }
 
-// Largest T with #{lanes: v >= T} >= k (the k-th largest of 64 values).
+// Largest T with #{lanes: v >= T} >= k (the k-th largest of 64 values),
+// two bits per step: three independent ballots decide bits (b+1, b).
 __device__ __forceinline__ uint32_t kth_largest_wave(uint32_t v, int k) {
     uint32_t t = 0u;
 #pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = t | (1u << bit);
-        if (__popcll(__ballot(v >= c)) >= k) t = c;
+    for (int shift = 30; shift >= 0; shift -= 2) {
+        const uint32_t c1 = t | (1u << shift), c2 = t | (2u << shift), c3 = t | (3u << shift);
+        const int n3 = __popcll(__ballot(v >= c3));
+        const int n2 = __popcll(__ballot(v >= c2));
+        const int n1 = __popcll(__ballot(v >= c1));
+        t = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : t;
     }
     return t;
 }
 
-// Scores of the unit live in LDS (one burst of independent loads) when they
-// fit the per-wave capacity `cap`; otherwise every pass reads them from global
-// memory (L2-resident after the first).
-template <bool kStaged>
-__device__ __forceinline__ void select_unit(const SelectArgs &a, const float *S, float *lds, int n,
-                                            int need, int32_t *out, uint32_t *cand) {
+// Top-`need` of keys[0..n) (order keys in LDS, n > need) for one wave, ties
+// to the lower index.  idx_of(j) gives element j's block index; emit(pos, key,
+// idx) receives the kept elements with pos = 0..need-1 in index order.
+// ck/ci: this wave's 64-entry LDS scratch for candidates.
+template <class IdxOf, class Emit>
+__device__ __forceinline__ void wave_top(const uint32_t *keys, int n, int need, IdxOf idx_of, Emit emit,
+                                         uint32_t *ck, int32_t *ci) {
     const int lane = threadIdx.x & 63;
-    auto key_at = [&](int b) -> uint32_t { return order_key(kStaged ? lds[b] : S[b]); };
-
+    if (n <= kWave) {
+        // one key per lane, already in index order: T directly
+        const uint32_t cv = lane < n ? keys[lane] : 0u;
+        const uint32_t t = kth_largest_wave(cv, need);
+        const int need_eq = need - __popcll(__ballot(cv > t));
+        const uint64_t em = __ballot(lane < n && cv == t);
+        const bool take = cv > t || (lane < n && cv == t && lanes_below(em) < need_eq);
+        const uint64_t tm = __ballot(take);
+        if (take) emit(lanes_below(tm), cv, idx_of(lane));
+        return;
+    }
     uint32_t lmax = 0u;
 #pragma unroll 8
-    for (int b = lane; b < n; b += kWave) lmax = max(lmax, key_at(b));
+    for (int j = lane; j < n; j += kWave) lmax = max(lmax, keys[j]);
     const uint32_t t0 = kth_largest_wave(lmax, need);
 
     int c = 0;
-    for (int b0 = 0; b0 < n; b0 += kWave) {
-        const int b = b0 + lane;
-        const uint32_t v = b < n ? key_at(b) : 0u;
-        const bool f = b < n && v >= t0;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + lane;
+        const uint32_t v = j < n ? keys[j] : 0u;
+        const bool f = j < n && v >= t0;
         const uint64_t mk = __ballot(f);
         const int pos = c + lanes_below(mk);
-        if (f && pos < kWave) cand[pos] = v;
+        if (f && pos < kWave) {
+            ck[pos] = v;
+            ci[pos] = idx_of(j);
+        }
         c += __popcll(mk);
     }
 
-    uint32_t t;
-    int n_gt;
     if (c <= kWave) {
+        // every key >= T (the need-th largest) is a candidate, kept in index order
         wave_lds_sync();
-        const uint32_t cv = lane < c ? cand[lane] : 0u;
-        t = kth_largest_wave(cv, need);
-        n_gt = __popcll(__ballot(cv > t));
-    } else {
-        t = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cb = t | (1u << bit);
-            int cnt = 0;
-#pragma unroll 8
-            for (int b = lane; b < n; b += kWave) cnt += key_at(b) >= cb;
-            if (wave_sum_int(cnt) >= need) t = cb;
-        }
+        const uint32_t cv = lane < c ? ck[lane] : 0u;
+        const int civ = lane < c ? ci[lane] : -1;
+        const uint32_t t = kth_largest_wave(cv, need);
+        const int need_eq = need - __popcll(__ballot(cv > t));
+        const uint64_t em = __ballot(lane < c && cv == t);
+        const bool take = cv > t || (lane < c && cv == t && lanes_below(em) < need_eq);
+        const uint64_t tm = __ballot(take);
+        if (take) emit(lanes_below(tm), cv, civ);
+        return;
+    }
+    // Many ties above T0: bitwise search for T over all keys, then one pass in
+    // index order.
+    uint32_t t = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cb = t | (1u << bit);
         int cnt = 0;
 #pragma unroll 8
-        for (int b = lane; b < n; b += kWave) cnt += key_at(b) > t;
-        n_gt = wave_sum_int(cnt);
+        for (int j = lane; j < n; j += kWave) cnt += keys[j] >= cb;
+        if (wave_sum_int(cnt) >= need) t = cb;
     }
-
-    const int need_eq = need - n_gt;
+    int cnt = 0;
+#pragma unroll 8
+    for (int j = lane; j < n; j += kWave) cnt += keys[j] > t;
+    const int need_eq = need - wave_sum_int(cnt);
     int taken = 0, eq_seen = 0;
-    for (int b0 = 0; b0 < n; b0 += kWave) {
-        const int b = b0 + lane;
-        const bool valid = b < n;
-        const uint32_t v = valid ? key_at(b) : 0u;
-        const bool gt = valid && v > t;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool valid = j < n;
+        const uint32_t v = valid ? keys[j] : 0u;
         const bool eq = valid && v == t;
         const uint64_t em = __ballot(eq);
-        const bool take = gt || (eq && eq_seen + lanes_below(em) < need_eq);
+        const bool take = (valid && v > t) || (eq && eq_seen + lanes_below(em) < need_eq);
         const uint64_t tm = __ballot(take);
-        if (take) out[taken + lanes_below(tm)] = b;
+        if (take) emit(taken + lanes_below(tm), v, idx_of(j));
         taken += __popcll(tm);
         eq_seen += __popcll(em);
     }
-    if (lane == 0) out[need] = n;  // the local block, largest index, last
 }
 
-__global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a, int cap) {
-    extern __shared__ float dyn[];             // [4 waves][cap] staged scores
-    __shared__ uint32_t cand[4][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
-    if (unit >= (int64_t)a.b.total_rows * a.H) return;
-    const int r = (int)(unit / a.H);
-    int32_t *out = a.idx + unit * a.top_k;
+struct SelUnit {
+    int64_t unit;
+    int n;        // candidate blocks 0..n-1 (n = nb - 1); the local block is n
+    bool direct;  // nb <= top_k: keep everything, no scores needed
+    bool ok;
+};
 
+__device__ __forceinline__ SelUnit sel_unit(const SelectArgs &a, int64_t unit) {
+    SelUnit u;
+    u.unit = unit;
+    const int r = (int)(unit / a.H);
     const int s = locate_seq(a.b.cu_rows, a.b.n_seqs, r);
     const int rows_s = a.b.cu_rows[s + 1] - a.b.cu_rows[s];
     const int L = a.b.seq_lens[s];
-    if (rows_s <= 0 || rows_s > L || L > a.b.max_seq_len) return;
+    u.ok = rows_s > 0 && rows_s <= L && L <= a.b.max_seq_len;
     const int p = L - rows_s + (r - a.b.cu_rows[s]);
     const int nb = p / kBlock + 1;
+    u.n = nb - 1;
+    u.direct = nb <= a.top_k;
+    return u;
+}
 
-    if (nb <= a.top_k) {
-        if (lane < a.top_k) out[lane] = lane < nb ? lane : -1;
+// Stage order keys of scores S[0..n) into LDS (a burst of independent loads).
+__device__ __forceinline__ void stage_keys(uint32_t *dst, const float *S, int n, int from, int step) {
+#pragma unroll 16
+    for (int j = from; j < n; j += step) dst[j] = order_key(S[j]);
+}
+
+// kMulti = false: a workgroup of 4 waves takes 4 units, one wave each (many
+// units).  kMulti = true: the 4 waves share one unit (few, long units): each
+// selects the top top_k-1 of its quarter of the candidates, then wave 0
+// selects among those 4*(top_k-1) -- every kept block is in its quarter's
+// top, with the same tie order, so the result is the same.
+template <bool kMulti>
+__global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a, int cap) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t ck[4][64];
+    __shared__ int32_t ci[4][64];
+    __shared__ uint32_t mk[4 * kMaxTopK];
+    __shared__ int32_t mi[4 * kMaxTopK];
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int64_t units = (int64_t)a.b.total_rows * a.H;
+    const int64_t unit = kMulti ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave;
+    if (unit >= units) return;
+    const SelUnit u = sel_unit(a, unit);
+    if (!u.ok) return;
+    int32_t *out = a.idx + unit * a.top_k;
+    const int need = a.top_k - 1;
+    if (u.direct || need == 0) {            // all causal blocks, or only the local one
+        if ((!kMulti || wave == 0) && lane < a.top_k) out[lane] = u.direct ? (lane <= u.n ? lane : -1) : u.n;
         return;
     }
     const float *S = a.scores + unit * a.bs_stride;
-    const int n = nb - 1;          // candidates: blocks 0 .. nb-2
-    const int need = a.top_k - 1;  // how many of them to keep
-    if (n <= cap) {
-        float *lds = dyn + wave * cap;
-#pragma unroll 8
-        for (int b = lane; b < n; b += kWave) lds[b] = S[b];
+    auto to_out = [&](int pos, uint32_t, int idx) { out[pos] = idx; };
+    if (!kMulti) {
+        uint32_t *keys = dyn + wave * cap;      // cap >= every row's candidate count
+        stage_keys(keys, S, u.n, lane, kWave);
         wave_lds_sync();
-        select_unit<true>(a, S, lds, n, need, out, cand[wave]);
-    } else {
-        select_unit<false>(a, S, nullptr, n, need, out, cand[wave]);
+        wave_top(keys, u.n, need, [](int j) { return j; }, to_out, ck[wave], ci[wave]);
+        if (lane == 0) out[need] = u.n;
+        return;
     }
+    uint32_t *keys = dyn;
+    stage_keys(keys, S, u.n, threadIdx.x, 256);
+    __syncthreads();
+    const int seg = (u.n + 3) / 4;
+    const int j0 = wave * seg, n_seg = max(0, min(seg, u.n - j0));
+    uint32_t *mkw = mk + wave * need;
+    int32_t *miw = mi + wave * need;
+    if (n_seg <= need) {
+        for (int j = lane; j < need; j += kWave) {
+            mkw[j] = j < n_seg ? keys[j0 + j] : 0u;     // 0 sorts below every score
+            miw[j] = j < n_seg ? j0 + j : -1;
+        }
+    } else {
+        wave_top(keys + j0, n_seg, need, [j0](int j) { return j0 + j; },
+                 [&](int pos, uint32_t k, int idx) { mkw[pos] = k; miw[pos] = idx; }, ck[wave], ci[wave]);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    wave_top(mk, 4 * need, need, [&](int j) { return mi[j]; }, to_out, ck[0], ci[0]);
+    if (lane == 0) out[need] = u.n;
 }
 
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
-    // stage up to 4,096 candidate blocks (262,144 keys) per unit in LDS
-    const int need = (a.b.max_seq_len + kBlock - 1) / kBlock;
-    const int cap = ((min(need, 4096) + 63) / 64) * 64;
-    dim3 grid((unsigned)((units + 3) / 4));
-    hipLaunchKernelGGL(select_blocks_kernel, grid, dim3(256), (size_t)4 * cap * sizeof(float), st, a, cap);
+    const int nb_max = (a.b.max_seq_len + kBlock - 1) / kBlock;
+    const int cap = ((nb_max + 63) / 64) * 64;      // staged keys per unit (<= kMaxSelectBlocks)
+    // One wave per unit when there are many units and their 4 stages fit 64 KiB;
+    // otherwise one workgroup per unit (its stage is at most 64 KiB).
+    const bool multi = cap * 16 > 64 * 1024 || (units <= 1024 && nb_max > 256);
+    if (multi) {
+        hipLaunchKernelGGL(select_blocks_kernel<true>, dim3((unsigned)units), dim3(256),
+                           (size_t)cap * sizeof(uint32_t), st, a, cap);
+    } else {
+        hipLaunchKernelGGL(select_blocks_kernel<false>, dim3((unsigned)((units + 3) / 4)), dim3(256),
+                           (size_t)4 * cap * sizeof(uint32_t), st, a, cap);
+    }
     return hipGetLastError();
 }
 

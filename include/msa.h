@@ -66,7 +66,7 @@ typedef enum msa_status {
     MSA_OK = 0,
     MSA_ERR_INVALID = -1,      /* null pointer, negative size, inconsistent sizes */
     MSA_ERR_UNSUPPORTED = -2,  /* a shape this build has no kernel for */
-    MSA_ERR_WORKSPACE = -3,    /* decode workspace smaller than required */
+    MSA_ERR_WORKSPACE = -3,    /* decode workspace missing or too small */
     MSA_ERR_HIP = -4           /* HIP runtime error (no device, launch failure) */
 } msa_status;
 
@@ -119,7 +119,9 @@ int msa_index_scores(const msa_shape *shape, const msa_batch *batch,
  * 0..nb-1.  Output is ascending and padded with -1.
  *   block_scores fp32 [total_rows, n_kv_heads, bs_stride] (as written above)
  *   block_idx    int32 [total_rows, n_kv_heads, top_k]
- * Scores must not be NaN.
+ * Scores must not be NaN.  max_seq_len may be at most 1,048,576 keys (16,384
+ * blocks; larger returns MSA_ERR_UNSUPPORTED): a row's scores are staged in
+ * on-chip memory.
  */
 int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
                       const float *block_scores, int32_t bs_stride,
@@ -144,18 +146,26 @@ int msa_prefill(const msa_shape *shape, const msa_batch *batch,
                 int64_t kv_tok_stride, int64_t kv_head_stride,
                 const int32_t *block_idx, void *out, float *lse, void *stream);
 
-/* Bytes of workspace msa_decode needs for total_rows rows (host function). */
+/* Bytes of device workspace msa_decode needs for total_rows rows (host
+ * function; 0 for an invalid shape). */
 size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
 
 /*
  * Step 4 for decode steps and verify windows: the same result as msa_prefill
- * (within rounding), computed as split-K over the kept keys: each wave owns a
- * 32-key piece, a workgroup merges its pieces, the partials
- * (max, sum, weighted values) go to `workspace` and a combine pass merges
- * them with log-sum-exp weights.  The split depends only on top_k and block,
- * never on the batch, so a row's bits do not depend on the other rows.
- *   workspace        device scratch of >= msa_decode_workspace_bytes() bytes;
- *                    contents on entry are ignored, on return unspecified.
+ * (within rounding), computed as split-K over the kept keys.  Each kept block
+ * (two 32-key pieces) is folded by its own wave into a partial (max, sum,
+ * weighted values) in `workspace`; the last workgroup of a (row, key head) to
+ * finish merges that row's partials, in block-slot order, with log-sum-exp
+ * weights.  The split depends only on top_k, never on the batch, so a row's
+ * bits do not depend on the other rows: a verify window equals the same rows
+ * decoded one at a time, bit for bit.
+ *   workspace        device memory of >= msa_decode_workspace_bytes() bytes,
+ *                    256-byte aligned.  Its first part holds one arrival
+ *                    counter per (row, key head): it must be zero before the
+ *                    first call that uses this workspace (allocate it zeroed),
+ *                    and every completed call leaves it zero again.  If a
+ *                    launch fails, zero it again before reuse.  Calls that
+ *                    share a workspace must not run concurrently.
  * Other arguments as msa_prefill.
  */
 int msa_decode(const msa_shape *shape, const msa_batch *batch,

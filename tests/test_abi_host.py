@@ -112,19 +112,25 @@ def test_pointer_stride_and_alignment_checks():
     assert "bs_stride" in _err()
 
 
-def test_decode_workspace_size_and_check():
+def test_decode_workspace_size_and_checks():
     L = msa.lib()
     sh = msa.make_shape(4, top_k=16)
-    per_row = 4 * 8 * (16 + 16 + 16 * 128) * 4     # heads * splits * partial floats * 4 bytes
-    assert msa.msa_decode_workspace_bytes(sh, 3) == 3 * per_row
-    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 4 * 1 * 2080 * 4
+    per_unit = 16 * (16 + 16 + 16 * 128) * 4      # top_k partials per (row, key head)
+    counters = lambda units: (units * 4 + 255) // 256 * 256
+    assert msa.msa_decode_workspace_bytes(sh, 3) == counters(12) + 12 * per_unit
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 256 + 4 * 2080 * 4
     assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=40), 1) == 0
     b = FakeBatch(total_rows=4)
-    rc = L.msa_decode(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096),
-                      ctypes.c_void_p(8192), ctypes.c_void_p(16384), 512, 128,
-                      ctypes.c_void_p(32768), ctypes.c_void_p(65536), None,
-                      ctypes.c_void_p(131072), 3 * per_row, None)
-    assert rc == -3 and "workspace" in _err()
+    need = msa.msa_decode_workspace_bytes(sh, 4)
+    args = lambda ws, nbytes, hs=128, out=65536: (
+        ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), ctypes.c_void_p(8192),
+        ctypes.c_void_p(16384), 512, hs, ctypes.c_void_p(32768),
+        ctypes.c_void_p(out) if out else None, None, ctypes.c_void_p(ws) if ws else None, nbytes, None)
+    assert L.msa_decode(*args(131072, need - 1)) == -3 and "workspace" in _err()
+    assert L.msa_decode(*args(0, need)) == -3
+    assert L.msa_decode(*args(131072 + 16, need)) == -1 and "aligned" in _err()
+    assert L.msa_decode(*args(131072, need, hs=64)) == -1 and "kv strides" in _err()
+    assert L.msa_decode(*args(131072, need, out=0)) == -1
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
@@ -138,3 +144,12 @@ def test_binding_raises_on_error():
     with pytest.raises(msa.MsaError) as ei:
         msa._check(-2)
     assert ei.value.status == -2
+
+
+def test_select_rejects_contexts_beyond_the_staging_limit():
+    L = msa.lib()
+    sh = msa.make_shape(1)
+    b = FakeBatch(max_seq_len=1048576 + 64)
+    rc = L.msa_select_blocks(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), 16385,
+                             ctypes.c_void_p(8192), None)
+    assert rc == -2 and "16384" in _err()

@@ -181,3 +181,39 @@ def test_strided_kv_views():
         a = gpu_run(case, mode, t=t)
         b = gpu_run(case, mode, t=t2)
         assert torch.equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("top_k", [1, 2, 16, 32])
+def test_selection_workgroup_mode(top_k):
+    """Few (row, key head) units with more than 256 blocks: a workgroup takes
+    one unit, selects per quarter and merges; the result must be the oracle's."""
+    case = make_case("wgsel", [20000, 17000], [3, 2], 2, seed=130 + top_k, top_k=top_k)
+    full_check(case, "decode", top_k=top_k)
+    # all scores equal: the lowest top_k-1 blocks plus the local one
+    case.iq = torch.zeros_like(case.iq)
+    g = gpu_run(case, "decode", top_k=top_k)
+    nb = oracle.causal_blocks(case)
+    for r in range(case.total_rows):
+        want = list(range(top_k - 1)) + [int(nb[r]) - 1]
+        for h in range(2):
+            assert list(g["block_idx"].numpy()[r, h]) == want
+
+
+def test_decode_workspace_reuse():
+    """One workspace across several msa_decode calls: the arrival counters
+    return to zero after every call, so repeated calls give the same bits."""
+    case = make_case("wsreuse", [9000, 3000], [5, 3], 2, seed=140)
+    shape = shape_of(case)
+    batch = msa.Batch(case.seq_lens, case.rows)
+    t = device_tensors(case)
+    first = msa.run_path(shape, batch, t, "prefill")          # block_idx from the path
+    ws = msa.decode_workspace(shape, batch.total_rows)
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(t["q"])
+        msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], first["block_idx"], o, workspace=ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    units = batch.total_rows * case.n_kv_heads
+    assert int(ws[:units * 4].view(torch.int32).abs().sum().item()) == 0
