@@ -75,6 +75,45 @@ def kept_kv_bytes(case):
     return total
 
 
+PROFILE_KERNELS = {"chunk/attention": "prefill_kernel", "chunk/index_scores": "index_scores_tiled",
+                   "long/index_scores": "index_scores_window"}
+
+
+def source_digest() -> str:
+    """SHA-256 over the library's kernel sources: counters taken on other
+    sources no longer describe the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_04_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str):
+    """Bytes past L2 per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by its copy-kernel calibration), or
+    None when no summary exists or the kernel sources changed since."""
+    short = PROFILE_KERNELS.get(kernel)
+    if short is None:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{short}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 class Timed:
     """Collects HIP-event pairs around library calls on the current stream."""
 
@@ -135,6 +174,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device copy of this size (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters in a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -215,7 +257,7 @@ def main():
             kernels.append(ent)
     dom = max(kernels, key=lambda e: e["ms"])
     roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roofline.update(kernel=dom["kernel"], traffic=None)
+    roofline.update(kernel=dom["kernel"], traffic=profiled_traffic(dom["kernel"]))
 
     t_chunk = sum(kms[f"chunk/{k}"] for k in ("index_scores", "select_blocks", "attention"))
     t_long = sum(kms[f"long/{k}"] for k in ("index_scores", "select_blocks", "attention"))
@@ -241,6 +283,15 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if args.copy_calibration_mib:
+        # an elementwise kernel that reads n bytes and writes n bytes once
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cases, args.cpu_threads)
