@@ -80,13 +80,14 @@ PROFILE_KERNELS = {"chunk/attention": "prefill_kernel", "chunk/index_scores": "i
 
 
 def source_digest() -> str:
-    """SHA-256 over the library's kernel sources: counters taken on other
-    sources no longer describe the kernels that run."""
+    """SHA-256 over the library's kernel sources and build flags: counters
+    taken on other sources no longer describe the kernels that run."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "block_sparse_attention_04_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    pkg = os.path.join(ROOT, "block_sparse_attention_04_amd")
+    files = [os.path.join("csrc", n) for n in sorted(os.listdir(os.path.join(pkg, "csrc")))] + ["build.py"]
+    for name in files:
+        with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
