@@ -17,9 +17,10 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.hip", "indexer.hip", "select.hip", "attention.hip"]
 # Per-source extras.  indexer: MFMA accumulators in ordinary VGPRs, so the
-# max-pool reads them without v_accvgpr copies (measured faster; the
+# max-pool reads them without v_accvgpr copies, and maxima skip NaN
+# canonicalisation (scores are finite or -inf) -- measured faster; the
 # attention kernels measured slower with it).
-SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 ARCH = "gfx950"
 
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -80,24 +80,12 @@ __device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, c
     }
 }
 
-// Fold one loaded 32-key chunk [kbase, kbase + 32) (keys <= p visible) into
-// st; vt is this wave's 8 KiB LDS tile.
-__device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
-                                           int kbase, int p, float scale_log2, uint8_t *vt) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-    floatx4 sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(c.ka[mt][s], qb[s], acc);
-        sacc[mt] = acc;
-    }
-
-    // V^T into LDS.  Key k of the chunk goes to slot 8*((k%16)/4) + 4*(k/16) + k%4,
-    // so lane group lg's k-slots (keys 4lg..4lg+3 and 16+4lg..16+4lg+3) are
-    // the 8 contiguous slots of group lg.  Keys 4kg..4kg+3 share one 8-byte
-    // word per dim.
+// Write one loaded chunk's V^T into this wave's 8 KiB LDS tile.  Key k of the
+// chunk goes to slot 8*((k%16)/4) + 4*(k/16) + k%4, so lane group lg's
+// k-slots (keys 4lg..4lg+3 and 16+4lg..16+4lg+3) are the 8 contiguous slots of
+// group lg.  Keys 4kg..4kg+3 share one 8-byte word per dim.
+__device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
+    const int lane = threadIdx.x & 63;
     const int kg = lane >> 3, dc = lane & 7;
     const int grp = kg & 3, half = kg >> 2;
 #pragma unroll
@@ -114,7 +102,21 @@ __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], co
         const int d = 16 * dc + t;
         *reinterpret_cast<uint2 *>(vt + vt_offset(d, grp) + 8 * half) = make_uint2(w0, w1);
     }
+}
 
+// Fold the chunk [kbase, kbase + 32) (keys <= p visible) into st: K operands
+// from registers, V^T from the LDS tile (already staged and synced).
+__device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], const u32x4 (&ka)[2][4],
+                                            int kbase, int p, float scale_log2, const uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    floatx4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
+        sacc[mt] = acc;
+    }
     // Online softmax over this lane's 8 keys of head lr.
     float z[2][4];
     float mx = -INFINITY;
@@ -145,13 +147,19 @@ __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], co
     for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
     const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
-
-    wave_lds_sync();
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
         const u32x4 va = *reinterpret_cast<const u32x4 *>(vt + vt_offset(16 * dt + lr, lg));
         st.o[dt] = mfma_16x16x32(va, pb, st.o[dt]);
     }
+}
+
+// Fold one loaded 32-key chunk into st (stage V^T, fold, release the tile).
+__device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
+                                           int kbase, int p, float scale_log2, uint8_t *vt) {
+    stage_v(c, vt);
+    wave_lds_sync();
+    fold_staged(st, qb, c.ka, kbase, p, scale_log2, vt);
     wave_lds_sync();   // reads finish before the next chunk overwrites the tile
 }
 
@@ -183,15 +191,16 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
     return u;
 }
 
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
-    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int lg = lane >> 4, lr = lane & 15;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
-    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+// Prefill.  One wave per (row, key head): it holds the group's 16 query heads
+// (so every kept block is read once for all of them) and walks the row's kept
+// blocks in ascending order, 32 keys at a time, with the next chunk's K/V
+// loads in flight while the current one is folded.  A row's bits depend only
+// on its own blocks and their order.  Consecutive units are consecutive rows
+// of one key head, so a workgroup's waves share their local blocks.
+__device__ __forceinline__ void prefill_unit(const AttnArgs &a, int64_t unit, uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     const Unit u = make_unit(a, unit);
     if (!u.ok) return;
-
     const int hq = a.H * kGroup;
     const int64_t kv0 = a.b.kv_start[u.s];
     const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
@@ -199,12 +208,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     u32x4 qb[4];
     load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
     // Lane t holds kept block t; read with v_readlane (loaded before the
-    // pipelined loop's explicit wait, so the loop never waits on it).
+    // pipelined loop, so the loop never waits on it).
     const int32_t *sel = a.idx + ((int64_t)u.r * a.H + u.g) * a.top_k;
     const int my_b = lane < a.top_k ? sel[lane] : -1;
 
-    // Walk the kept blocks in list (ascending) order, 32 keys at a time, with
-    // the next chunk's K/V loads in flight while the current one is folded.
     Softmax st;
     softmax_init(st);
     int t = 0, half = 0;
@@ -221,11 +228,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
             if (kb >= 0) return kb;
         }
     };
-    force_ready(my_b);                   // the block list has arrived
+    force_ready(my_b);
     int kb0 = chunk_base(0, 0);
     if (kb0 < 0) kb0 = next_chunk();
     ChunkRegs ca, cb;
-    uint8_t *vt = vt_all[wave];
     if (kb0 >= 0) load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
 #pragma unroll
     for (int s = 0; s < 4; ++s) force_ready(qb[s]);   // q complete before the loop
@@ -250,6 +256,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
         *reinterpret_cast<uint2 *>(dst + 16 * dt) = w;
     }
     if (a.lse && lg == 0) a.lse[(int64_t)u.r * hq + h] = l > 0.f ? (st.m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    const int wave = uniform(threadIdx.x >> 6);
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
+    if (unit < (int64_t)a.b.total_rows * a.H) prefill_unit(a, unit, vt_all[wave]);
 }
 
 // Decode: the kept list of a (row, key head) is split into top_k partials of
