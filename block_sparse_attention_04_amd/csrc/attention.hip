@@ -289,14 +289,17 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     if (slot < a.top_k) {
         Softmax st;
         softmax_init(st);
-        const int b = u.ok ? a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot] : -1;
+        // the block index, q and the sequence's first key do not depend on one
+        // another: issue them together (in bounds for every unit of the grid)
+        const int b_raw = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
+        const int64_t kv0 = a.b.kv_start[u.s];
+        u32x4 qb[4];
+        load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+        const int b = u.ok ? b_raw : -1;
         const int kb0 = b * kBlock, kb1 = kb0 + 32;
         if (b >= 0 && kb0 <= u.p) {
-            const int64_t kv0 = a.b.kv_start[u.s];
             const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
             const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
-            u32x4 qb[4];
-            load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
             ChunkRegs ca, cb;
             load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
             if (kb1 <= u.p) load_chunk(cb, kseq, vseq, a.kv_tok, kb1, u.p);

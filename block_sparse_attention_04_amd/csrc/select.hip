@@ -183,6 +183,15 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a, int ca
     const int64_t units = (int64_t)a.b.total_rows * a.H;
     const int64_t unit = kMulti ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave;
     if (unit >= units) return;
+    // Stage the unit's scores before its metadata arrives, so both go out in one
+    // round of loads.  min(cap, bs_stride) entries stay inside the unit's row and
+    // cover every causal block; entries past the row's count are never read.
+    {
+        const float *S = a.scores + unit * a.bs_stride;
+        const int n_stage = min(cap, a.bs_stride);
+        if (kMulti) stage_keys(dyn, S, n_stage, threadIdx.x, 256);
+        else stage_keys(dyn + wave * cap, S, n_stage, lane, kWave);
+    }
     const SelUnit u = sel_unit(a, unit);
     if (!u.ok) return;
     int32_t *out = a.idx + unit * a.top_k;
@@ -191,18 +200,15 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a, int ca
         if ((!kMulti || wave == 0) && lane < a.top_k) out[lane] = u.direct ? (lane <= u.n ? lane : -1) : u.n;
         return;
     }
-    const float *S = a.scores + unit * a.bs_stride;
     auto to_out = [&](int pos, uint32_t, int idx) { out[pos] = idx; };
     if (!kMulti) {
         uint32_t *keys = dyn + wave * cap;      // cap >= every row's candidate count
-        stage_keys(keys, S, u.n, lane, kWave);
         wave_lds_sync();
         wave_top(keys, u.n, need, [](int j) { return j; }, to_out, ck[wave], ci[wave]);
         if (lane == 0) out[need] = u.n;
         return;
     }
     uint32_t *keys = dyn;
-    stage_keys(keys, S, u.n, threadIdx.x, 256);
     __syncthreads();
     const int seg = (u.n + 3) / 4;
     const int j0 = wave * seg, n_seg = max(0, min(seg, u.n - j0));
