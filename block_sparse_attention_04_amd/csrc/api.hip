@@ -99,6 +99,9 @@ int check_kv(const void *k, const void *v, int64_t tok, int64_t head, int n_kv_h
                     (long long)tok, (long long)head, msa::kHeadDim);
     if (!aligned16(k) || !aligned16(v) || (tok * 2) % 16 || (head * 2) % 16)
         return fail(MSA_ERR_INVALID, "k/v rows must be 16-byte aligned");
+    if (tok > msa::kMaxKvTokStride)   // the kernels address 32 tokens with 32-bit offsets
+        return fail(MSA_ERR_UNSUPPORTED, "kv token stride %lld above %lld elements", (long long)tok,
+                    (long long)msa::kMaxKvTokStride);
     return MSA_OK;
 }
 

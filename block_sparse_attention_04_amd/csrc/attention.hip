@@ -17,8 +17,9 @@
 // P^T operand layout of the second product, so probabilities go from the
 // softmax straight into the MFMA without leaving registers, and the running
 // max / sum / rescale of a head stay inside its 4 lanes.  V is written to LDS
-// transposed (d-major, keys permuted to the lanes' k-slot order, 16-byte
-// groups XOR-swizzled) so each V^T operand is one conflict-free 16-byte read.
+// row-major (one 256-byte row per key, 32-byte column blocks XOR-swizzled by
+// key mod 8) and each V^T operand is gathered by two transposing LDS reads
+// (ds_read_b64_tr_b16), with no repacking in registers.
 // Softmax runs in base 2 on scale*log2(e)-prescaled scores.
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -38,9 +39,20 @@ __device__ __forceinline__ void softmax_init(Softmax &st) {
     st.l = 0.f;
 }
 
-// Byte offset of 16-byte group `grp` (of 4) in row d of the transposed V tile.
-__device__ __forceinline__ int vt_offset(int d, int grp) {
-    return d * 64 + ((grp ^ (((d >> 2) ^ (d >> 4)) & 3)) << 4);
+// V tile of one 32-key chunk in LDS: key k's 256-byte row at k*256, its
+// 16-byte column unit u (dims 8u..8u+7) at unit u ^ (2 * (k % 8)).  With this
+// swizzle the stores below and the transposing reads in fold_staged touch
+// distinct banks.
+__device__ __forceinline__ int v_unit(int key, int u) { return u ^ (2 * (key & 7)); }
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4a + c receives element c
+// of the 4-element (8-byte) pieces addressed by lanes a, a+4, a+8, a+12.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v *)(p));
+    return make_uint2((uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16),
+                      (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16));
 }
 
 // Query B operand: head (lane % 16), dims 32*(lane/16) + 8*s + (0..7).
@@ -51,56 +63,74 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[4], const uint16_t *qrow_head
     for (int s = 0; s < 4; ++s) qb[s] = load16(src + 8 * s);
 }
 
+// q of one row in LDS: 16 heads x 128 dims bf16, head rows padded to 272 B so
+// the 16 heads of one operand read fall in different banks.
+constexpr int kQRowBytes = 272;
+constexpr float kLazyLog2 = 8.f;   // weights stay <= 256 between rescales
+constexpr int kQTileBytes = kGroup * kQRowBytes;
+
+// Copy the row's q (16 heads) from global memory into its LDS tile.
+__device__ __forceinline__ void stage_q(uint8_t *qt, const uint16_t *qrow_head0) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int e = s * kWave + lane;            // 16-byte piece e of 256
+        const int h = e >> 4, c = e & 15;
+        *reinterpret_cast<u32x4 *>(qt + h * kQRowBytes + c * 16) = load16(qrow_head0 + h * kHeadDim + 8 * c);
+    }
+}
+
+// The query B operand (as load_q) from an LDS tile.
+__device__ __forceinline__ void read_q(u32x4 (&qb)[4], const uint8_t *qt) {
+    const int lane = threadIdx.x & 63;
+    const uint8_t *src = qt + (lane & 15) * kQRowBytes + 64 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const u32x4 *>(src + 16 * s);
+}
+
 // Registers of one 32-key chunk: K as MFMA A operands (key kbase + 16*mt +
-// lane%16, dims 32*(lane/16) + 8*s) and V rows (keys kbase + 4*(lane/8) +
-// 0..3, dims 16*(lane%8) + 0..15).  A key past p is read from key p instead
-// (always in bounds): its score is masked to -inf, so its weight is 0.
+// lane%16, dims 32*(lane/16) + 8*s) and V pieces (keys kbase + 4*(lane/8) +
+// kk, 16-byte units lane%8 and lane%8 + 8).  A key past p is read from key p
+// instead (always in bounds): its score is masked to -inf, so its weight is 0.
 struct ChunkRegs {
     u32x4 ka[2][4];
     u32x4 vr[4][2];
 };
 
+// Addressing: the chunk's first key is a wave-uniform base; each lane adds a
+// 32-bit byte offset (a chunk spans 32 tokens, so offsets stay small).
 __device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, const uint16_t *vseq,
                                            int64_t tok, int kbase, int p) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    const int last = p - kbase;                       // keys past it read key p instead
+    const uint32_t tok_bytes = (uint32_t)tok * 2u;
+    const char *kb = reinterpret_cast<const char *>(kseq + (int64_t)kbase * tok);
+    const char *vb = reinterpret_cast<const char *>(vseq + (int64_t)kbase * tok);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const int key = min(kbase + 16 * mt + lr, p);
-        const uint16_t *src = kseq + (int64_t)key * tok + 32 * lg;
+        const uint32_t off = (uint32_t)min(16 * mt + lr, last) * tok_bytes + 64u * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) c.ka[mt][s] = load16(src + 8 * s);
+        for (int s = 0; s < 4; ++s) c.ka[mt][s] = *reinterpret_cast<const u32x4 *>(kb + off + 16 * s);
     }
     const int kg = lane >> 3, dc = lane & 7;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const int key = min(kbase + 4 * kg + kk, p);
-        const uint16_t *src = vseq + (int64_t)key * tok + 16 * dc;
-        c.vr[kk][0] = load16(src);
-        c.vr[kk][1] = load16(src + 8);
+        const uint32_t off = (uint32_t)min(4 * kg + kk, last) * tok_bytes + 16u * dc;
+        c.vr[kk][0] = *reinterpret_cast<const u32x4 *>(vb + off);
+        c.vr[kk][1] = *reinterpret_cast<const u32x4 *>(vb + off + 128);
     }
 }
 
-// Write one loaded chunk's V^T into this wave's 8 KiB LDS tile.  Key k of the
-// chunk goes to slot 8*((k%16)/4) + 4*(k/16) + k%4, so lane group lg's
-// k-slots (keys 4lg..4lg+3 and 16+4lg..16+4lg+3) are the 8 contiguous slots of
-// group lg.  Keys 4kg..4kg+3 share one 8-byte word per dim.
+// Write one loaded chunk's V rows into this wave's 8 KiB LDS tile.
 __device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
     const int lane = threadIdx.x & 63;
     const int kg = lane >> 3, dc = lane & 7;
-    const int grp = kg & 3, half = kg >> 2;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int reg = t >> 3, dw = (t & 7) >> 1;
-        uint32_t w0, w1;
-        if (t & 1) {
-            w0 = (c.vr[0][reg][dw] >> 16) | (c.vr[1][reg][dw] & 0xffff0000u);
-            w1 = (c.vr[2][reg][dw] >> 16) | (c.vr[3][reg][dw] & 0xffff0000u);
-        } else {
-            w0 = (c.vr[0][reg][dw] & 0xffffu) | (c.vr[1][reg][dw] << 16);
-            w1 = (c.vr[2][reg][dw] & 0xffffu) | (c.vr[3][reg][dw] << 16);
-        }
-        const int d = 16 * dc + t;
-        *reinterpret_cast<uint2 *>(vt + vt_offset(d, grp) + 8 * half) = make_uint2(w0, w1);
+    for (int kk = 0; kk < 4; ++kk) {
+        const int key = 4 * kg + kk;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            *reinterpret_cast<u32x4 *>(vt + key * 256 + 16 * v_unit(key, dc + 8 * hf)) = c.vr[kk][hf];
     }
 }
 
@@ -117,39 +147,58 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
         for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
         sacc[mt] = acc;
     }
-    // Online softmax over this lane's 8 keys of head lr.
+    // Online softmax over this lane's 8 keys of head lr.  Only the chunk that
+    // holds position p has keys to mask.
     float z[2][4];
     float mx = -INFINITY;
+    const bool edge = kbase + 31 > p;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float v = sacc[mt][i] * scale_log2;
-            if (kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
+            if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
             z[mt][i] = v;
             mx = fmaxf(mx, v);
         }
-    mx = max_over_lane_groups(mx);
-    const float m_new = fmaxf(st.m, mx);        // finite: key kbase <= p is visible
-    const float alpha = exp2f(st.m - m_new);    // 0 on the first chunk
+    mx = max_over_lane_groups(mx);              // finite: key kbase <= p is visible
+    // The reference max st.m moves only when a head's scores exceed it by more
+    // than kLazyLog2 (always on the first chunk): until then the weights are
+    // exp2(z - st.m) <= 2^kLazyLog2 and the accumulators need no rescale.  The
+    // result is the same softmax; st.m is the reference, not necessarily the max.
+    if (__ballot(mx > st.m + kLazyLog2) != 0) {
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = exp2f(st.m - m_new);    // 0 on the first chunk
+        st.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+        st.m = m_new;
+    }
     float pr[2][4];
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pr[mt][i] = exp2f(z[mt][i] - m_new);
+            pr[mt][i] = exp2f(z[mt][i] - st.m);
             psum += pr[mt][i];
         }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    st.l += psum;
     const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+    // V^T operand of d-tile dt: lane (lg, lr) needs dim 16*dt + lr of keys
+    // 4*lg + 0..3 and 16 + 4*lg + 0..3 (the P^T k-order).  Lane t of group lg
+    // addresses the 8-byte piece (dims 16*dt + 4*(t%4) .. +3) of key 4*lg + t/4
+    // (and key + 16); the swizzle only flips address bits 5..7, so the piece
+    // for d-tile dt sits at the dt = 0 offset XOR (dt << 5).
+    const int vkey = 4 * lg + (lr >> 2);
+    const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-        const u32x4 va = *reinterpret_cast<const u32x4 *>(vt + vt_offset(16 * dt + lr, lg));
+        const int rd = rd0 ^ (dt << 5);
+        const uint2 lo = lds_read_tr16(vt + rd);
+        const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
+        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
         st.o[dt] = mfma_16x16x32(va, pb, st.o[dt]);
     }
 }
@@ -179,90 +228,168 @@ struct Unit {
     bool ok;
 };
 
-__device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
+// Row r of key head g: its sequence, position and whether the batch metadata
+// is consistent for it.
+__device__ __forceinline__ Unit row_unit(const AttnArgs &a, int r, int g) {
     Unit u;
-    u.g = (int)(unit / a.b.total_rows);
-    u.r = (int)(unit % a.b.total_rows);
-    u.s = locate_seq(a.b.cu_rows, a.b.n_seqs, u.r);
+    u.g = g;
+    u.r = r;
+    u.s = locate_seq(a.b.cu_rows, a.b.n_seqs, r);
     const int rows_s = a.b.cu_rows[u.s + 1] - a.b.cu_rows[u.s];
     const int L = a.b.seq_lens[u.s];
     u.ok = rows_s > 0 && rows_s <= L && L <= a.b.max_seq_len;
-    u.p = L - rows_s + (u.r - a.b.cu_rows[u.s]);
+    u.p = L - rows_s + (r - a.b.cu_rows[u.s]);
     return u;
 }
 
-// Prefill.  One wave per (row, key head): it holds the group's 16 query heads
-// (so every kept block is read once for all of them) and walks the row's kept
-// blocks in ascending order, 32 keys at a time, with the next chunk's K/V
-// loads in flight while the current one is folded.  A row's bits depend only
-// on its own blocks and their order.  Consecutive units are consecutive rows
-// of one key head, so a workgroup's waves share their local blocks.
-__device__ __forceinline__ void prefill_unit(const AttnArgs &a, int64_t unit, uint8_t *vt) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-    const Unit u = make_unit(a, unit);
-    if (!u.ok) return;
-    const int hq = a.H * kGroup;
-    const int64_t kv0 = a.b.kv_start[u.s];
-    const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
-    const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
-    u32x4 qb[4];
-    load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
-    // Lane t holds kept block t; read with v_readlane (loaded before the
-    // pipelined loop, so the loop never waits on it).
-    const int32_t *sel = a.idx + ((int64_t)u.r * a.H + u.g) * a.top_k;
-    const int my_b = lane < a.top_k ? sel[lane] : -1;
-
-    Softmax st;
-    softmax_init(st);
-    int t = 0, half = 0;
-    auto chunk_base = [&](int tt, int hh) -> int {
-        const int b = __builtin_amdgcn_readlane(my_b, tt);
-        const int kb = b * kBlock + 32 * hh;
-        return (b < 0 || kb > u.p) ? -1 : kb;
-    };
-    auto next_chunk = [&]() -> int {     // advances (t, half) to the next visible chunk
-        for (;;) {
-            half ^= 1;
-            if (half == 0 && ++t >= a.top_k) return -1;
-            const int kb = chunk_base(t, half);
-            if (kb >= 0) return kb;
-        }
-    };
-    force_ready(my_b);
-    int kb0 = chunk_base(0, 0);
-    if (kb0 < 0) kb0 = next_chunk();
-    ChunkRegs ca, cb;
-    if (kb0 >= 0) load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) force_ready(qb[s]);   // q complete before the loop
-    while (kb0 >= 0) {
-        const int kb1 = next_chunk();
-        if (kb1 >= 0) load_chunk(cb, kseq, vseq, a.kv_tok, kb1, u.p);
-        fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt);
-        if (kb1 < 0) break;
-        kb0 = next_chunk();
-        if (kb0 >= 0) load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
-        fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt);
-    }
-
-    const float l = sum_over_lane_groups(st.l);
-    const int h = u.g * kGroup + lr;
-    uint16_t *dst = a.out + ((int64_t)u.r * hq + h) * kHeadDim + 4 * lg;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const uint2 w = make_uint2(pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv),
-                                   pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv));
-        *reinterpret_cast<uint2 *>(dst + 16 * dt) = w;
-    }
-    if (a.lse && lg == 0) a.lse[(int64_t)u.r * hq + h] = l > 0.f ? (st.m + log2f(l)) * kLn2 : -INFINITY;
+__device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
+    return row_unit(a, (int)(unit % a.b.total_rows), (int)(unit / a.b.total_rows));
 }
 
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+// Prefill.  One wave per group of RW consecutive rows of one key head.  For each row it holds the 16 query heads (so every
+// kept block is read once for all of them) and an online-softmax state.  The
+// rows' kept blocks are merged into one list sorted by block index and walked
+// 32 keys at a time, the next chunk's K/V loads in flight while the current
+// one is folded into its row's state.  Each row still sees its own blocks in
+// ascending order, so its bits depend only on its blocks.  Walking the merged
+// list keeps every resident wave of a key head near the same key position at
+// the same time, so rows that keep the same block read it while it is still
+// in L2: with independent per-row walks, two rows reach a shared block at
+// different ranks of their own lists, long after L2 has turned over.
+constexpr int kInvalidKey = 1 << 25;   // above every block index of an int32 position
+
+template <int RW>
+__device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, uint8_t *vt, uint8_t *qt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    const int hq = a.H * kGroup;
+    const int top_k = a.top_k;
+
+    Unit u[RW];
+    Softmax st[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        const int r = min(r0 + i, a.b.total_rows - 1);   // rows past the end: not ok
+        u[i] = row_unit(a, r, g);
+        u[i].ok = u[i].ok && r0 + i < a.b.total_rows;
+        stage_q(qt + i * kQTileBytes, a.q + ((int64_t)r * hq + g * kGroup) * kHeadDim);
+        softmax_init(st[i]);
+    }
+    // Entry (row li, slot lt) on lane li*top_k + lt: its block if kept and
+    // visible, with its row's position and K/V offset.
+    const int li = lane / top_k, lt = lane - li * top_k;
+    const int rl = min(r0 + li, a.b.total_rows - 1);
+    const Unit ul = row_unit(a, rl, g);
+    int key = kInvalidKey;
+    if (li < RW && r0 + li < a.b.total_rows && ul.ok) {
+        const int b = a.idx[((int64_t)rl * a.H + g) * top_k + lt];
+        if (b >= 0 && b * kBlock <= ul.p) key = b;
+    }
+    const int64_t koff_l = a.b.kv_start[ul.s] * a.kv_tok + (int64_t)g * a.kv_head;
+    // Sort the entries by (block, lane): lane k of the e_* values holds the
+    // k-th entry (block * 4 + row, its row's position and K/V offset).
+    const uint32_t skey = ((uint32_t)key << 6) | (uint32_t)lane;
+    force_ready((int)skey);
+    int rank = 0;
+#pragma unroll 8
+    for (int m = 0; m < kWave; ++m) rank += (uint32_t)__builtin_amdgcn_readlane((int)skey, m) < skey;
+    const int dst = rank << 2;
+    const int e_key = __builtin_amdgcn_ds_permute(dst, (key << 2) | (li & 3));
+    const int e_p = __builtin_amdgcn_ds_permute(dst, ul.p);
+    const int e_lo = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)koff_l);
+    const int e_hi = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)((uint64_t)koff_l >> 32));
+    const int n_ent = (int)__popcll(__ballot(key != kInvalidKey));
+
+    // A chunk of the walk: entry k (wave-uniform values), half hh of its block.
+    struct Chunk {
+        int kb, row, p;
+        int64_t koff;
+    };
+    auto chunk_at = [&](int k, int hh) -> Chunk {
+        Chunk c;
+        const int e = __builtin_amdgcn_readlane(e_key, k);
+        c.row = e & 3;
+        c.kb = (e >> 2) * kBlock + 32 * hh;
+        c.p = __builtin_amdgcn_readlane(e_p, k);
+        c.koff = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(e_lo, k));
+        return c;
+    };
+    int k = 0, half = 0;
+    auto next_chunk = [&](Chunk &c) -> bool {   // advances (k, half) to the next visible chunk
+        for (;;) {
+            half ^= 1;
+            if (half == 0 && ++k >= n_ent) return false;
+            c = chunk_at(k, half);
+            if (c.kb <= c.p) return true;
+        }
+    };
+    auto load = [&](ChunkRegs &r, const Chunk &c) {
+        load_chunk(r, a.k + c.koff, a.v + c.koff, a.kv_tok, c.kb, c.p);
+    };
+    auto fold = [&](const ChunkRegs &r, const Chunk &c) {
+        u32x4 qb[4];
+        read_q(qb, qt + c.row * kQTileBytes);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            if (c.row == i) fold_chunk(st[i], qb, r, c.kb, c.p, a.scale_log2, vt);
+    };
+
+    force_ready(e_key);
+    force_ready(e_p);
+    force_ready(e_lo);
+    force_ready(e_hi);
+    // The prefetch is unconditional (past the last chunk it re-reads the chunk
+    // being folded), so every path through the loop has the same loads in
+    // flight and a fold waits only for its own chunk, never for the prefetch.
+    wave_lds_sync();   // q tiles written before the first fold reads them
+    if (n_ent > 0) {
+        Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
+        ChunkRegs ca, cb;
+        load(ca, c0);
+        for (;;) {
+            const bool have1 = next_chunk(c1);
+            if (!have1) c1 = c0;
+            load(cb, c1);
+            fold(ca, c0);
+            if (!have1) break;
+            const bool have0 = next_chunk(c0);
+            if (!have0) c0 = c1;
+            load(ca, c0);
+            fold(cb, c1);
+            if (!have0) break;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        if (!u[i].ok) continue;
+        const float l = sum_over_lane_groups(st[i].l);
+        const int h = g * kGroup + lr;
+        uint16_t *dst_o = a.out + ((int64_t)u[i].r * hq + h) * kHeadDim + 4 * lg;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint2 w = make_uint2(pack_bf16x2(st[i].o[dt][0] * inv, st[i].o[dt][1] * inv),
+                                       pack_bf16x2(st[i].o[dt][2] * inv, st[i].o[dt][3] * inv));
+            *reinterpret_cast<uint2 *>(dst_o + 16 * dt) = w;
+        }
+        if (a.lse && lg == 0)
+            a.lse[(int64_t)u[i].r * hq + h] = l > 0.f ? (st[i].m + log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
+// Groups are enumerated head-major (consecutive groups: consecutive rows of one
+// key head), one per wave.
+template <int RW>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    __shared__ __attribute__((aligned(16))) uint8_t qt_all[4][RW * kQTileBytes];
     const int wave = uniform(threadIdx.x >> 6);
-    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
-    if (unit < (int64_t)a.b.total_rows * a.H) prefill_unit(a, unit, vt_all[wave]);
+    const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
+    if (grp >= (int64_t)groups_per_head * a.H) return;
+    const int g = (int)(grp / groups_per_head);
+    const int r0 = (int)(grp % groups_per_head) * RW;
+    prefill_group<RW>(a, g, r0, vt_all[wave], qt_all[wave]);
 }
 
 // Decode: the kept list of a (row, key head) is split into top_k partials of
@@ -383,8 +510,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
-    const int64_t units = (int64_t)a.b.total_rows * a.H;
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);
+    // Two rows per wave: their 2 * top_k <= 64 entries fit the lanes, and two
+    // rows' accumulators fit the register file next to two chunks in flight.
+    constexpr int kRows = 2;
+    const int gph = (a.b.total_rows + kRows - 1) / kRows;
+    const int64_t waves = (int64_t)gph * a.H;
+    hipLaunchKernelGGL(prefill_kernel<kRows>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ constexpr int kHeadDim = 128;   // q/k/v head dim
 constexpr int kIndexDim = 64;   // indexer dim
 constexpr int kBlock = 64;      // keys per block
 constexpr int kMaxTopK = 32;
+constexpr int64_t kMaxKvTokStride = int64_t(1) << 24;   // elements between consecutive tokens of k/v
 constexpr int kMaxSelectBlocks = 16384;  // selection stages a row's block scores in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -94,6 +95,11 @@ __device__ __forceinline__ void force_ready(const u32x4 &x) { asm volatile("" ::
 __device__ __forceinline__ void force_ready(int x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Make LDS writes of this wave visible to its own later LDS reads (and keep
 // the compiler from moving LDS accesses across this point).

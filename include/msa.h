@@ -135,7 +135,8 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
  * order, so a row's bits do not depend on the other rows in the batch.
  *   q, out    bf16 [total_rows, n_kv_heads*group, head_dim], contiguous
  *   k, v      bf16, element (token t, key head g, dim d) at
- *             k[t*kv_tok_stride + g*kv_head_stride + d]; 16-byte aligned rows
+ *             k[t*kv_tok_stride + g*kv_head_stride + d]; 16-byte aligned rows;
+ *             kv_tok_stride <= 2^24 elements (else MSA_ERR_UNSUPPORTED)
  *   block_idx int32 [total_rows, n_kv_heads, top_k] (from msa_select_blocks)
  *   lse       fp32 [total_rows, n_kv_heads*group] natural-log log-sum-exp of
  *             the scaled scores, or NULL.  A row with no kept visible key gets

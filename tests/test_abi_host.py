@@ -133,6 +133,16 @@ def test_decode_workspace_size_and_checks():
     assert L.msa_decode(*args(131072, need, out=0)) == -1
 
 
+def test_kv_token_stride_limit():
+    L = msa.lib()
+    sh = msa.make_shape(1)
+    b = FakeBatch()
+    call = lambda tok: L.msa_prefill(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096),
+                                     ctypes.c_void_p(8192), ctypes.c_void_p(16384), tok, 0,
+                                     ctypes.c_void_p(32768), ctypes.c_void_p(65536), None, None)
+    assert call((1 << 24) + 8) == -2 and "stride" in _err()
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
 def test_no_device_returns_hip_error():
     # every argument is valid, so only the device check can fail here
