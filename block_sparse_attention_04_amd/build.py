@@ -20,7 +20,8 @@ SOURCES = ["api.hip", "indexer.hip", "select.hip", "attention.hip"]
 # max-pool reads them without v_accvgpr copies, and maxima skip NaN
 # canonicalisation (scores are finite or -inf) -- measured faster; the
 # attention kernels measured slower with it).
-SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+                "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -510,12 +510,16 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
-    // Two rows per wave: their 2 * top_k <= 64 entries fit the lanes, and two
-    // rows' accumulators fit the register file next to two chunks in flight.
-    constexpr int kRows = 2;
-    const int gph = (a.b.total_rows + kRows - 1) / kRows;
-    const int64_t waves = (int64_t)gph * a.H;
-    hipLaunchKernelGGL(prefill_kernel<kRows>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+    // 4 rows per wave while their 4 * top_k entries fit the 64 lanes, else 2.
+    if (a.top_k <= 16) {
+        const int gph = (a.b.total_rows + 3) / 4;
+        const int64_t waves = (int64_t)gph * a.H;
+        hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+    } else {
+        const int gph = (a.b.total_rows + 1) / 2;
+        const int64_t waves = (int64_t)gph * a.H;
+        hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+    }
     return hipGetLastError();
 }
 
