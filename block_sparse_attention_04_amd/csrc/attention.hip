@@ -63,6 +63,11 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[4], const uint16_t *qrow_head
     for (int s = 0; s < 4; ++s) qb[s] = load16(src + 8 * s);
 }
 
+// 2^x with the hardware instruction (v_exp_f32, ~1 ulp).  Results below the
+// smallest normal float may flush to zero; a softmax weight that small is
+// below fp32 resolution of the sum it joins, so nothing is lost.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // q of one row in LDS: 16 heads x 128 dims bf16, head rows padded to 272 B so
 // the 16 heads of one operand read fall in different banks.
 constexpr int kQRowBytes = 272;
@@ -148,7 +153,10 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
         sacc[mt] = acc;
     }
     // Online softmax over this lane's 8 keys of head lr.  Only the chunk that
-    // holds position p has keys to mask.
+    // holds position p has keys to mask.  The max is taken on the raw scores
+    // and scaled once (scaling by a positive constant is monotone, so this is
+    // the max of the scaled scores bit for bit); each weight is one FMA and
+    // one exp2.
     float z[2][4];
     float mx = -INFINITY;
     const bool edge = kbase + 31 > p;
@@ -156,19 +164,19 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float v = sacc[mt][i] * scale_log2;
+            float v = sacc[mt][i];
             if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
             z[mt][i] = v;
             mx = fmaxf(mx, v);
         }
-    mx = max_over_lane_groups(mx);              // finite: key kbase <= p is visible
+    mx = max_over_lane_groups(mx) * scale_log2;   // finite: key kbase <= p is visible
     // The reference max st.m moves only when a head's scores exceed it by more
     // than kLazyLog2 (always on the first chunk): until then the weights are
     // exp2(z - st.m) <= 2^kLazyLog2 and the accumulators need no rescale.  The
     // result is the same softmax; st.m is the reference, not necessarily the max.
     if (__ballot(mx > st.m + kLazyLog2) != 0) {
         const float m_new = fmaxf(st.m, mx);
-        const float alpha = exp2f(st.m - m_new);    // 0 on the first chunk
+        const float alpha = fast_exp2(st.m - m_new);    // 0 on the first chunk
         st.l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
@@ -180,7 +188,7 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pr[mt][i] = exp2f(z[mt][i] - st.m);
+            pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -st.m));
             psum += pr[mt][i];
         }
     st.l += psum;
