@@ -211,6 +211,89 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
     }
 }
 
+// Fold the chunk into row `row` (wave-uniform) of a group of RW rows' states.
+// The same arithmetic as fold_staged on st[row]; the scores and softmax run
+// once, with the row's max and sum picked by selects, and only the rare
+// rescale and the 8 PV MFMAs sit under a branch on the row.
+template <int RW>
+__device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x4 (&qb)[4],
+                                          const u32x4 (&ka)[2][4], int kbase, int p, float scale_log2,
+                                          const uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    floatx4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
+        sacc[mt] = acc;
+    }
+    float z[2][4];
+    float mx = -INFINITY;
+    const bool edge = kbase + 31 > p;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = sacc[mt][i];
+            if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
+            z[mt][i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = max_over_lane_groups(mx) * scale_log2;
+    float m_cur = st[0].m, l_cur = st[0].l;
+#pragma unroll
+    for (int i = 1; i < RW; ++i) {
+        m_cur = row == i ? st[i].m : m_cur;
+        l_cur = row == i ? st[i].l : l_cur;
+    }
+    if (__ballot(mx > m_cur + kLazyLog2) != 0) {
+        const float m_new = fmaxf(m_cur, mx);
+        const float alpha = fast_exp2(m_cur - m_new);
+        l_cur *= alpha;
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            if (row == i) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) st[i].o[dt] *= alpha;
+            }
+        m_cur = m_new;
+    }
+    float pr[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -m_cur));
+            psum += pr[mt][i];
+        }
+    l_cur += psum;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        st[i].m = row == i ? m_cur : st[i].m;
+        st[i].l = row == i ? l_cur : st[i].l;
+    }
+    const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                      pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+    const int vkey = 4 * lg + (lr >> 2);
+    const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
+    u32x4 va[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const int rd = rd0 ^ (dt << 5);
+        const uint2 lo = lds_read_tr16(vt + rd);
+        const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
+        va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+        if (row == i) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) st[i].o[dt] = mfma_16x16x32(va[dt], pb, st[i].o[dt]);
+        }
+}
+
 // Fold one loaded 32-key chunk into st (stage V^T, fold, release the tile).
 __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
                                            int kbase, int p, float scale_log2, uint8_t *vt) {
@@ -337,9 +420,10 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     auto fold = [&](const ChunkRegs &r, const Chunk &c) {
         u32x4 qb[4];
         read_q(qb, qt + c.row * kQTileBytes);
-#pragma unroll
-        for (int i = 0; i < RW; ++i)
-            if (c.row == i) fold_chunk(st[i], qb, r, c.kb, c.p, a.scale_log2, vt);
+        stage_v(r, vt);
+        wave_lds_sync();
+        fold_rows<RW>(st, c.row, qb, r.ka, c.kb, c.p, a.scale_log2, vt);
+        wave_lds_sync();   // reads finish before the next chunk overwrites the tile
     };
 
     force_ready(e_key);
