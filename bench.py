@@ -5,7 +5,9 @@ One step = the whole path on the two workloads the metric is quoted on:
          keys), 4 key heads x 16 query heads: index scores -> block
          selection -> msa_prefill;
   long:  one decode row at 262,144 keys, 4 key heads x 16 query heads:
-         index scores -> block selection -> msa_decode (split-K, last-arriver combine).
+         msa_index_select (index scores and block selection in one launch)
+         -> msa_decode (split-K, last-arriver combine); --unfused runs the
+         two separate steps instead.
 value = rows per second of the step (4,097 rows).  Inputs are resident in HBM
 before timing; the timed region enqueues K steps back to back, bracketed by a
 device synchronisation on both sides.  Inputs rotate over replicas so the
@@ -55,6 +57,9 @@ def algorithmic_work(case):
         flops=2 * dI * pairs * H,
         bytes=keys * ik_heads * dI * 2 + rows * H * dI * 2 + rows * H * nbk * 4)
     w["select_blocks"] = dict(flops=0, bytes=rows * H * nbk * 4 + rows * H * k * 4)
+    # fused: the scores are written once (the exchange buffer) and read back from cache
+    w["index_select"] = dict(flops=w["index_scores"]["flops"],
+                             bytes=w["index_scores"]["bytes"] + rows * H * k * 4)
     attn_bytes = rows * H * G * D * 2 * 2 + rows * H * k * 4     # q in, out
     # kept K/V blocks, counted once per distinct (sequence, key head, block)
     attn_bytes += kept_kv_bytes(case)
@@ -175,6 +180,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--unfused", action="store_true",
+                    help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters in a profiler run)")
@@ -194,13 +201,16 @@ def main():
     cases = {"chunk": config("chunk"), "long": config("long")}
     reps = {"chunk": 2, "long": 4}       # replicas: >= 512 MB rotated per workload
     modes = {"chunk": "prefill", "long": "decode"}
+    fused = {"chunk": False, "long": not args.unfused}
+    steps_of = {n: (("index_select", "attention") if fused[n] else ("index_scores", "select_blocks", "attention"))
+                for n in modes}
     state = {}
     for name, case in cases.items():
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
         inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(reps[name] - 1)]
         shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
         batch = msa.Batch(case.seq_lens, case.rows, device=dev)
-        outs = msa.run_path(shape, batch, inputs[0], modes[name])
+        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name])
         state[name] = (shape, batch, inputs, outs)
     torch.cuda.synchronize()
 
@@ -210,10 +220,17 @@ def main():
         for name in ("chunk", "long"):
             shape, batch, inputs, o = state[name]
             t = inputs[i % len(inputs)]
-            calls = [
-                ("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])),
-                ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"])),
-            ]
+            if fused[name]:
+                calls = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"],
+                                                                       o["block_scores"], o["block_idx"],
+                                                                       o["select_workspace"]))]
+            else:
+                calls = [
+                    ("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
+                                                                  o["block_scores"])),
+                    ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
+                                                                    o["block_idx"])),
+                ]
             if modes[name] == "prefill":
                 calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"],
                                                                    o["block_idx"], o["out"], o["lse"])))
@@ -242,7 +259,7 @@ def main():
     kernels = []
     for name, case in cases.items():
         work = algorithmic_work(case)
-        for kname in ("index_scores", "select_blocks", "attention"):
+        for kname in steps_of[name]:
             ms = kms[f"{name}/{kname}"]
             wk = work[kname]
             bound = "mfma" if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm"
@@ -260,8 +277,8 @@ def main():
     roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roofline.update(kernel=dom["kernel"], traffic=profiled_traffic(dom["kernel"]))
 
-    t_chunk = sum(kms[f"chunk/{k}"] for k in ("index_scores", "select_blocks", "attention"))
-    t_long = sum(kms[f"long/{k}"] for k in ("index_scores", "select_blocks", "attention"))
+    t_chunk = sum(kms[f"chunk/{k}"] for k in steps_of["chunk"])
+    t_long = sum(kms[f"long/{k}"] for k in steps_of["long"])
     res = {
         "metric": METRIC,
         "value": rows / (ms_step * 1e-3),

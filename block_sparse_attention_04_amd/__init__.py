@@ -41,8 +41,9 @@ class _BatchC(ctypes.Structure):
                 ("kv_start", ctypes.c_void_p)]
 
 
-EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode",
-           "msa_decode_workspace_bytes", "msa_status_string", "msa_last_error", "msa_version")
+EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
+           "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
+           "msa_last_error", "msa_version")
 
 
 def lib():
@@ -59,10 +60,12 @@ def lib():
             L.msa_select_blocks.argtypes = [SP, BP, vp, i32, vp, vp]
             L.msa_prefill.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp]
             L.msa_decode.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
-            for n in ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode"):
+            L.msa_index_select.argtypes = [SP, BP, vp, vp, i64, i64, vp, i32, vp, vp, ctypes.c_size_t, vp]
+            for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode"):
                 getattr(L, n).restype = ctypes.c_int
-            L.msa_decode_workspace_bytes.argtypes = [SP, i32]
-            L.msa_decode_workspace_bytes.restype = ctypes.c_size_t
+            for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
+                getattr(L, n).argtypes = [SP, i32]
+                getattr(L, n).restype = ctypes.c_size_t
             L.msa_status_string.argtypes = [ctypes.c_int]
             L.msa_status_string.restype = ctypes.c_char_p
             L.msa_last_error.argtypes = []
@@ -162,6 +165,31 @@ def msa_select_blocks(shape: Shape, batch: Batch, block_scores, block_idx, strea
                                    block_scores.shape[-1], _ptr(block_idx), _stream(stream)))
 
 
+def msa_index_select_workspace_bytes(shape: Shape, n_seqs: int) -> int:
+    return int(lib().msa_index_select_workspace_bytes(ctypes.byref(shape), int(n_seqs)))
+
+
+def index_select_workspace(shape: Shape, n_seqs: int, device="cuda"):
+    """A zero-filled workspace for msa_index_select (its arrival counters must
+    start at 0; the library leaves them at 0 after every completed call)."""
+    n = max(msa_index_select_workspace_bytes(shape, n_seqs), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def msa_index_select(shape: Shape, batch: Batch, iq, ik, block_scores, block_idx, workspace=None,
+                     stream=None):
+    _need(iq, torch.bfloat16, "iq")
+    _need(ik, torch.bfloat16, "ik", contiguous=False)
+    _need(block_scores, torch.float32, "block_scores")
+    _need(block_idx, torch.int32, "block_idx")
+    tok, head = _strides_tok_head(ik, "ik")
+    if workspace is None:
+        workspace = index_select_workspace(shape, batch.n_seqs, iq.device)
+    _check(lib().msa_index_select(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(iq), _ptr(ik), tok, head,
+                                  _ptr(block_scores), block_scores.shape[-1], _ptr(block_idx), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def msa_prefill(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, stream=None):
     _need(q, torch.bfloat16, "q")
     _need(out, torch.bfloat16, "out")
@@ -208,9 +236,10 @@ def msa_decode(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, wo
 
 
 def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: dict | None = None,
-             stream=None) -> dict:
+             stream=None, fused: bool = False) -> dict:
     """Enqueue the whole path -- index scores, selection, attention -- on
     device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
+    fused: steps 1-3 through msa_index_select (at most 16 rows per sequence).
     Output buffers are allocated unless given in `out`."""
     out = {} if out is None else out
     dev = t["q"].device
@@ -223,8 +252,14 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
         out["out"] = torch.empty_like(t["q"])
     if "lse" not in out:
         out["lse"] = torch.empty(rows, H * GROUP, dtype=torch.float32, device=dev)
-    msa_index_scores(shape, batch, t["iq"], t["ik"], out["block_scores"], stream)
-    msa_select_blocks(shape, batch, out["block_scores"], out["block_idx"], stream)
+    if fused:
+        if "select_workspace" not in out:
+            out["select_workspace"] = index_select_workspace(shape, batch.n_seqs, dev)
+        msa_index_select(shape, batch, t["iq"], t["ik"], out["block_scores"], out["block_idx"],
+                         out["select_workspace"], stream)
+    else:
+        msa_index_scores(shape, batch, t["iq"], t["ik"], out["block_scores"], stream)
+        msa_select_blocks(shape, batch, out["block_scores"], out["block_idx"], stream)
     if mode == "prefill":
         msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
     elif mode == "decode":

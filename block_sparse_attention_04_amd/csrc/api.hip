@@ -178,6 +178,56 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch, const floa
     return launched(msa::launch_select_blocks(a, static_cast<hipStream_t>(stream)), "select_blocks");
 }
 
+size_t msa_index_select_workspace_bytes(const msa_shape *shape, int32_t n_seqs) {
+    if (!shape || check_shape(shape) || n_seqs < 0) return 0;
+    return msa::index_select_workspace_bytes(n_seqs, shape->n_kv_heads);
+}
+
+int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
+                     int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores, int32_t bs_stride,
+                     int32_t *block_idx, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc;
+    bool empty;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
+    if (empty) return ok();
+    if (!iq || !ik || !block_scores || !block_idx)
+        return fail(MSA_ERR_INVALID, "iq/ik/block_scores/block_idx must not be NULL");
+    if (ik_tok_stride < msa::kIndexDim || ik_head_stride < 0 ||
+        (ik_head_stride > 0 && ik_head_stride < msa::kIndexDim))
+        return fail(MSA_ERR_INVALID, "ik strides (%lld, %lld) overlap a %d-element row",
+                    (long long)ik_tok_stride, (long long)ik_head_stride, msa::kIndexDim);
+    if (!aligned16(iq) || !aligned16(ik) || (ik_tok_stride * 2) % 16 || (ik_head_stride * 2) % 16)
+        return fail(MSA_ERR_INVALID, "iq/ik rows must be 16-byte aligned");
+    const int64_t need = ((int64_t)batch->max_seq_len + msa::kBlock - 1) / msa::kBlock;
+    if (bs_stride < need)
+        return fail(MSA_ERR_INVALID, "bs_stride=%d < ceil(max_seq_len/64)=%lld", bs_stride, (long long)need);
+    if (need > msa::kMaxSelectBlocks)
+        return fail(MSA_ERR_UNSUPPORTED, "max_seq_len=%d: selection supports at most %d blocks (%d keys)",
+                    batch->max_seq_len, msa::kMaxSelectBlocks, msa::kMaxSelectBlocks * msa::kBlock);
+    if (batch->max_rows > 16)
+        return fail(MSA_ERR_UNSUPPORTED, "max_rows=%d: the fused path takes at most 16 rows per sequence "
+                    "(use msa_index_scores + msa_select_blocks)", batch->max_rows);
+    const size_t ws_need = msa::index_select_workspace_bytes(batch->n_seqs, shape->n_kv_heads);
+    if (!workspace || workspace_bytes < ws_need)
+        return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws_need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if ((rc = check_device())) return rc;
+    msa::IndexArgs a;
+    a.b = to_dev(batch);
+    a.H = shape->n_kv_heads;
+    a.iq = static_cast<const uint16_t *>(iq);
+    a.ik = static_cast<const uint16_t *>(ik);
+    a.ik_tok = ik_tok_stride;
+    a.ik_head = ik_head_stride;
+    a.scores = block_scores;
+    a.bs_stride = bs_stride;
+    msa::SelectTail t{};
+    t.top_k = shape->top_k;
+    t.idx = block_idx;
+    t.count = static_cast<unsigned *>(workspace);
+    return launched(msa::launch_index_select(a, t, static_cast<hipStream_t>(stream)), "index_select");
+}
+
 static int attn_common(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
                        const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
                        const int32_t *block_idx, void *out, float *lse, msa::AttnArgs *a, bool *empty) {

@@ -23,6 +23,7 @@
 //                       and the key axis is spread over the whole chip.
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "msa_select.h"
 
 namespace msa {
 
@@ -234,48 +235,102 @@ __device__ __forceinline__ float window_block_max(const u32x4 (&av)[4][2], u32x4
 // is discarded), and lane group lg ends up holding block b_begin + lg.
 constexpr int kWindowBlocks = 4;
 
-__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// kSelect: the fused index-and-select variant.  Every workgroup of a
+// (sequence, key head) counts itself in on an agent-scope counter after its
+// scores are stored (release); the last one (acquire) selects the sequence's
+// rows from the scores all of them wrote, resets the counter and leaves.
+template <bool kSelect>
+__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t) {
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
     const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
     if (s >= a.b.n_seqs) return;
     const int row0 = a.b.cu_rows[s];
     const int rows_s = a.b.cu_rows[s + 1] - row0;
     const int L = a.b.seq_lens[s];
-    if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;
+    if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;   // whole (s, g) alike
     const int b_begin = (blockIdx.x * 4 + wave) * kWindowBlocks;
     const int b_end = min(b_begin + kWindowBlocks, a.bs_stride);
-    if (b_begin >= b_end) return;
-    const int nb_seq = (L - 1) / kBlock + 1;
-    const int nblk = min(b_end, nb_seq) - b_begin;    // blocks with visible keys
-    const int64_t kv0 = a.b.kv_start[s];
-
-    const bool rvalid = lr < rows_s;
     const int p_first = L - rows_s;
-    const int prow = p_first + lr;
-    float mine = -INFINITY;
-    if (nblk > 0) {
-        u32x4 bq0 = zero16(), bq1 = zero16();
-        if (rvalid) {
-            const uint16_t *src = a.iq + ((int64_t)(row0 + lr) * a.H + g) * kIndexDim + 16 * lg;
-            bq0 = load16(src);
-            bq1 = load16(src + 8);
+    if (b_begin < b_end) {
+        const int nb_seq = (L - 1) / kBlock + 1;
+        const int nblk = min(b_end, nb_seq) - b_begin;    // blocks with visible keys
+        const int64_t kv0 = a.b.kv_start[s];
+        const bool rvalid = lr < rows_s;
+        const int prow = p_first + lr;
+        float mine = -INFINITY;
+        if (nblk > 0) {
+            u32x4 bq0 = zero16(), bq1 = zero16();
+            if (rvalid) {
+                const uint16_t *src = a.iq + ((int64_t)(row0 + lr) * a.H + g) * kIndexDim + 16 * lg;
+                bq0 = load16(src);
+                bq1 = load16(src + 8);
+            }
+            const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
+            u32x4 av[kWindowBlocks][4][2];
+#pragma unroll
+            for (int q = 0; q < kWindowBlocks; ++q)
+                window_load_block(av[q], ik_g, kv0, a.ik_tok, b_begin + min(q, nblk - 1), L, lr);
+#pragma unroll
+            for (int q = 0; q < kWindowBlocks; ++q) {
+                if (q < nblk) {
+                    const float m = window_block_max(av[q], bq0, bq1, b_begin + q, prow, p_first);
+                    if (lg == q) mine = m;
+                }
+            }
         }
-        const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
-        u32x4 av[kWindowBlocks][4][2];
-#pragma unroll
-        for (int q = 0; q < kWindowBlocks; ++q)
-            window_load_block(av[q], ik_g, kv0, a.ik_tok, b_begin + min(q, nblk - 1), L, lr);
-#pragma unroll
-        for (int q = 0; q < kWindowBlocks; ++q) {
-            if (q < nblk) {
-                const float m = window_block_max(av[q], bq0, bq1, b_begin + q, prow, p_first);
-                if (lg == q) mine = m;
+        const int blk = b_begin + lg;
+        if (rvalid && blk < b_end) {
+            float *dst = a.scores + ((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk;
+            if constexpr (kSelect)   // device-coherent store (written through to the device level)
+                __hip_atomic_store(dst, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *dst = mine;
+        }
+    }
+    if constexpr (kSelect) {
+        // Every score store above is device-scoped, so publishing them needs only
+        // their completion (no write-back of the whole L2, which an agent-scope
+        // release fence would issue in each of the many workgroups): wait for
+        // this wave's stores, meet at the barrier, then count the workgroup in.
+        // The last workgroup reads the scores with device-scoped loads.
+        extern __shared__ uint32_t dyn[];
+        __shared__ SelScratch sc;
+        __shared__ int is_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(t.count + blockIdx.z, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == gridDim.x - 1;
+        }
+        __syncthreads();
+        if (!is_last) return;
+        if (threadIdx.x == 0)   // leave the counter at zero for the next call
+            __hip_atomic_store(t.count + blockIdx.z, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t.wave_mode) {
+            // one wave per row, rows wave, wave + 4, ...
+            uint32_t *keys = dyn + wave * t.cap;
+            for (int r = wave; r < rows_s; r += 4) {
+                const int row = row0 + r;
+                const int nb = (p_first + r) / kBlock + 1;
+                wave_lds_sync();   // the previous row's reads are done before restaging
+                stage_keys_coherent(keys, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, lane, kWave);
+                select_unit_wave(keys, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc.ck[wave],
+                                 sc.ci[wave]);
+            }
+        } else {
+            // the workgroup per row
+            for (int r = 0; r < rows_s; ++r) {
+                const int row = row0 + r;
+                const int nb = (p_first + r) / kBlock + 1;
+                __syncthreads();   // the previous row's reads are done before restaging
+                stage_keys_coherent(dyn, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, threadIdx.x,
+                                    256);
+                select_unit_wg(dyn, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc);
             }
         }
     }
-    const int blk = b_begin + lg;
-    if (rvalid && blk < b_end) a.scores[((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk] = mine;
 }
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
@@ -283,13 +338,25 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
     if (a.b.max_rows <= 16) {
         const int per_wg = kWindowBlocks * 4;
         dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, gz);
-        hipLaunchKernelGGL(index_scores_window, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(index_scores_window<false>, grid, dim3(256), 0, st, a, SelectTail{});
     } else {
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
         dim3 grid((a.bs_stride + kTiledBlocks - 1) / kTiledBlocks, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
         hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, kTiledBlocks);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st) {
+    const int per_wg = kWindowBlocks * 4;
+    dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, a.b.n_seqs * a.H);
+    const int nb_max = (a.b.max_seq_len + kBlock - 1) / kBlock;
+    t.cap = ((nb_max + 63) / 64) * 64;                      // staged keys per row
+    // one wave per row when a sequence has several rows and 4 stages fit 64 KiB
+    t.wave_mode = a.b.max_rows > 1 && t.cap * 16 <= 64 * 1024;
+    const size_t lds = (size_t)(t.wave_mode ? 4 : 1) * t.cap * sizeof(uint32_t);
+    hipLaunchKernelGGL(index_scores_window<true>, grid, dim3(256), lds, st, a, t);
     return hipGetLastError();
 }
 

@@ -46,6 +46,18 @@ struct AttnArgs {
     float *ws_part;              // decode: top_k partials per (row, key head)
 };
 
+// Selection fused after the decode-shaped indexer.
+struct SelectTail {
+    int top_k;
+    int32_t *idx;                // [total_rows, H, top_k]
+    unsigned *count;             // one arrival counter per (sequence, key head); zero between calls
+    int cap;                     // staged keys per row (set by the launcher)
+    int wave_mode;               // 1: one wave per row; 0: the workgroup per row (set by the launcher)
+};
+inline size_t index_select_workspace_bytes(int64_t n_seqs, int H) {
+    return (size_t)((n_seqs * H * 4 + 255) / 256 * 256);
+}
+
 // Decode partial: m[16], l[16], acc[16][128] (fp32) for one kept block.
 constexpr int kPartialFloats = 16 + 16 + 16 * 128;
 inline int decode_wg_per_unit(int top_k) { return (top_k + 3) / 4; }
@@ -57,6 +69,7 @@ inline size_t decode_workspace_bytes(int64_t units, int top_k) {
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
+hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st);
 

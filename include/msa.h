@@ -128,6 +128,35 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
                       int32_t *block_idx, void *stream);
 
 /*
+ * Steps 1-3 fused, for decode steps and verify windows (at most 16 rows per
+ * sequence): the index scores and max-pool of msa_index_scores, then the
+ * selection of msa_select_blocks, in one launch.  The key axis of every
+ * (sequence, key head) is spread over many workgroups; the last of them to
+ * finish (an arrival counter in `workspace`) selects that sequence's rows, so
+ * there is no second launch and the scores are read back while still in the
+ * caches.  block_idx is bit-identical to msa_index_scores followed by
+ * msa_select_blocks; block_scores is written as by msa_index_scores (it is
+ * the exchange buffer).  The computation is the one of steps 1-3 (TensorFold
+ * pull request 1388, commit adding the minimax_m3 family: index scores and a
+ * top-16 block selection per row and key head); the pages keep the block
+ * scores as a buffer of their own between the two steps (a later commit of the
+ * same pull request shares its memory with other buffers).  Running both in
+ * one launch is this library's addition, for decode latency.
+ *   workspace   device, 256-byte aligned, msa_index_select_workspace_bytes()
+ *               bytes: one arrival counter per (sequence, key head).  Must be
+ *               zero before the first call; every call leaves it zero.  Calls
+ *               that share a workspace must not overlap in time.
+ * Errors: as msa_index_scores and msa_select_blocks; max_rows > 16 ->
+ * MSA_ERR_UNSUPPORTED (use the two separate steps); a missing or short
+ * workspace -> MSA_ERR_WORKSPACE.
+ */
+size_t msa_index_select_workspace_bytes(const msa_shape *shape, int32_t n_seqs);
+int msa_index_select(const msa_shape *shape, const msa_batch *batch,
+                     const void *iq, const void *ik, int64_t ik_tok_stride, int64_t ik_head_stride,
+                     float *block_scores, int32_t bs_stride, int32_t *block_idx,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Step 4 for prompt chunks: out[r, h, :] = softmax over the kept, visible keys
  * of scale * q[r,h,:].k[j,g,:], applied to v[j,g,:], g = h / group.  One pass
  * per row; the group's query heads share the row's selection, so each kept

@@ -40,13 +40,14 @@ def shape_of(case, top_k=None):
     return msa.make_shape(case.n_kv_heads, case.top_k if top_k is None else top_k, case.scale)
 
 
-def gpu_run(case, mode, t=None, batch=None, top_k=None, block_idx=None):
+def gpu_run(case, mode, t=None, batch=None, top_k=None, block_idx=None, fused=False):
     """Run the path on the GPU; block_idx (host int32) replaces the GPU's own
-    selection for the attention step when given."""
+    selection for the attention step when given.  fused: steps 1-3 through
+    msa_index_select."""
     shape = shape_of(case, top_k)
     batch = batch or msa.Batch(case.seq_lens, case.rows)
     t = t or device_tensors(case)
-    out = msa.run_path(shape, batch, t, mode)
+    out = msa.run_path(shape, batch, t, mode, fused=fused)
     if block_idx is not None:
         bi = torch.as_tensor(block_idx, dtype=torch.int32).cuda().contiguous()
         o2 = torch.empty_like(t["q"])
@@ -57,7 +58,7 @@ def gpu_run(case, mode, t=None, batch=None, top_k=None, block_idx=None):
             msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], bi, o2, l2)
         out["out_fed"], out["lse_fed"] = o2, l2
     torch.cuda.synchronize()
-    return {k: v.cpu() for k, v in out.items() if k != "workspace"}
+    return {k: v.cpu() for k, v in out.items() if k not in ("workspace", "select_workspace")}
 
 
 def score_tol(case) -> float:
@@ -108,13 +109,14 @@ def check_lse(got, want, label):
     assert float(d.max()) <= LSE_ABS, f"{label}: lse error {float(d.max()):.3e}"
 
 
-def full_check(case, mode, rows=None, top_k=None, t=None):
+def full_check(case, mode, rows=None, top_k=None, t=None, fused=False):
     """Everything for one case and one attention entry point; returns metrics."""
     top_k = case.top_k if top_k is None else top_k
     rows = np.arange(case.total_rows) if rows is None else np.asarray(rows)
-    say(f"[gpu] {case.name} mode={mode} rows={len(rows)} top_k={top_k}")
+    say(f"[gpu] {case.name} mode={mode} fused={fused} rows={len(rows)} top_k={top_k}")
     ref = oracle.run(case, rows, top_k=top_k)
-    g = gpu_run(case, mode, t=t, top_k=top_k, block_idx=_expand(case, rows, ref["block_idx"], top_k))
+    g = gpu_run(case, mode, t=t, top_k=top_k, block_idx=_expand(case, rows, ref["block_idx"], top_k),
+                fused=fused)
     serr = check_scores(case, g, rows, ref)
     clear = check_selection(case, g, rows, ref, top_k)
     # attention on the oracle's selection (independent of near-ties), all rows

@@ -163,3 +163,19 @@ def test_select_rejects_contexts_beyond_the_staging_limit():
     rc = L.msa_select_blocks(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), 16385,
                              ctypes.c_void_p(8192), None)
     assert rc == -2 and "16384" in _err()
+
+
+def test_index_select_checks():
+    L = msa.lib()
+    sh = msa.make_shape(2)
+    assert msa.msa_index_select_workspace_bytes(sh, 3) == 256
+    assert msa.msa_index_select_workspace_bytes(sh, 100) == 1024     # 100 * 2 * 4 -> 800 -> 1024
+    call = lambda b, ws, nbytes, bs=2: L.msa_index_select(
+        ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), ctypes.c_void_p(8192), 64, 0,
+        ctypes.c_void_p(12288), bs, ctypes.c_void_p(16384), ctypes.c_void_p(ws) if ws else None, nbytes, None)
+    assert call(FakeBatch(max_rows=17, total_rows=17), 65536, 256) == -2 and "16 rows" in _err()
+    assert call(FakeBatch(), 65536, 255) == -3
+    assert call(FakeBatch(), 0, 256) == -3
+    assert call(FakeBatch(), 65536 + 4, 256) == -1 and "aligned" in _err()
+    big = FakeBatch(max_seq_len=(1 << 20) + 64)
+    assert call(big, 65536, 256, bs=16385) == -2 and "16384" in _err()
