@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--paged", action="store_true",
+                    help="keys in pools of 64-token pages in a random page order, addressed through a page "
+                         "table (the contiguous layout is the default)")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -207,9 +210,14 @@ def main():
     state = {}
     for name, case in cases.items():
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        page_table = None
+        if args.paged:
+            from workloads import to_pages
+            pool, page_table = to_pages(case, seed=7)
+            base.update({n: x.to(dev) for n, x in pool.items()})
         inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(reps[name] - 1)]
         shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
-        batch = msa.Batch(case.seq_lens, case.rows, device=dev)
+        batch = msa.Batch(case.seq_lens, case.rows, device=dev, page_table=page_table)
         outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name])
         state[name] = (shape, batch, inputs, outs)
     torch.cuda.synchronize()
@@ -295,7 +303,8 @@ def main():
         "config": {"workload": "chunked prefill (1 seq, 4,096 rows on a 65,536-key prefix, 69,632 keys) "
                                "+ long decode (1 row at 262,144 keys); 4 key heads x 16 query heads, "
                                "head_dim 128, index_dim 64, block 64, top-16 incl. local block",
-                   "rows_per_step": rows, "kv_heads": 4, "q_heads": 64},
+                   "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
+                   "kv_layout": "paged (64-token pages, random order)" if args.paged else "contiguous"},
         "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
         "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
         "roofline": roofline,

@@ -38,7 +38,8 @@ class _BatchC(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("total_rows", ctypes.c_int32),
                 ("max_rows", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("cu_rows", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
-                ("kv_start", ctypes.c_void_p)]
+                ("kv_start", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("pages_per_seq", ctypes.c_int32)]
 
 
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
@@ -84,9 +85,11 @@ def make_shape(n_kv_heads: int, top_k: int = 16, scale: float | None = None) -> 
 class Batch:
     """A ragged batch: host sizes plus device arrays (kept alive here).
     Sequence s has seq_lens[s] keys and rows[s] query rows, its last positions;
-    its keys start at token kv_start[s] (default: packed back to back)."""
+    its keys start at token kv_start[s] (default: packed back to back), or,
+    with page_table (int32 [n_seqs, pages_per_seq]), key j of sequence s is
+    token page_table[s, j // 64] * 64 + j % 64 of the k / v / ik pools."""
 
-    def __init__(self, seq_lens, rows, device="cuda", kv_start=None):
+    def __init__(self, seq_lens, rows, device="cuda", kv_start=None, page_table=None):
         seq_lens = [int(x) for x in seq_lens]
         rows = [int(x) for x in rows]
         cu = [0]
@@ -104,8 +107,17 @@ class Batch:
         self.cu_rows = torch.tensor(cu, dtype=torch.int32, device=device)
         self.seq_lens_d = torch.tensor(seq_lens or [0], dtype=torch.int32, device=device)
         self.kv_start = torch.tensor(list(kv_start) or [0], dtype=torch.int64, device=device)
+        self.page_table = None
+        pt_ptr, pps = None, 0
+        if page_table is not None:
+            pt = torch.as_tensor(page_table, dtype=torch.int32)
+            if pt.dim() != 2 or pt.shape[0] != self.n_seqs:
+                raise ValueError("page_table must be [n_seqs, pages_per_seq]")
+            self.page_table = pt.to(device).contiguous()
+            pt_ptr, pps = self.page_table.data_ptr(), int(pt.shape[1])
         self.c = _BatchC(self.n_seqs, self.total_rows, self.max_rows, self.max_seq_len,
-                         self.cu_rows.data_ptr(), self.seq_lens_d.data_ptr(), self.kv_start.data_ptr())
+                         self.cu_rows.data_ptr(), self.seq_lens_d.data_ptr(), self.kv_start.data_ptr(),
+                         pt_ptr, pps)
 
     @property
     def n_blocks(self) -> int:

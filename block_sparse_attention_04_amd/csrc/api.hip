@@ -51,8 +51,11 @@ int check_batch(const msa_batch *b, const msa_shape *sh, bool *empty) {
         if (b->total_rows != 0) return fail(MSA_ERR_INVALID, "n_seqs=0 but total_rows=%d", b->total_rows);
         return MSA_OK;
     }
-    if (!b->cu_rows || !b->seq_lens || !b->kv_start)
+    if (!b->cu_rows || !b->seq_lens || (!b->kv_start && !b->page_table))
         return fail(MSA_ERR_INVALID, "batch device arrays must not be NULL");
+    if (b->page_table && (int64_t)b->pages_per_seq * msa::kBlock < b->max_seq_len)
+        return fail(MSA_ERR_INVALID, "pages_per_seq=%d covers fewer than max_seq_len=%d keys", b->pages_per_seq,
+                    b->max_seq_len);
     if (b->max_rows < 1 || b->max_seq_len < 1 || b->total_rows < b->n_seqs)
         return fail(MSA_ERR_INVALID, "every sequence needs >= 1 row and >= 1 key");
     if (b->max_rows > b->max_seq_len)
@@ -84,6 +87,8 @@ msa::BatchDev to_dev(const msa_batch *b) {
     d.cu_rows = b->cu_rows;
     d.seq_lens = b->seq_lens;
     d.kv_start = b->kv_start;
+    d.page_table = b->page_table;
+    d.pages_per_seq = b->page_table ? b->pages_per_seq : 0;
     return d;
 }
 
@@ -109,7 +114,7 @@ int check_kv(const void *k, const void *v, int64_t tok, int64_t head, int n_kv_h
 
 extern "C" {
 
-const char *msa_version(void) { return "msa-mi355x 0.1 (gfx950)"; }
+const char *msa_version(void) { return "msa-mi355x 0.2 (gfx950)"; }
 
 const char *msa_last_error(void) { return g_last_error; }
 

@@ -375,7 +375,9 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         const int b = a.idx[((int64_t)rl * a.H + g) * top_k + lt];
         if (b >= 0 && b * kBlock <= ul.p) key = b;
     }
-    const int64_t koff_l = a.b.kv_start[ul.s] * a.kv_tok + (int64_t)g * a.kv_head;
+    // element offset of the entry's block (first key, key head g) in k and v
+    const int64_t koff_l = block_token0(a.b, ul.s, seq_token0(a.b, ul.s), key == kInvalidKey ? 0 : key) * a.kv_tok +
+                           (int64_t)g * a.kv_head;
     // Sort the entries by (block, lane): lane k of the e_* values holds the
     // k-th entry (block * 4 + row, its row's position and K/V offset).
     const uint32_t skey = ((uint32_t)key << 6) | (uint32_t)lane;
@@ -402,7 +404,8 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         c.kb = (e >> 2) * kBlock + 32 * hh;
         c.p = __builtin_amdgcn_readlane(e_p, k);
         c.koff = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane(e_lo, k));
+                           (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) +
+                 (int64_t)(32 * hh) * a.kv_tok;     // the chunk's first key
         return c;
     };
     int k = 0, half = 0;
@@ -415,7 +418,7 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         }
     };
     auto load = [&](ChunkRegs &r, const Chunk &c) {
-        load_chunk(r, a.k + c.koff, a.v + c.koff, a.kv_tok, c.kb, c.p);
+        load_chunk(r, a.k + c.koff, a.v + c.koff, a.kv_tok, 0, c.p - c.kb);
     };
     auto fold = [&](const ChunkRegs &r, const Chunk &c) {
         u32x4 qb[4];
@@ -511,17 +514,17 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         // the block index, q and the sequence's first key do not depend on one
         // another: issue them together (in bounds for every unit of the grid)
         const int b_raw = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
-        const int64_t kv0 = a.b.kv_start[u.s];
+        const int64_t kv0 = seq_token0(a.b, u.s);
         u32x4 qb[4];
         load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
         const int b = u.ok ? b_raw : -1;
         const int kb0 = b * kBlock, kb1 = kb0 + 32;
         if (b >= 0 && kb0 <= u.p) {
-            const uint16_t *kseq = a.k + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
-            const uint16_t *vseq = a.v + kv0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+            const int64_t off = block_token0(a.b, u.s, kv0, b) * a.kv_tok + (int64_t)u.g * a.kv_head;
+            const uint16_t *kblk = a.k + off, *vblk = a.v + off;   // the block's first key
             ChunkRegs ca, cb;
-            load_chunk(ca, kseq, vseq, a.kv_tok, kb0, u.p);
-            if (kb1 <= u.p) load_chunk(cb, kseq, vseq, a.kv_tok, kb1, u.p);
+            load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
+            if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
             fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave]);
             if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave]);
         }

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     const int b_end = min(b_begin + blocks_per_wg, a.bs_stride);
     if (b_begin >= b_end) return;
     const int b_cmp_end = min(b_end, nb_tile);
-    const int64_t kv0 = a.b.kv_start[s];
+    const int64_t kv0 = seq_token0(a.b, s);
 
     // This wave's rows and their indexer queries (the B operand, kept in VGPRs).
     const int wrow0 = tile0 + wave * kRowsWave;
@@ -116,9 +116,19 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     };
     // Keys past the sequence end read its last key instead (always in
     // bounds); they lie past every row's position, so the max-pool masks them.
+    // First token of each of the workgroup's blocks, looked up once: lane q
+    // holds block b_begin + q (clamped to the blocks with visible keys), so
+    // the loop's loads never wait on a page-table read.
+    const int64_t blk_tok = block_token0(a.b, s, kv0, max(min(b_begin + (lane & 15), b_cmp_end - 1), 0));
+    const int blk_tok_lo = (int)(uint32_t)blk_tok, blk_tok_hi = (int)(uint32_t)((uint64_t)blk_tok >> 32);
     auto gload = [&](int b, Stage &r) {
-        const int j = min(b * kBlock + st_key, L - 1);
-        const uint16_t *src = ik_g + (kv0 + j) * a.ik_tok;
+        // b is in [b_begin, b_cmp_end) when the range has visible blocks, else
+        // b_cmp_end - 1 < b_begin, which every lane holds (the clamp above)
+        const int q = max(b - b_begin, 0);
+        const int64_t tok0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(blk_tok_hi, q) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane(blk_tok_lo, q));
+        const int j = min(b * kBlock + st_key, L - 1);    // stays in block b (b holds a visible key)
+        const uint16_t *src = ik_g + (tok0 + (j - b * kBlock)) * a.ik_tok;
         r.x0 = load16(src);
         r.x1 = load16(src + 8);
     };
@@ -207,12 +217,14 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     }
 }
 
-__device__ __forceinline__ void window_load_block(u32x4 (&av)[4][2], const uint16_t *ik_g, int64_t kv0,
+// tok0: token of the block's first key; keys past the sequence end read its
+// last key (in the same block) and are masked.
+__device__ __forceinline__ void window_load_block(u32x4 (&av)[4][2], const uint16_t *ik_g, int64_t tok0,
                                                   int64_t tok, int b, int L, int lr) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const int j = min(b * kBlock + 16 * mt + lr, L - 1);   // past the end: masked
-        const uint16_t *src = ik_g + (kv0 + j) * tok;
+        const int j = min(b * kBlock + 16 * mt + lr, L - 1);
+        const uint16_t *src = ik_g + (tok0 + (j - b * kBlock)) * tok;
         av[mt][0] = load16(src);
         av[mt][1] = load16(src + 8);
     }
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
     if (b_begin < b_end) {
         const int nb_seq = (L - 1) / kBlock + 1;
         const int nblk = min(b_end, nb_seq) - b_begin;    // blocks with visible keys
-        const int64_t kv0 = a.b.kv_start[s];
+        const int64_t kv0 = seq_token0(a.b, s);
         const bool rvalid = lr < rows_s;
         const int prow = p_first + lr;
         float mine = -INFINITY;
@@ -269,8 +281,10 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
             const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
             u32x4 av[kWindowBlocks][4][2];
 #pragma unroll
-            for (int q = 0; q < kWindowBlocks; ++q)
-                window_load_block(av[q], ik_g, kv0, a.ik_tok, b_begin + min(q, nblk - 1), L, lr);
+            for (int q = 0; q < kWindowBlocks; ++q) {
+                const int bq = b_begin + min(q, nblk - 1);
+                window_load_block(av[q], ik_g, block_token0(a.b, s, kv0, bq), a.ik_tok, bq, L, lr);
+            }
 #pragma unroll
             for (int q = 0; q < kWindowBlocks; ++q) {
                 if (q < nblk) {

@@ -11,8 +11,22 @@ struct BatchDev {
     int n_seqs, total_rows, max_rows, max_seq_len;
     const int32_t *cu_rows;
     const int32_t *seq_lens;
-    const int64_t *kv_start;
+    const int64_t *kv_start;     // contiguous layout
+    const int32_t *page_table;   // paged layout (null: contiguous)
+    int pages_per_seq;
 };
+
+// First token of sequence s in the key tensors (contiguous layout; 0 when paged).
+__device__ __forceinline__ int64_t seq_token0(const BatchDev &b, int s) {
+    return b.page_table ? 0 : b.kv_start[s];
+}
+
+// Token of the first key of logical block blk of sequence s, whose contiguous
+// start is kv0 (from seq_token0).  Keys blk*64 + i (i < 64) follow at + i.
+__device__ __forceinline__ int64_t block_token0(const BatchDev &b, int s, int64_t kv0, int blk) {
+    return b.page_table ? (int64_t)b.page_table[(int64_t)s * b.pages_per_seq + blk] * 64
+                        : kv0 + (int64_t)blk * 64;
+}
 
 struct IndexArgs {
     BatchDev b;

@@ -19,7 +19,21 @@
  * included) and rows_s = cu_rows[s+1] - cu_rows[s] query rows, which are its
  * LAST rows_s positions: row i sits at p = seq_lens[s] - rows_s + i.  Key j of
  * the sequence (0-based) lives at token kv_start[s] + j of the key tensors and
- * is visible to the row at p iff j <= p.  Blocks are `block` consecutive keys;
+ * is visible to the row at p iff j <= p.
+ *
+ * Paged layout (page_table != NULL): the key tensors k, v and ik are pools of
+ * pages of `block` tokens -- a page is exactly one sparse block -- and key j
+ * of sequence s lives at token page_table[s * pages_per_seq + j / block] *
+ * block + j % block.  Sequences may share pages (a cached prompt prefix is
+ * stored once and referenced by every sequence that extends it; prompt chunks
+ * resume on top of it).  The page table is a precondition like cu_rows: every
+ * entry a sequence's keys reach must name a page inside the pools.
+ * (Serving stacks on the pages share one longest-prefix KV cache between
+ * requests -- "minimax-rs", API section -- keep the prompt cache on by default
+ * -- "minimax3-on-2-nodes", Performance & tuning -- and keep prompt-cache
+ * snapshots at chunk starts -- TensorFold pull request 1388, commit adding the
+ * minimax_m3 family.  Pages of one sparse block are this library's layout for
+ * that reuse.)  Blocks are `block` consecutive keys;
  * the row's causal block count is nb = floor(p / block) + 1 and its local
  * block is nb - 1.  Query head h belongs to key head floor(h / group).
  *
@@ -91,7 +105,10 @@ typedef struct msa_batch {
     int32_t max_seq_len;       /* >= every seq_lens[s] */
     const int32_t *cu_rows;    /* device [n_seqs + 1], prefix sums of rows_s, cu_rows[0] = 0 */
     const int32_t *seq_lens;   /* device [n_seqs] */
-    const int64_t *kv_start;   /* device [n_seqs], first token of each sequence in k/v/ik */
+    const int64_t *kv_start;   /* device [n_seqs], first token of each sequence in k/v/ik
+                                  (contiguous layout; not read when page_table is set) */
+    const int32_t *page_table; /* device [n_seqs, pages_per_seq] or NULL: paged layout, below */
+    int32_t pages_per_seq;     /* row stride of page_table, >= ceil(max_seq_len / block) */
 } msa_batch;
 
 /*

@@ -179,3 +179,13 @@ def test_index_select_checks():
     assert call(FakeBatch(), 65536 + 4, 256) == -1 and "aligned" in _err()
     big = FakeBatch(max_seq_len=(1 << 20) + 64)
     assert call(big, 65536, 256, bs=16385) == -2 and "16384" in _err()
+
+
+def test_paged_batch_checks():
+    sh = msa.make_shape(1)
+    b = FakeBatch(max_seq_len=200)
+    b.c.kv_start = None
+    assert _call_index(sh, b, bs=4) == -1                           # neither kv_start nor page_table
+    b.c.page_table = 1024
+    b.c.pages_per_seq = 3                                           # 3 * 64 < 200 keys
+    assert _call_index(sh, b, bs=4) == -1 and "pages_per_seq" in _err()

@@ -191,3 +191,38 @@ def config(name: str, **overrides) -> Case:
     kw = dict(CONFIGS[name])
     kw.update(overrides)
     return make_case(name, **kw)
+
+
+def to_pages(case: Case, seed: int, extra_pages: int = 0, shared=None):
+    """The case's k, v and ik laid out in pools of 64-token pages, in a random
+    page order (a layout only: the values are the case's own).
+
+    shared = (s_src, s_dst, n_pages): sequence s_dst's first n_pages blocks
+    reuse s_src's pages (their keys must already be equal).  Returns
+    ({"k", "v", "ik"} CPU pools, page_table int32 numpy [n_seqs, pages_per_seq]);
+    key j of sequence s is pool token page_table[s, j // 64] * 64 + j % 64.
+    """
+    import numpy as np
+    B = case.block
+    n_blocks = [math.ceil(L / B) for L in case.seq_lens]
+    total = sum(n_blocks) + extra_pages
+    order = np.random.default_rng(seed).permutation(total)
+    pt = np.zeros((case.n_seqs, max(n_blocks)), dtype=np.int32)
+    k = torch.zeros(total * B, *case.k.shape[1:], dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    ik = torch.zeros(total * B, *case.ik.shape[1:], dtype=torch.bfloat16)
+    used = 0
+    for s, L in enumerate(case.seq_lens):
+        k0 = case.kv_start[s]
+        for blk in range(n_blocks[s]):
+            if shared and s == shared[1] and blk < shared[2]:
+                pt[s, blk] = pt[shared[0], blk]
+                continue
+            page = int(order[used])
+            used += 1
+            pt[s, blk] = page
+            n = min(B, L - blk * B)
+            src = slice(k0 + blk * B, k0 + blk * B + n)
+            dst = slice(page * B, page * B + n)
+            k[dst], v[dst], ik[dst] = case.k[src], case.v[src], case.ik[src]
+    return {"k": k, "v": v, "ik": ik}, pt
