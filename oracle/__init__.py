@@ -68,6 +68,17 @@ def _load():
             lib.oracle_select_blocks.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, I64P, F32P, ctypes.c_int,
                 I32P, ctypes.c_int]
+            I8P = ctypes.POINTER(ctypes.c_int8)
+            lib.oracle_attention_kv8.restype = ctypes.c_int
+            lib.oracle_attention_kv8.argtypes = [
+                ctypes.c_int, I32P, I32P, I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_double, U16P, I8P, I8P, F32P, F32P,
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                I32P, I32P, ctypes.c_int, F64P, F64P, ctypes.c_int]
+            lib.oracle_quantize_kv8.restype = None
+            lib.oracle_quantize_kv8.argtypes = [
+                ctypes.c_int64, ctypes.c_int, ctypes.c_int, U16P, ctypes.c_int64, ctypes.c_int64,
+                I8P, ctypes.c_int64, ctypes.c_int64, F32P, ctypes.c_int64, ctypes.c_int64]
             lib.oracle_attention.restype = ctypes.c_int
             lib.oracle_attention.argtypes = [
                 ctypes.c_int, I32P, I32P, I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -177,6 +188,50 @@ def attention(case, block_idx: np.ndarray, rows=None, threads=None):
         threads or threads_default())
     if rc != 0:
         raise ValueError("oracle_attention: malformed metadata or block list")
+    return out, lse
+
+
+def quantize_kv8(x):
+    """int8 codes and fp32 scales of a bf16 [tokens, heads, dim] tensor, one
+    scale per (token, head): scale = max|x| / 127, code = round-half-even(x /
+    scale) clamped to +-127, both in fp32.  Returns (codes int8 numpy
+    [tokens, heads, dim], scales float32 numpy [tokens, heads])."""
+    lib = _load()
+    T, H, D = x.shape
+    xb = _bits(x).reshape(T, H, D)
+    codes = np.empty((T, H, D), dtype=np.int8)
+    scales = np.empty((T, H), dtype=np.float32)
+    lib.oracle_quantize_kv8(T, H, D, _ptr(xb, U16P), H * D, D, codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                            H * D, D, _ptr(scales, F32P), H, 1)
+    return codes, scales
+
+
+def attention_kv8(case, k8, v8, k_scale, v_scale, block_idx: np.ndarray, rows=None, threads=None):
+    """As attention(), over an int8 cache: every key / value element is
+    code * scale (codes [tokens, H_kv, D] int8, scales [tokens, H_kv] fp32, in
+    the case's token order).  Returns (out, lse) in double."""
+    lib = _load()
+    rows = _rows(case, rows)
+    cu, sl, ks = _meta(case)
+    q = _bits(case.q)
+    k8 = np.ascontiguousarray(k8, dtype=np.int8)
+    v8 = np.ascontiguousarray(v8, dtype=np.int8)
+    ksc = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vsc = np.ascontiguousarray(v_scale, dtype=np.float32)
+    bi = np.ascontiguousarray(block_idx, dtype=np.int32)
+    top_k = bi.shape[2]
+    H, D = case.n_kv_heads, case.head_dim
+    hq = H * case.group
+    out = np.empty((len(rows), hq, D), dtype=np.float64)
+    lse = np.empty((len(rows), hq), dtype=np.float64)
+    i8 = ctypes.POINTER(ctypes.c_int8)
+    rc = lib.oracle_attention_kv8(
+        case.n_seqs, _ptr(cu, I32P), _ptr(sl, I32P), _ptr(ks, I64P), H, case.group, D, case.block, top_k,
+        float(case.scale), _ptr(q, U16P), k8.ctypes.data_as(i8), v8.ctypes.data_as(i8), _ptr(ksc, F32P),
+        _ptr(vsc, F32P), H * D, D, H, 1, _ptr(bi, I32P), _ptr(rows, I32P), len(rows), _ptr(out, F64P),
+        _ptr(lse, F64P), threads or threads_default())
+    if rc != 0:
+        raise ValueError("oracle_attention_kv8: malformed metadata or block list")
     return out, lse
 
 

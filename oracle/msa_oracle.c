@@ -191,13 +191,32 @@ int oracle_select_blocks(int n_out, int n_kv_heads, int bs_stride,
  * An empty J gives o = 0 and lse = -inf.  block_idx rows follow `rows`.
  * out is double [n_out, n_kv_heads*group, head_dim]; lse may be NULL.
  */
-int oracle_attention(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens,
-                     const int64_t *kv_start, int n_kv_heads, int group,
-                     int head_dim, int block, int top_k, double scale,
-                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                     int64_t kv_tok_stride, int64_t kv_head_stride,
-                     const int32_t *block_idx, const int32_t *rows, int n_out,
-                     double *out, double *lse, int n_threads)
+/* Where attention reads its keys and values: bf16 values, or int8 codes with
+ * one fp32 scale per (token, key head) (the value is code * scale). */
+typedef struct {
+    int int8;
+    const uint16_t *k16, *v16;
+    const int8_t *k8, *v8;
+    const float *ks, *vs;
+    int64_t tok, head;          /* elements of k / v */
+    int64_t stok, shead;        /* elements of the scale arrays */
+} kv_source;
+
+static double kv_value(const kv_source *src, int is_v, int64_t t, int g, int d)
+{
+    int64_t e = t * src->tok + (int64_t)g * src->head + d;
+    if (!src->int8)
+        return bf16_value(is_v ? src->v16[e] : src->k16[e]);
+    double scale = (double)(is_v ? src->vs : src->ks)[t * src->stok + (int64_t)g * src->shead];
+    return (double)(is_v ? src->v8[e] : src->k8[e]) * scale;
+}
+
+static int attention_core(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens,
+                          const int64_t *kv_start, int n_kv_heads, int group,
+                          int head_dim, int block, int top_k, double scale,
+                          const uint16_t *q, const kv_source *src,
+                          const int32_t *block_idx, const int32_t *rows, int n_out,
+                          double *out, double *lse, int n_threads)
 {
     int bad = 0;
     int n_q = n_kv_heads * group;
@@ -244,23 +263,21 @@ int oracle_attention(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens
                 }
                 double m = -INFINITY;
                 for (int64_t t = 0; t < nk; ++t) {
-                    const uint16_t *kv = k + (kv_start[s] + key[t]) * kv_tok_stride +
-                                         (int64_t)g * kv_head_stride;
+                    int64_t tok = kv_start[s] + key[t];
                     double acc = 0.0;
                     for (int d = 0; d < head_dim; ++d)
-                        acc += bf16_value(qv[d]) * bf16_value(kv[d]);
+                        acc += bf16_value(qv[d]) * kv_value(src, 0, tok, g, d);
                     z[t] = scale * acc;
                     if (z[t] > m)
                         m = z[t];
                 }
                 double l = 0.0;
                 for (int64_t t = 0; t < nk; ++t) {
-                    const uint16_t *vv = v + (kv_start[s] + key[t]) * kv_tok_stride +
-                                         (int64_t)g * kv_head_stride;
+                    int64_t tok = kv_start[s] + key[t];
                     double w = exp(z[t] - m);
                     l += w;
                     for (int d = 0; d < head_dim; ++d)
-                        ov[d] += w * bf16_value(vv[d]);
+                        ov[d] += w * kv_value(src, 1, tok, g, d);
                 }
                 for (int d = 0; d < head_dim; ++d)
                     ov[d] /= l;
@@ -272,4 +289,93 @@ int oracle_attention(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens
         free(key);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_attention(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens,
+                     const int64_t *kv_start, int n_kv_heads, int group,
+                     int head_dim, int block, int top_k, double scale,
+                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     int64_t kv_tok_stride, int64_t kv_head_stride,
+                     const int32_t *block_idx, const int32_t *rows, int n_out,
+                     double *out, double *lse, int n_threads)
+{
+    kv_source src = {0};
+    src.k16 = k;
+    src.v16 = v;
+    src.tok = kv_tok_stride;
+    src.head = kv_head_stride;
+    return attention_core(n_seqs, cu_rows, seq_lens, kv_start, n_kv_heads, group, head_dim, block,
+                          top_k, scale, q, &src, block_idx, rows, n_out, out, lse, n_threads);
+}
+
+/*
+ * Attention over an int8 key/value cache: every key and value element is
+ * code * scale, with one fp32 scale per (token, key head) (TensorFold pull
+ * request 1388, commit adding the minimax_m3 family: keys and values cached as
+ * int8 with a scale per position and head; the scores take the keys' scales
+ * and the weights the values' scales).  Otherwise exactly oracle_attention.
+ */
+int oracle_attention_kv8(int n_seqs, const int32_t *cu_rows, const int32_t *seq_lens,
+                         const int64_t *kv_start, int n_kv_heads, int group,
+                         int head_dim, int block, int top_k, double scale,
+                         const uint16_t *q, const int8_t *k8, const int8_t *v8,
+                         const float *k_scale, const float *v_scale,
+                         int64_t tok_stride, int64_t head_stride,
+                         int64_t scale_tok_stride, int64_t scale_head_stride,
+                         const int32_t *block_idx, const int32_t *rows, int n_out,
+                         double *out, double *lse, int n_threads)
+{
+    kv_source src = {0};
+    src.int8 = 1;
+    src.k8 = k8;
+    src.v8 = v8;
+    src.ks = k_scale;
+    src.vs = v_scale;
+    src.tok = tok_stride;
+    src.head = head_stride;
+    src.stok = scale_tok_stride;
+    src.shead = scale_head_stride;
+    return attention_core(n_seqs, cu_rows, seq_lens, kv_start, n_kv_heads, group, head_dim, block,
+                          top_k, scale, q, &src, block_idx, rows, n_out, out, lse, n_threads);
+}
+
+/*
+ * The int8 cache's quantisation of one bf16 (token, head) row of head_dim
+ * values (this library's reading: the pages name a scale per position and head
+ * but not its rule).  Taken in fp32, as the kernel that writes the cache does:
+ *   scale = max_d |x_d| / 127             (fp32 division)
+ *   code_d = round_half_even(x_d / scale), clamped to [-127, 127]
+ * A row of zeros gets scale 0 and codes 0.  Inputs must be finite.
+ */
+void oracle_quantize_kv8(int64_t n_tokens, int n_heads, int head_dim, const uint16_t *x,
+                         int64_t tok_stride, int64_t head_stride, int8_t *codes,
+                         int64_t code_tok_stride, int64_t code_head_stride, float *scales,
+                         int64_t scale_tok_stride, int64_t scale_head_stride)
+{
+    for (int64_t t = 0; t < n_tokens; ++t)
+        for (int g = 0; g < n_heads; ++g) {
+            const uint16_t *row = x + t * tok_stride + (int64_t)g * head_stride;
+            int8_t *crow = codes + t * code_tok_stride + (int64_t)g * code_head_stride;
+            float amax = 0.0f;
+            for (int d = 0; d < head_dim; ++d) {
+                float a = fabsf((float)bf16_value(row[d]));
+                if (a > amax)
+                    amax = a;
+            }
+            volatile float sc = amax / 127.0f;     /* a float, stored: no wider intermediate */
+            scales[t * scale_tok_stride + (int64_t)g * scale_head_stride] = sc;
+            for (int d = 0; d < head_dim; ++d) {
+                if (sc == 0.0f) {
+                    crow[d] = 0;
+                    continue;
+                }
+                volatile float ratio = (float)bf16_value(row[d]) / sc;
+                float c = rintf(ratio);
+                if (c > 127.0f)
+                    c = 127.0f;
+                if (c < -127.0f)
+                    c = -127.0f;
+                crow[d] = (int8_t)c;
+            }
+        }
 }

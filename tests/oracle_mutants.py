@@ -8,7 +8,8 @@ import numpy as np
 import torch
 
 MUTATIONS = ("causal_off_by_one", "drop_local", "head_map_mod", "no_scale",
-             "mean_pool", "ties_high", "ik_head0", "local_plus_k")
+             "mean_pool", "ties_high", "ik_head0", "local_plus_k",
+             "quant_half_up", "quant_scale_128", "kv8_vscale_off")
 
 
 def _f(t):
@@ -100,3 +101,23 @@ class Impl:
                 out[o, h] = w @ v[k0 + np.array(keys), g] / w.sum()
                 lse[o, h] = m + np.log(w.sum())
         return out, lse
+
+    def quantize_kv8(self, x):
+        xf = x.float().numpy()
+        amax = np.abs(xf).max(axis=2).astype(np.float32)
+        div = np.float32(128.0 if self.m == "quant_scale_128" else 127.0)
+        sc = (amax / div).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = (xf / sc[..., None]).astype(np.float32)
+        c = np.floor(ratio + np.float32(0.5)) if self.m == "quant_half_up" else np.rint(ratio)
+        c = np.clip(np.nan_to_num(c), -127, 127)
+        c[sc == 0] = 0
+        return c.astype(np.int8), sc
+
+    def attention_kv8(self, case, k8, v8, k_scale, v_scale, block_idx, rows=None):
+        import copy
+        vs = np.ones_like(v_scale) if self.m == "kv8_vscale_off" else v_scale
+        c = copy.copy(case)
+        c.k = torch.from_numpy(k8.astype(np.float64) * k_scale.astype(np.float64)[..., None])
+        c.v = torch.from_numpy(v8.astype(np.float64) * vs.astype(np.float64)[..., None])
+        return self.attention(c, block_idx, rows)

@@ -410,9 +410,88 @@ def check_golden_path(impl):
         assert abs(out[0, 0, 0] - c["expected_out_dim0"]) < 1e-12, (c["name"], out[0, 0, 0])
 
 
+def check_kv8_golden_codes(impl):
+    """int8 cache quantisation on hand-derived rows: max |x| = 127 gives scale 1
+    and max |x| = 63.5 gives scale 0.5 (both exact), so each code is x / scale
+    rounded half to even: -3.5 -> -4, 2.5 -> 2, 0.5 -> 0, 1.5 -> 2, 2.5 -> 2,
+    -1.5 -> -2, 0.5 -> 0, 20.5 -> 20."""
+    x = torch.tensor([[[127., -3.5, 2.5, 0.5, -1.25, 100., 0., 1.5],
+                       [63.5, 1.25, -0.75, 3., -63.5, 0.25, 10.25, -2.]]], dtype=torch.bfloat16)
+    codes, sc = impl.quantize_kv8(x)
+    assert [float(v) for v in sc[0]] == [1.0, 0.5]
+    assert list(codes[0, 0]) == [127, -4, 2, 0, -1, 100, 0, 2]
+    assert list(codes[0, 1]) == [127, 2, -2, 6, -127, 0, 20, -4]
+
+
+def check_kv8_quant_bounds(impl):
+    """Any row: |code| <= 127, the largest |x| gets |code| = 127, code * scale is
+    within half a step of x (plus the fp32 quotient's own rounding, at most
+    127 * 2^-24 of a step), and an all-zero row has scale 0 and codes 0."""
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn(64, 3, 128, generator=g) * torch.exp(torch.randn(64, 3, 1, generator=g) * 3)
+    x[5, 1] = 0.0
+    x = x.to(torch.bfloat16)
+    codes, sc = impl.quantize_kv8(x)
+    xf = x.double().numpy()
+    assert np.abs(codes.astype(np.int32)).max() <= 127
+    assert sc[5, 1] == 0 and not codes[5, 1].any()
+    nz = sc > 0
+    am = np.abs(xf).argmax(axis=2)
+    top = np.take_along_axis(np.abs(codes.astype(np.int32)), am[..., None], axis=2)[..., 0]
+    assert (top[nz] == 127).all()
+    err = np.abs(xf - codes.astype(np.float64) * sc.astype(np.float64)[..., None])
+    assert (err <= sc.astype(np.float64)[..., None] * (0.5 + 2 ** -16) + 1e-300).all()
+
+
+def _kv8_exact_case(seed):
+    """A case whose K and V are codes times power-of-two scales, so the bf16
+    tensors hold the dequantised values exactly."""
+    case = make_case("kv8x", [700, 130, 64], [20, 5, 64], 2, seed=seed)
+    g = torch.Generator().manual_seed(seed)
+    T, H, D = case.k.shape
+    out = []
+    for _ in range(2):
+        codes = torch.randint(-127, 128, (T, H, D), generator=g).to(torch.int8)
+        e = torch.randint(3, 9, (T, H), generator=g)
+        sc = torch.pow(2.0, -e.double()).float()
+        out += [codes.numpy(), sc.numpy()]
+    k8, ks, v8, vs = out
+    case.k = torch.from_numpy(k8.astype(np.float64) * ks.astype(np.float64)[..., None]).to(torch.bfloat16)
+    case.v = torch.from_numpy(v8.astype(np.float64) * vs.astype(np.float64)[..., None]).to(torch.bfloat16)
+    return case, k8, ks, v8, vs
+
+
+def check_kv8_attention_exact(impl):
+    """Attention over the int8 cache equals attention over bf16 tensors holding
+    the same values (codes times power-of-two scales are exact in bf16)."""
+    case, k8, ks, v8, vs = _kv8_exact_case(42)
+    s32 = impl.block_scores(case).astype(np.float32)
+    idx = impl.select_blocks(s32, impl.causal_blocks(case), case.top_k)
+    a, la = impl.attention(case, idx)
+    b, lb = impl.attention_kv8(case, k8, v8, ks, vs, idx)
+    assert np.max(np.abs(a - b)) < 1e-12 and np.max(np.abs(la - lb)) < 1e-12
+
+
+def check_kv8_dense(impl):
+    """Rows with <= top_k causal blocks over the int8 cache are dense causal
+    attention over the dequantised keys and values (torch SDPA in float64)."""
+    import copy
+    case = make_case("kv8d", [300, 64, 1], [40, 64, 1], 2, seed=43)
+    k8, ks = impl.quantize_kv8(case.k)
+    v8, vs = impl.quantize_kv8(case.v)
+    idx = impl.select_blocks(impl.block_scores(case).astype(np.float32), impl.causal_blocks(case), case.top_k)
+    out, _ = impl.attention_kv8(case, k8, v8, ks, vs, idx)
+    deq = copy.copy(case)
+    deq.k = torch.from_numpy(k8.astype(np.float64) * ks.astype(np.float64)[..., None])
+    deq.v = torch.from_numpy(v8.astype(np.float64) * vs.astype(np.float64)[..., None])
+    ref = sdpa_reference(deq, _causal(deq))
+    assert np.max(np.abs(out - ref)) < 1e-10
+
+
 ALL_CHECKS = [
     check_onehot_scores, check_causal_scores, check_integer_scores, check_shared_index_key,
     check_float_scores_bound, check_select_bruteforce, check_select_ties,
     check_select_invariants, check_dense_equivalence, check_dense_topk_covers,
     check_masked_dense, check_closed_forms, check_golden_selection, check_golden_path,
+    check_kv8_golden_codes, check_kv8_quant_bounds, check_kv8_attention_exact, check_kv8_dense,
 ]
