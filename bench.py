@@ -36,8 +36,9 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
-def algorithmic_work(case):
-    """Per-launch algorithmic FLOPs and bytes of each step for one workload."""
+def algorithmic_work(case, kv8=False):
+    """Per-launch algorithmic FLOPs and bytes of each step for one workload
+    (kv8: the int8 cache, 128 + 4 bytes per key and key head for K and for V)."""
     import numpy as np
     H, G, D, dI, B, k = case.n_kv_heads, case.group, case.head_dim, case.index_dim, case.block, case.top_k
     pairs = 0           # causal (row, key) pairs per key head
@@ -62,7 +63,7 @@ def algorithmic_work(case):
                              bytes=w["index_scores"]["bytes"] + rows * H * k * 4)
     attn_bytes = rows * H * G * D * 2 * 2 + rows * H * k * 4     # q in, out
     # kept K/V blocks, counted once per distinct (sequence, key head, block)
-    attn_bytes += kept_kv_bytes(case)
+    attn_bytes += kept_kv_bytes(case) * (132 if kv8 else 256) // 256
     w["attention"] = dict(flops=4 * D * kept * H * G, bytes=attn_bytes)
     return w
 
@@ -183,6 +184,9 @@ def main():
     ap.add_argument("--paged", action="store_true",
                     help="keys in pools of 64-token pages in a random page order, addressed through a page "
                          "table (the contiguous layout is the default)")
+    ap.add_argument("--kv8", action="store_true",
+                    help="attention over the int8 key/value cache (codes + one fp32 scale per token and key "
+                         "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -217,8 +221,14 @@ def main():
             base.update({n: x.to(dev) for n, x in pool.items()})
         inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(reps[name] - 1)]
         shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
+        if args.kv8:
+            for t in inputs:
+                kc, ks = msa.msa_quantize_kv8(shape, t["k"])
+                vc, vs = msa.msa_quantize_kv8(shape, t["v"])
+                t["kv8"] = msa.KV8(kc, vc, ks, vs)
+                del t["k"], t["v"]
         batch = msa.Batch(case.seq_lens, case.rows, device=dev, page_table=page_table)
-        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name])
+        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name], kv8=inputs[0].get("kv8"))
         state[name] = (shape, batch, inputs, outs)
     torch.cuda.synchronize()
 
@@ -239,9 +249,16 @@ def main():
                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
                                                                     o["block_idx"])),
                 ]
-            if modes[name] == "prefill":
+            if modes[name] == "prefill" and args.kv8:
+                calls.append(("attention", lambda: msa.msa_prefill_kv8(shape, batch, t["q"], t["kv8"],
+                                                                       o["block_idx"], o["out"], o["lse"])))
+            elif modes[name] == "prefill":
                 calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"],
                                                                    o["block_idx"], o["out"], o["lse"])))
+            elif args.kv8:
+                calls.append(("attention", lambda: msa.msa_decode_kv8(shape, batch, t["q"], t["kv8"],
+                                                                      o["block_idx"], o["out"], o["lse"],
+                                                                      o["workspace"])))
             else:
                 calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"],
                                                                   o["block_idx"], o["out"], o["lse"],
@@ -266,7 +283,7 @@ def main():
 
     kernels = []
     for name, case in cases.items():
-        work = algorithmic_work(case)
+        work = algorithmic_work(case, kv8=args.kv8)
         for kname in steps_of[name]:
             ms = kms[f"{name}/{kname}"]
             wk = work[kname]
@@ -298,13 +315,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 (int8 key/value cache)" if args.kv8 else "bf16",
         "data": "synthetic",
         "config": {"workload": "chunked prefill (1 seq, 4,096 rows on a 65,536-key prefix, 69,632 keys) "
                                "+ long decode (1 row at 262,144 keys); 4 key heads x 16 query heads, "
                                "head_dim 128, index_dim 64, block 64, top-16 incl. local block",
                    "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
-                   "kv_layout": "paged (64-token pages, random order)" if args.paged else "contiguous"},
+                   "kv_layout": "paged (64-token pages, random order)" if args.paged else "contiguous",
+                   "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16"},
         "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
         "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
         "roofline": roofline,

@@ -43,8 +43,15 @@ class _BatchC(ctypes.Structure):
 
 
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
+           "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
            "msa_last_error", "msa_version")
+
+
+class _KV8C(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("scale_tok_stride", ctypes.c_int64), ("scale_head_stride", ctypes.c_int64)]
 
 
 def lib():
@@ -62,7 +69,12 @@ def lib():
             L.msa_prefill.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp]
             L.msa_decode.argtypes = [SP, BP, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.msa_index_select.argtypes = [SP, BP, vp, vp, i64, i64, vp, i32, vp, vp, ctypes.c_size_t, vp]
-            for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode"):
+            KP = ctypes.POINTER(_KV8C)
+            L.msa_quantize_kv8.argtypes = [SP, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp]
+            L.msa_prefill_kv8.argtypes = [SP, BP, vp, KP, vp, vp, vp, vp]
+            L.msa_decode_kv8.argtypes = [SP, BP, vp, KP, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
+                      "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8"):
                 getattr(L, n).restype = ctypes.c_int
             for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
                 getattr(L, n).argtypes = [SP, i32]
@@ -247,11 +259,76 @@ def msa_decode(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, wo
                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+class KV8:
+    """An int8 key/value cache: codes int8 [tokens, H, 128] and scales fp32
+    [tokens, H] for k and v (device tensors, kept alive here)."""
+
+    def __init__(self, k_codes, v_codes, k_scale, v_scale):
+        for t, name in ((k_codes, "k codes"), (v_codes, "v codes")):
+            _need(t, torch.int8, name, contiguous=False)
+        for t, name in ((k_scale, "k scale"), (v_scale, "v scale")):
+            _need(t, torch.float32, name, contiguous=False)
+        tok, head = _strides_tok_head(k_codes, "k codes")
+        if _strides_tok_head(v_codes, "v codes") != (tok, head):
+            raise ValueError("k and v codes must share strides")
+        if k_scale.dim() != 2 or k_scale.stride() != v_scale.stride():
+            raise ValueError("scales must be [tokens, heads] with equal strides")
+        sh = 0 if k_scale.shape[1] == 1 else k_scale.stride(1)
+        self.tensors = (k_codes, v_codes, k_scale, v_scale)
+        self.c = _KV8C(k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                       tok, head, k_scale.stride(0), sh)
+
+
+def msa_quantize_kv8(shape: Shape, x, codes=None, scales=None, stream=None):
+    """int8 codes and fp32 scales of a bf16 [tokens, H, 128] tensor (one
+    (token, head) row at a time: scale = max|x| / 127, code = round half to
+    even of x / scale).  Returns (codes, scales)."""
+    _need(x, torch.bfloat16, "x", contiguous=False)
+    tok, head = _strides_tok_head(x, "x")
+    T, H, D = x.shape
+    if codes is None:
+        codes = torch.empty(T, H, D, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(T, H, dtype=torch.float32, device=x.device)
+    _need(codes, torch.int8, "codes", contiguous=False)
+    _need(scales, torch.float32, "scales", contiguous=False)
+    ctok, chead = _strides_tok_head(codes, "codes")
+    sh = 0 if scales.shape[1] == 1 else scales.stride(1)
+    _check(lib().msa_quantize_kv8(ctypes.byref(shape), T, _ptr(x), tok, head, _ptr(codes), ctok, chead,
+                                  _ptr(scales), scales.stride(0), sh, _stream(stream)))
+    return codes, scales
+
+
+def msa_prefill_kv8(shape: Shape, batch: Batch, q, kv: KV8, block_idx, out, lse=None, stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().msa_prefill_kv8(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
+                                 _ptr(block_idx), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def msa_decode_kv8(shape: Shape, batch: Batch, q, kv: KV8, block_idx, out, lse=None, workspace=None,
+                   stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    if workspace is None:
+        workspace = decode_workspace(shape, batch.total_rows, q.device)
+    _check(lib().msa_decode_kv8(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
+                                _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: dict | None = None,
-             stream=None, fused: bool = False) -> dict:
+             stream=None, fused: bool = False, kv8: KV8 | None = None) -> dict:
     """Enqueue the whole path -- index scores, selection, attention -- on
     device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
     fused: steps 1-3 through msa_index_select (at most 16 rows per sequence).
+    kv8: attend over this int8 cache instead of t["k"], t["v"].
     Output buffers are allocated unless given in `out`."""
     out = {} if out is None else out
     dev = t["q"].device
@@ -273,12 +350,19 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
         msa_index_scores(shape, batch, t["iq"], t["ik"], out["block_scores"], stream)
         msa_select_blocks(shape, batch, out["block_scores"], out["block_idx"], stream)
     if mode == "prefill":
-        msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
+        if kv8 is not None:
+            msa_prefill_kv8(shape, batch, t["q"], kv8, out["block_idx"], out["out"], out["lse"], stream)
+        else:
+            msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
     elif mode == "decode":
         if "workspace" not in out:
             out["workspace"] = decode_workspace(shape, rows, dev)
-        msa_decode(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"],
-                   out["workspace"], stream)
+        if kv8 is not None:
+            msa_decode_kv8(shape, batch, t["q"], kv8, out["block_idx"], out["out"], out["lse"],
+                           out["workspace"], stream)
+        else:
+            msa_decode(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"],
+                       out["workspace"], stream)
     else:
         raise ValueError(mode)
     return out

@@ -233,15 +233,42 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     return launched(msa::launch_index_select(a, t, static_cast<hipStream_t>(stream)), "index_select");
 }
 
+static int check_kv8(const msa_kv8 *kv, int n_kv_heads) {
+    if (!kv) return fail(MSA_ERR_INVALID, "kv is NULL");
+    if (!kv->k || !kv->v || !kv->k_scale || !kv->v_scale)
+        return fail(MSA_ERR_INVALID, "int8 cache codes and scales must not be NULL");
+    if (kv->tok_stride < msa::kHeadDim || kv->head_stride < 0 ||
+        (n_kv_heads > 1 && kv->head_stride < msa::kHeadDim))
+        return fail(MSA_ERR_INVALID, "code strides (%lld, %lld) overlap a %d-element row",
+                    (long long)kv->tok_stride, (long long)kv->head_stride, msa::kHeadDim);
+    if (!aligned16(kv->k) || !aligned16(kv->v) || kv->tok_stride % 16 || kv->head_stride % 16)
+        return fail(MSA_ERR_INVALID, "int8 code rows must be 16-byte aligned");
+    if (kv->tok_stride > msa::kMaxKvTokStride)
+        return fail(MSA_ERR_UNSUPPORTED, "kv token stride %lld above %lld elements", (long long)kv->tok_stride,
+                    (long long)msa::kMaxKvTokStride);
+    if (kv->scale_tok_stride < 1 || kv->scale_head_stride < 0 || (n_kv_heads > 1 && kv->scale_head_stride < 1) ||
+        ((uintptr_t)kv->k_scale & 3u) || ((uintptr_t)kv->v_scale & 3u))
+        return fail(MSA_ERR_INVALID, "scale strides (%lld, %lld) or scale alignment invalid",
+                    (long long)kv->scale_tok_stride, (long long)kv->scale_head_stride);
+    return MSA_OK;
+}
+
 static int attn_common(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
                        const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
-                       const int32_t *block_idx, void *out, float *lse, msa::AttnArgs *a, bool *empty) {
+                       const int32_t *block_idx, void *out, float *lse, msa::AttnArgs *a, bool *empty,
+                       const msa_kv8 *kv8 = nullptr) {
     int rc;
     if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, empty))) return rc;
     if (*empty) return MSA_OK;
     if (!q || !block_idx || !out) return fail(MSA_ERR_INVALID, "q/block_idx/out must not be NULL");
     if (!aligned16(q) || !aligned16(out)) return fail(MSA_ERR_INVALID, "q/out must be 16-byte aligned");
-    if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, shape->n_kv_heads))) return rc;
+    if (kv8) {
+        if ((rc = check_kv8(kv8, shape->n_kv_heads))) return rc;
+        kv_tok_stride = kv8->tok_stride;
+        kv_head_stride = kv8->head_stride;
+    } else if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, shape->n_kv_heads))) {
+        return rc;
+    }
     a->b = to_dev(batch);
     a->H = shape->n_kv_heads;
     a->top_k = shape->top_k;
@@ -256,6 +283,12 @@ static int attn_common(const msa_shape *shape, const msa_batch *batch, const voi
     a->lse = lse;
     a->ws_count = nullptr;
     a->ws_part = nullptr;
+    a->k8 = kv8 ? kv8->k : nullptr;
+    a->v8 = kv8 ? kv8->v : nullptr;
+    a->ks = kv8 ? kv8->k_scale : nullptr;
+    a->vs = kv8 ? kv8->v_scale : nullptr;
+    a->s_tok = kv8 ? kv8->scale_tok_stride : 0;
+    a->s_head = kv8 ? kv8->scale_head_stride : 0;
     return MSA_OK;
 }
 
@@ -277,13 +310,14 @@ size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows) {
     return msa::decode_workspace_bytes((int64_t)total_rows * shape->n_kv_heads, shape->top_k);
 }
 
-int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
-               const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
-               void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+static int decode_common(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
+                         const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
+                         void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                         const msa_kv8 *kv8) {
     msa::AttnArgs a;
     bool empty = false;
     int rc = attn_common(shape, batch, q, k, v, kv_tok_stride, kv_head_stride, block_idx, out, lse, &a,
-                         &empty);
+                         &empty, kv8);
     if (rc) return rc;
     if (empty) return ok();
     const int64_t units = (int64_t)batch->total_rows * shape->n_kv_heads;
@@ -295,6 +329,63 @@ int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, co
     a.ws_count = static_cast<unsigned *>(workspace);
     a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::decode_count_bytes(units));
     return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
+               const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
+               void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(shape, batch, q, k, v, kv_tok_stride, kv_head_stride, block_idx, out, lse, workspace,
+                         workspace_bytes, stream, nullptr);
+}
+
+int msa_decode_kv8(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv8 *kv,
+                   const int32_t *block_idx, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (!kv) return fail(MSA_ERR_INVALID, "kv is NULL");
+    return decode_common(shape, batch, q, nullptr, nullptr, 0, 0, block_idx, out, lse, workspace,
+                         workspace_bytes, stream, kv);
+}
+
+int msa_prefill_kv8(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv8 *kv,
+                    const int32_t *block_idx, void *out, float *lse, void *stream) {
+    msa::AttnArgs a;
+    bool empty = false;
+    if (!kv) return fail(MSA_ERR_INVALID, "kv is NULL");
+    int rc = attn_common(shape, batch, q, nullptr, nullptr, 0, 0, block_idx, out, lse, &a, &empty, kv);
+    if (rc) return rc;
+    if (empty) return ok();
+    if ((rc = check_device())) return rc;
+    return launched(msa::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill_kv8");
+}
+
+int msa_quantize_kv8(const msa_shape *shape, int64_t n_tokens, const void *x, int64_t tok_stride,
+                     int64_t head_stride, int8_t *codes, int64_t code_tok_stride, int64_t code_head_stride,
+                     float *scales, int64_t scale_tok_stride, int64_t scale_head_stride, void *stream) {
+    int rc;
+    if ((rc = check_shape(shape))) return rc;
+    if (n_tokens < 0) return fail(MSA_ERR_INVALID, "n_tokens < 0");
+    if (n_tokens == 0) return ok();
+    const int H = shape->n_kv_heads;
+    if (!x || !codes || !scales) return fail(MSA_ERR_INVALID, "x/codes/scales must not be NULL");
+    if ((rc = check_kv(x, x, tok_stride, head_stride, H))) return rc;
+    msa_kv8 kv = {codes, codes, scales, scales, code_tok_stride, code_head_stride, scale_tok_stride,
+                  scale_head_stride};
+    if ((rc = check_kv8(&kv, H))) return rc;
+    if (n_tokens * H > (int64_t)0x7fffffff / 16) return fail(MSA_ERR_UNSUPPORTED, "n_tokens * n_kv_heads too large");
+    if ((rc = check_device())) return rc;
+    msa::QuantArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.tok = tok_stride;
+    a.head = head_stride;
+    a.codes = codes;
+    a.ctok = code_tok_stride;
+    a.chead = code_head_stride;
+    a.scales = scales;
+    a.stok = scale_tok_stride;
+    a.shead = scale_head_stride;
+    a.n_tokens = n_tokens;
+    a.H = H;
+    return launched(msa::launch_quantize_kv8(a, static_cast<hipStream_t>(stream)), "quantize_kv8");
 }
 
 }  // extern "C"

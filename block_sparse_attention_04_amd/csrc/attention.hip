@@ -21,6 +21,8 @@
 // key mod 8) and each V^T operand is gathered by two transposing LDS reads
 // (ds_read_b64_tr_b16), with no repacking in registers.
 // Softmax runs in base 2 on scale*log2(e)-prescaled scores.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -41,7 +43,7 @@ __device__ __forceinline__ void softmax_init(Softmax &st) {
 
 // V tile of one 32-key chunk in LDS: key k's 256-byte row at k*256, its
 // 16-byte column unit u (dims 8u..8u+7) at unit u ^ (2 * (k % 8)).  With this
-// swizzle the stores below and the transposing reads in fold_staged touch
+// swizzle the stores below and the transposing reads in fold_rows touch
 // distinct banks.
 __device__ __forceinline__ int v_unit(int key, int u) { return u ^ (2 * (key & 7)); }
 
@@ -139,10 +141,86 @@ __device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
     }
 }
 
-// Fold the chunk [kbase, kbase + 32) (keys <= p visible) into st: K operands
-// from registers, V^T from the LDS tile (already staged and synced).
-__device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], const u32x4 (&ka)[2][4],
-                                            int kbase, int p, float scale_log2, const uint8_t *vt) {
+// Raw registers of one 32-key chunk of an int8 cache: K codes (key kbase +
+// 16*mt + lane%16, dims 32*(lane/16) + 16*h .. +15), V codes (key kbase +
+// 4*(lane/8) + kk, dims 8*(lane%8 + 8*hf) .. +7) and one scale per lane:
+// lanes 0..31 the key scale of key kbase + lane, lanes 32..63 the value scale
+// of key kbase + lane - 32.  Keys past p read key p, as in load_chunk.
+struct ChunkRegs8 {
+    u32x4 ka[2][2];
+    uint2 vr[4][2];
+    float sc;
+};
+
+// kc / vc: the chunk's first key (head g) in the code arrays; ksc / vsc: its
+// first key's scale; tok / stok: element strides between tokens.
+__device__ __forceinline__ void load_chunk8(ChunkRegs8 &c, const int8_t *kc, const int8_t *vc, const float *ksc,
+                                            const float *vsc, int64_t tok, int64_t stok, int last) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    const uint32_t t = (uint32_t)tok;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int8_t *src = kc + (uint32_t)min(16 * mt + lr, last) * t + 32u * lg;
+        c.ka[mt][0] = *reinterpret_cast<const u32x4 *>(src);
+        c.ka[mt][1] = *reinterpret_cast<const u32x4 *>(src + 16);
+    }
+    const int kg = lane >> 3, dc = lane & 7;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int8_t *src = vc + (uint32_t)min(4 * kg + kk, last) * t + 8u * dc;
+        c.vr[kk][0] = *reinterpret_cast<const uint2 *>(src);
+        c.vr[kk][1] = *reinterpret_cast<const uint2 *>(src + 64);
+    }
+    const float *sp = lane < 32 ? ksc : vsc;
+    c.sc = sp[(int64_t)min(lane & 31, last) * stok];
+}
+
+// 8 int8 codes -> 8 bf16 (exact: |code| <= 127 needs 7 significant bits).
+__device__ __forceinline__ float i8_at(uint32_t w, int k) { return (float)(int8_t)(uint8_t)(w >> (8 * k)); }
+__device__ __forceinline__ u32x4 i8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    return u32x4{pack_bf16x2(i8_at(w0, 0), i8_at(w0, 1)), pack_bf16x2(i8_at(w0, 2), i8_at(w0, 3)),
+                 pack_bf16x2(i8_at(w1, 0), i8_at(w1, 1)), pack_bf16x2(i8_at(w1, 2), i8_at(w1, 3))};
+}
+
+// K operands of an int8 chunk, as ChunkRegs::ka holds them for bf16.
+__device__ __forceinline__ void k_operands8(const ChunkRegs8 &c, u32x4 (&ka)[2][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ka[mt][2 * h] = i8x8_to_bf16(c.ka[mt][h][0], c.ka[mt][h][1]);
+            ka[mt][2 * h + 1] = i8x8_to_bf16(c.ka[mt][h][2], c.ka[mt][h][3]);
+        }
+}
+
+// V codes as bf16 into the V tile (stage_v's layout); the scales into the
+// wave's 64-float scale tile (keys' scales, then values').
+__device__ __forceinline__ void stage_v8(const ChunkRegs8 &c, uint8_t *vt, float *sct) {
+    const int lane = threadIdx.x & 63;
+    const int kg = lane >> 3, dc = lane & 7;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int key = 4 * kg + kk;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            *reinterpret_cast<u32x4 *>(vt + key * 256 + 16 * v_unit(key, dc + 8 * hf)) =
+                i8x8_to_bf16(c.vr[kk][hf].x, c.vr[kk][hf].y);
+    }
+    sct[lane] = c.sc;
+}
+
+// Fold the chunk [kbase, kbase + 32) (keys <= p visible) into row `row`
+// (wave-uniform) of a group of RW rows' states: K operands from registers,
+// V^T from the LDS tile (already staged and synced).  The scores and softmax
+// run once, with the row's max and sum picked by selects; only the rare
+// rescale and the 8 PV MFMAs sit under a branch on the row.
+// KV8 (int8 cache): every key's score is scaled by its key scale and every
+// weight by its value scale before the PV product (the sum of weights is
+// unscaled), with the scales from the wave's scale tile `sct`.
+template <int RW, bool KV8>
+__device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x4 (&qb)[4],
+                                          const u32x4 (&ka)[2][4], int kbase, int p, float scale_log2,
+                                          const uint8_t *vt, const float *sct) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     floatx4 sacc[2];
 #pragma unroll
@@ -152,11 +230,19 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
         for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
         sacc[mt] = acc;
     }
+    floatx4 ksc[2], vsc[2];
+    if constexpr (KV8) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            ksc[mt] = *reinterpret_cast<const floatx4 *>(sct + 16 * mt + 4 * lg);
+            vsc[mt] = *reinterpret_cast<const floatx4 *>(sct + 32 + 16 * mt + 4 * lg);
+        }
+    }
     // Online softmax over this lane's 8 keys of head lr.  Only the chunk that
-    // holds position p has keys to mask.  The max is taken on the raw scores
-    // and scaled once (scaling by a positive constant is monotone, so this is
-    // the max of the scaled scores bit for bit); each weight is one FMA and
-    // one exp2.
+    // holds position p has keys to mask.  The max is taken on the unscaled
+    // scores and scaled once (scaling by a positive constant is monotone, so
+    // this is the max of the scaled scores bit for bit); each weight is one
+    // FMA and one exp2.
     float z[2][4];
     float mx = -INFINITY;
     const bool edge = kbase + 31 > p;
@@ -165,91 +251,25 @@ __device__ __forceinline__ void fold_staged(Softmax &st, const u32x4 (&qb)[4], c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float v = sacc[mt][i];
+            if constexpr (KV8) v *= ksc[mt][i];
             if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
             z[mt][i] = v;
             mx = fmaxf(mx, v);
         }
     mx = max_over_lane_groups(mx) * scale_log2;   // finite: key kbase <= p is visible
-    // The reference max st.m moves only when a head's scores exceed it by more
-    // than kLazyLog2 (always on the first chunk): until then the weights are
-    // exp2(z - st.m) <= 2^kLazyLog2 and the accumulators need no rescale.  The
-    // result is the same softmax; st.m is the reference, not necessarily the max.
-    if (__ballot(mx > st.m + kLazyLog2) != 0) {
-        const float m_new = fmaxf(st.m, mx);
-        const float alpha = fast_exp2(st.m - m_new);    // 0 on the first chunk
-        st.l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
-        st.m = m_new;
-    }
-    float pr[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -st.m));
-            psum += pr[mt][i];
-        }
-    st.l += psum;
-    const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
-                      pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
-    // V^T operand of d-tile dt: lane (lg, lr) needs dim 16*dt + lr of keys
-    // 4*lg + 0..3 and 16 + 4*lg + 0..3 (the P^T k-order).  Lane t of group lg
-    // addresses the 8-byte piece (dims 16*dt + 4*(t%4) .. +3) of key 4*lg + t/4
-    // (and key + 16); the swizzle only flips address bits 5..7, so the piece
-    // for d-tile dt sits at the dt = 0 offset XOR (dt << 5).
-    const int vkey = 4 * lg + (lr >> 2);
-    const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const int rd = rd0 ^ (dt << 5);
-        const uint2 lo = lds_read_tr16(vt + rd);
-        const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
-        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-        st.o[dt] = mfma_16x16x32(va, pb, st.o[dt]);
-    }
-}
-
-// Fold the chunk into row `row` (wave-uniform) of a group of RW rows' states.
-// The same arithmetic as fold_staged on st[row]; the scores and softmax run
-// once, with the row's max and sum picked by selects, and only the rare
-// rescale and the 8 PV MFMAs sit under a branch on the row.
-template <int RW>
-__device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x4 (&qb)[4],
-                                          const u32x4 (&ka)[2][4], int kbase, int p, float scale_log2,
-                                          const uint8_t *vt) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-    floatx4 sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
-        sacc[mt] = acc;
-    }
-    float z[2][4];
-    float mx = -INFINITY;
-    const bool edge = kbase + 31 > p;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v = sacc[mt][i];
-            if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
-            z[mt][i] = v;
-            mx = fmaxf(mx, v);
-        }
-    mx = max_over_lane_groups(mx) * scale_log2;
     float m_cur = st[0].m, l_cur = st[0].l;
 #pragma unroll
     for (int i = 1; i < RW; ++i) {
         m_cur = row == i ? st[i].m : m_cur;
         l_cur = row == i ? st[i].l : l_cur;
     }
+    // The reference max moves only when a head's scores exceed it by more
+    // than kLazyLog2 (always on the first chunk): until then the weights are
+    // exp2(z - m) <= 2^kLazyLog2 and the accumulators need no rescale.  The
+    // result is the same softmax; m is the reference, not necessarily the max.
     if (__ballot(mx > m_cur + kLazyLog2) != 0) {
         const float m_new = fmaxf(m_cur, mx);
-        const float alpha = fast_exp2(m_cur - m_new);
+        const float alpha = fast_exp2(m_cur - m_new);    // 0 on the first chunk
         l_cur *= alpha;
 #pragma unroll
         for (int i = 0; i < RW; ++i)
@@ -267,6 +287,7 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
         for (int i = 0; i < 4; ++i) {
             pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -m_cur));
             psum += pr[mt][i];
+            if constexpr (KV8) pr[mt][i] *= vsc[mt][i];
         }
     l_cur += psum;
 #pragma unroll
@@ -276,6 +297,11 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
     }
     const u32x4 pb = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+    // V^T operand of d-tile dt: lane (lg, lr) needs dim 16*dt + lr of keys
+    // 4*lg + 0..3 and 16 + 4*lg + 0..3 (the P^T k-order).  Lane t of group lg
+    // addresses the 8-byte piece (dims 16*dt + 4*(t%4) .. +3) of key 4*lg + t/4
+    // (and key + 16); the swizzle only flips address bits 5..7, so the piece
+    // for d-tile dt sits at the dt = 0 offset XOR (dt << 5).
     const int vkey = 4 * lg + (lr >> 2);
     const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
     u32x4 va[8];
@@ -294,22 +320,24 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
         }
 }
 
-// Fold one loaded 32-key chunk into st (stage V^T, fold, release the tile).
+// Fold one loaded 32-key chunk into a single state st (stage V, fold,
+// release the tile).
 __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
-                                           int kbase, int p, float scale_log2, uint8_t *vt) {
+                                           int kbase, int p, float scale_log2, uint8_t *vt, float *) {
     stage_v(c, vt);
     wave_lds_sync();
-    fold_staged(st, qb, c.ka, kbase, p, scale_log2, vt);
+    fold_rows<1, false>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, c.ka, kbase, p, scale_log2, vt, nullptr);
     wave_lds_sync();   // reads finish before the next chunk overwrites the tile
 }
 
-__device__ __forceinline__ void attend_chunk32(Softmax &st, const u32x4 (&qb)[4],
-                                               const uint16_t *kseq, const uint16_t *vseq,
-                                               int64_t tok, int kbase, int p, float scale_log2,
-                                               uint8_t *vt) {
-    ChunkRegs c;
-    load_chunk(c, kseq, vseq, tok, kbase, p);
-    fold_chunk(st, qb, c, kbase, p, scale_log2, vt);
+__device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs8 &c,
+                                           int kbase, int p, float scale_log2, uint8_t *vt, float *sct) {
+    stage_v8(c, vt, sct);
+    wave_lds_sync();
+    u32x4 ka[2][4];
+    k_operands8(c, ka);
+    fold_rows<1, true>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, ka, kbase, p, scale_log2, vt, sct);
+    wave_lds_sync();
 }
 
 // Unit (row r, key head g) of a head-major enumeration: consecutive units are
@@ -349,8 +377,9 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 // different ranks of their own lists, long after L2 has turned over.
 constexpr int kInvalidKey = 1 << 25;   // above every block index of an int32 position
 
-template <int RW>
-__device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, uint8_t *vt, uint8_t *qt) {
+template <int RW, bool KV8>
+__device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, uint8_t *vt, uint8_t *qt,
+                                              float *sct) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     const int hq = a.H * kGroup;
     const int top_k = a.top_k;
@@ -375,11 +404,10 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         const int b = a.idx[((int64_t)rl * a.H + g) * top_k + lt];
         if (b >= 0 && b * kBlock <= ul.p) key = b;
     }
-    // element offset of the entry's block (first key, key head g) in k and v
-    const int64_t koff_l = block_token0(a.b, ul.s, seq_token0(a.b, ul.s), key == kInvalidKey ? 0 : key) * a.kv_tok +
-                           (int64_t)g * a.kv_head;
+    // token of the entry's block's first key in the key / value arrays
+    const int64_t tok_l = block_token0(a.b, ul.s, seq_token0(a.b, ul.s), key == kInvalidKey ? 0 : key);
     // Sort the entries by (block, lane): lane k of the e_* values holds the
-    // k-th entry (block * 4 + row, its row's position and K/V offset).
+    // k-th entry (block * 4 + row, its row's position and block token).
     const uint32_t skey = ((uint32_t)key << 6) | (uint32_t)lane;
     force_ready((int)skey);
     int rank = 0;
@@ -388,14 +416,14 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     const int dst = rank << 2;
     const int e_key = __builtin_amdgcn_ds_permute(dst, (key << 2) | (li & 3));
     const int e_p = __builtin_amdgcn_ds_permute(dst, ul.p);
-    const int e_lo = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)koff_l);
-    const int e_hi = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)((uint64_t)koff_l >> 32));
+    const int e_lo = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)tok_l);
+    const int e_hi = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)((uint64_t)tok_l >> 32));
     const int n_ent = (int)__popcll(__ballot(key != kInvalidKey));
 
     // A chunk of the walk: entry k (wave-uniform values), half hh of its block.
     struct Chunk {
         int kb, row, p;
-        int64_t koff;
+        int64_t tok;      // token of the chunk's first key
     };
     auto chunk_at = [&](int k, int hh) -> Chunk {
         Chunk c;
@@ -403,9 +431,8 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         c.row = e & 3;
         c.kb = (e >> 2) * kBlock + 32 * hh;
         c.p = __builtin_amdgcn_readlane(e_p, k);
-        c.koff = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) +
-                 (int64_t)(32 * hh) * a.kv_tok;     // the chunk's first key
+        c.tok = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) + 32 * hh;
         return c;
     };
     int k = 0, half = 0;
@@ -417,16 +444,31 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
             if (c.kb <= c.p) return true;
         }
     };
-    auto load = [&](ChunkRegs &r, const Chunk &c) {
-        load_chunk(r, a.k + c.koff, a.v + c.koff, a.kv_tok, 0, c.p - c.kb);
+    using Regs = typename std::conditional<KV8, ChunkRegs8, ChunkRegs>::type;
+    auto load = [&](Regs &r, const Chunk &c) {
+        const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
+        if constexpr (KV8) {
+            const int64_t soff = c.tok * a.s_tok + (int64_t)g * a.s_head;
+            load_chunk8(r, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, c.p - c.kb);
+        } else {
+            load_chunk(r, a.k + off, a.v + off, a.kv_tok, 0, c.p - c.kb);
+        }
     };
-    auto fold = [&](const ChunkRegs &r, const Chunk &c) {
+    auto fold = [&](const Regs &r, const Chunk &c) {
         u32x4 qb[4];
         read_q(qb, qt + c.row * kQTileBytes);
-        stage_v(r, vt);
-        wave_lds_sync();
-        fold_rows<RW>(st, c.row, qb, r.ka, c.kb, c.p, a.scale_log2, vt);
-        wave_lds_sync();   // reads finish before the next chunk overwrites the tile
+        if constexpr (KV8) {
+            stage_v8(r, vt, sct);
+            wave_lds_sync();
+            u32x4 ka[2][4];
+            k_operands8(r, ka);
+            fold_rows<RW, true>(st, c.row, qb, ka, c.kb, c.p, a.scale_log2, vt, sct);
+        } else {
+            stage_v(r, vt);
+            wave_lds_sync();
+            fold_rows<RW, false>(st, c.row, qb, r.ka, c.kb, c.p, a.scale_log2, vt, nullptr);
+        }
+        wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
     };
 
     force_ready(e_key);
@@ -439,7 +481,7 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     wave_lds_sync();   // q tiles written before the first fold reads them
     if (n_ent > 0) {
         Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
-        ChunkRegs ca, cb;
+        Regs ca, cb;
         load(ca, c0);
         for (;;) {
             const bool have1 = next_chunk(c1);
@@ -475,16 +517,17 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
 
 // Groups are enumerated head-major (consecutive groups: consecutive rows of one
 // key head), one per wave.
-template <int RW>
+template <int RW, bool KV8>
 __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
     __shared__ __attribute__((aligned(16))) uint8_t qt_all[4][RW * kQTileBytes];
+    __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
     const int wave = uniform(threadIdx.x >> 6);
     const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
     if (grp >= (int64_t)groups_per_head * a.H) return;
     const int g = (int)(grp / groups_per_head);
     const int r0 = (int)(grp % groups_per_head) * RW;
-    prefill_group<RW>(a, g, r0, vt_all[wave], qt_all[wave]);
+    prefill_group<RW, KV8>(a, g, r0, vt_all[wave], qt_all[wave], sc_all[wave]);
 }
 
 // Decode: the kept list of a (row, key head) is split into top_k partials of
@@ -495,8 +538,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per
 // partials, in slot order, with log-sum-exp weights.  The partials and their
 // merge order depend only on top_k, so a row's bits never depend on the rest
 // of the batch or on which workgroup finished last.
+template <bool KV8>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
     __shared__ int is_last;
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
@@ -520,13 +565,26 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         const int b = u.ok ? b_raw : -1;
         const int kb0 = b * kBlock, kb1 = kb0 + 32;
         if (b >= 0 && kb0 <= u.p) {
-            const int64_t off = block_token0(a.b, u.s, kv0, b) * a.kv_tok + (int64_t)u.g * a.kv_head;
-            const uint16_t *kblk = a.k + off, *vblk = a.v + off;   // the block's first key
-            ChunkRegs ca, cb;
-            load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
-            if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
-            fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave]);
-            if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave]);
+            const int64_t t0 = block_token0(a.b, u.s, kv0, b);     // the block's first key
+            const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+            if constexpr (KV8) {
+                const int64_t soff = t0 * a.s_tok + (int64_t)u.g * a.s_head;
+                const int64_t off1 = off + 32 * a.kv_tok, soff1 = soff + 32 * a.s_tok;
+                ChunkRegs8 ca, cb;
+                load_chunk8(ca, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, u.p - kb0);
+                if (kb1 <= u.p)
+                    load_chunk8(cb, a.k8 + off1, a.v8 + off1, a.ks + soff1, a.vs + soff1, a.kv_tok, a.s_tok,
+                                u.p - kb1);
+                fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave], sc_all[wave]);
+                if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave], sc_all[wave]);
+            } else {
+                const uint16_t *kblk = a.k + off, *vblk = a.v + off;
+                ChunkRegs ca, cb;
+                load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
+                if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
+                fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave], nullptr);
+                if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave], nullptr);
+            }
         }
         const float l = sum_over_lane_groups(st.l);
         float *part = part_unit + slot * (int64_t)kPartialFloats;
@@ -604,24 +662,31 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     if (a.lse && d0 == 0) a.lse[(int64_t)u.r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
+template <bool KV8>
+static void launch_prefill_t(const AttnArgs &a, hipStream_t st) {
     // 4 rows per wave while their 4 * top_k entries fit the 64 lanes, else 2.
     if (a.top_k <= 16) {
         const int gph = (a.b.total_rows + 3) / 4;
         const int64_t waves = (int64_t)gph * a.H;
-        hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+        hipLaunchKernelGGL((prefill_kernel<4, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
     } else {
         const int gph = (a.b.total_rows + 1) / 2;
         const int64_t waves = (int64_t)gph * a.H;
-        hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+        hipLaunchKernelGGL((prefill_kernel<2, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
     }
+}
+
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
+    if (a.k8) launch_prefill_t<true>(a, st);
+    else launch_prefill_t<false>(a, st);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
     const int wg = decode_wg_per_unit(a.top_k);
-    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
+    if (a.k8) hipLaunchKernelGGL(decode_kernel<true>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
+    else hipLaunchKernelGGL(decode_kernel<false>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
     return hipGetLastError();
 }
 

@@ -58,6 +58,11 @@ struct AttnArgs {
     float *lse;                  // [total_rows, H*16] or null
     unsigned *ws_count;          // decode: one arrival counter per (row, key head)
     float *ws_part;              // decode: top_k partials per (row, key head)
+    // int8 cache (k8 non-null): codes with the kv_tok / kv_head strides, one
+    // fp32 scale per (token, key head) with the s_tok / s_head strides
+    const int8_t *k8, *v8;
+    const float *ks, *vs;
+    int64_t s_tok, s_head;
 };
 
 // Selection fused after the decode-shaped indexer.
@@ -81,6 +86,19 @@ inline size_t decode_workspace_bytes(int64_t units, int top_k) {
     return decode_count_bytes(units) + (size_t)units * top_k * kPartialFloats * sizeof(float);
 }
 
+// int8 cache writer: one bf16 [tokens, H, 128] tensor -> codes + scales.
+struct QuantArgs {
+    const uint16_t *x;
+    int64_t tok, head;           // element strides of x
+    int8_t *codes;
+    int64_t ctok, chead;         // element strides of codes
+    float *scales;
+    int64_t stok, shead;         // element strides of scales
+    int64_t n_tokens;
+    int H;
+};
+
+hipError_t launch_quantize_kv8(const QuantArgs &a, hipStream_t st);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);

@@ -193,6 +193,51 @@ int msa_prefill(const msa_shape *shape, const msa_batch *batch,
                 int64_t kv_tok_stride, int64_t kv_head_stride,
                 const int32_t *block_idx, void *out, float *lse, void *stream);
 
+/*
+ * int8 key/value cache (opt-in; it changes the arithmetic, so it is checked
+ * against its own reference, not against the bf16 path).  Keys and values are
+ * int8 codes with one fp32 scale per (token, key head): the element value is
+ * code * scale.  Attention over it scales each key's score by the key's scale
+ * and each weight by the value's scale before the weighted sum (the softmax
+ * sum uses the unscaled weights), so the codes feed the matrix cores as exact
+ * bf16.  (TensorFold pull request 1388, commit adding the minimax_m3 family:
+ * keys and values cached as int8 with a scale a position and head, 57% of
+ * bf16's bytes; prompt chunks scale scores by the keys' scales and
+ * probabilities by the values'.  A later commit of the same pull request
+ * removed the int8 cache because it changes the model's arithmetic; here it
+ * is an alternative entry point and the bf16 path is unchanged.)
+ * Index keys stay bf16.  The paged layout applies to the codes and scales as
+ * to k and v.
+ */
+typedef struct msa_kv8 {
+    const int8_t *k, *v;            /* codes, element (token t, key head g, dim d) at
+                                       t*tok_stride + g*head_stride + d; rows 16-byte aligned */
+    const float *k_scale, *v_scale; /* scales, element (t, g) at t*scale_tok_stride + g*scale_head_stride */
+    int64_t tok_stride, head_stride;            /* elements (= bytes) */
+    int64_t scale_tok_stride, scale_head_stride;  /* elements */
+} msa_kv8;
+
+/*
+ * Write the int8 cache rows of n_tokens tokens from a bf16 tensor x (k or v,
+ * one call each), per (token, key head) row of head_dim values, in fp32:
+ * scale = max|x| / 127, code = round-half-even(x / scale) clamped to +-127
+ * (IEEE division); an all-zero row gets scale 0.  x must be finite.  This rule
+ * is this library's reading: the pages give the scale's granularity only.
+ */
+int msa_quantize_kv8(const msa_shape *shape, int64_t n_tokens,
+                     const void *x, int64_t tok_stride, int64_t head_stride,
+                     int8_t *codes, int64_t code_tok_stride, int64_t code_head_stride,
+                     float *scales, int64_t scale_tok_stride, int64_t scale_head_stride, void *stream);
+
+/* msa_prefill over an int8 cache (other arguments and errors as msa_prefill). */
+int msa_prefill_kv8(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv8 *kv,
+                    const int32_t *block_idx, void *out, float *lse, void *stream);
+
+/* msa_decode over an int8 cache (other arguments, workspace and errors as msa_decode). */
+int msa_decode_kv8(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv8 *kv,
+                   const int32_t *block_idx, void *out, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace msa_decode needs for total_rows rows (host
  * function; 0 for an invalid shape). */
 size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);

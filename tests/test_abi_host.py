@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH), reason="libmsa
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_the_four_steps():
