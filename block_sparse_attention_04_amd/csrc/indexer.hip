@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     __shared__ __attribute__((aligned(16))) uint8_t lds[3][kBlock * kLdsRow];
     __shared__ float otile[kTiledWaves][kRowsWave * kTiledBlocks];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
     const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
     if (s >= a.b.n_seqs) return;
@@ -152,28 +152,41 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     auto step = [&](int i, Stage &r) {
         const int b = b_begin + i;
         const uint8_t *buf = lds[i % 3];
-        floatx4 acc[NT][4];
+        // A operands of the block's 4 key tiles (both k-steps), read once.
+        u32x4 av[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const uint8_t *src = buf + (16 * mt + lr) * kLdsRow + 32 * lg;
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(src);
-            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(src + 16);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                floatx4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma_16x16x32(a0, bq[nt][0], c);
-                acc[nt][mt] = mfma_16x16x32(a1, bq[nt][1], c);
-            }
+            av[mt][0] = *reinterpret_cast<const u32x4 *>(src);
+            av[mt][1] = *reinterpret_cast<const u32x4 *>(src + 16);
         }
-        // Unconditional (clamped) so every step issues the same two loads and
-        // the compiler can wait for exactly the older set: block i+1 was
-        // requested two steps ago; buffer (i+1)%3 is not read this step.
-        sstore((i + 1) % 3, r);
-        gload(min(b + 3, b_cmp_end - 1), r);
         const bool need_mask = b * kBlock + kBlock - 1 > wave_p_min;
+        // Row tile by row tile: the MFMAs of tile nt are independent of the
+        // max-pool of tile nt-1, so the pool fills the MFMA pipeline's gaps.
         float m[NT];
+        floatx4 prev[4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) m[nt] = block_max_64(acc[nt], b * kBlock, prow[nt], need_mask);
+        for (int nt = 0; nt < NT; ++nt) {
+            floatx4 cur[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma_16x16x32(av[mt][0], bq[nt][0], c);
+                cur[mt] = mfma_16x16x32(av[mt][1], bq[nt][1], c);
+            }
+            if (nt == 1) {
+                // Unconditional (clamped) so every step issues the same two
+                // loads and the compiler can wait for exactly the older set:
+                // block i+1 was requested two steps ago; buffer (i+1)%3 is
+                // not read this step.
+                sstore((i + 1) % 3, r);
+                gload(min(b + 3, b_cmp_end - 1), r);
+            }
+            if (nt > 0) m[nt - 1] = block_max_64(prev, b * kBlock, prow[nt - 1], need_mask);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) prev[mt] = cur[mt];
+        }
+        m[NT - 1] = block_max_64(prev, b * kBlock, prow[NT - 1], need_mask);
         __syncthreads();
         emit(b, m);
     };
@@ -189,10 +202,15 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     gload(min(b_begin + 1, b_cmp_end - 1), r1);
     gload(min(b_begin + 2, b_cmp_end - 1), r0);
     __syncthreads();
-    for (int i = 0; i < nblk; i += 2) {
+    // Both halves unconditional inside the loop (the odd last block after
+    // it), so every path into a step has the same loads outstanding and each
+    // step waits only for its own register set, never for the prefetch.
+    int i = 0;
+    for (; i + 1 < nblk; i += 2) {
         step(i, r1);
-        if (i + 1 < nblk) step(i + 1, r0);
+        step(i + 1, r0);
     }
+    if (i < nblk) step(i, r1);
     for (int b = b_cmp_end; b < b_end; ++b) {
         float m[NT];
 #pragma unroll
