@@ -82,7 +82,7 @@ def kept_kv_bytes(case):
 
 
 PROFILE_KERNELS = {"chunk/attention": "prefill_kernel", "chunk/index_scores": "index_scores_tiled",
-                   "long/index_scores": "index_scores_window"}
+                   "long/index_scores": "index_scores_window", "long/index_select": "index_scores_window"}
 
 
 def source_digest() -> str:
@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--paged", action="store_true",
                     help="keys in pools of 64-token pages in a random page order, addressed through a page "
                          "table (the contiguous layout is the default)")
+    ap.add_argument("--head-major", action="store_true",
+                    help="contiguous key, value and index-key caches stored head-major ([heads, tokens, dim], "
+                         "passed as [tokens, heads, dim] views with their strides) instead of token-major")
     ap.add_argument("--kv8", action="store_true",
                     help="attention over the int8 key/value cache (codes + one fp32 scale per token and key "
                          "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
@@ -193,6 +196,8 @@ def main():
                     help="after timing, run one device copy of this size (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters in a profiler run)")
     args = ap.parse_args()
+    if args.paged and args.head_major:
+        ap.error("--head-major applies to the contiguous layout only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding by key head is described in the design notes)", file=sys.stderr)
@@ -214,6 +219,9 @@ def main():
     state = {}
     for name, case in cases.items():
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        if args.head_major:
+            for n in ("k", "v", "ik"):
+                base[n] = base[n].permute(1, 0, 2).contiguous().permute(1, 0, 2)
         page_table = None
         if args.paged:
             from workloads import to_pages
@@ -321,7 +329,8 @@ def main():
                                "+ long decode (1 row at 262,144 keys); 4 key heads x 16 query heads, "
                                "head_dim 128, index_dim 64, block 64, top-16 incl. local block",
                    "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
-                   "kv_layout": "paged (64-token pages, random order)" if args.paged else "contiguous",
+                   "kv_layout": ("paged (64-token pages, random order)" if args.paged else
+                                 "contiguous, head-major" if args.head_major else "contiguous, token-major"),
                    "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16"},
         "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
         "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
