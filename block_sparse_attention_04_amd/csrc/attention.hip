@@ -57,12 +57,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
                       (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16));
 }
 
-// Query B operand: head (lane % 16), dims 32*(lane/16) + 8*s + (0..7).
+// Query B operand of the 4 k-steps s: head (lane % 16) and 8 dims that depend
+// on the key operand's layout, which the two must share:
+//   interleaved (bf16 keys): dims 32*s + 8*(lane/16) -- one key load of a
+//                k-step covers 64 contiguous bytes of each key's row;
+//   blocked (int8 keys):     dims 32*(lane/16) + 8*s -- one 32-byte code load
+//                per lane covers all 4 k-steps.
+template <bool kBlocked>
 __device__ __forceinline__ void load_q(u32x4 (&qb)[4], const uint16_t *qrow_head0) {
     const int lane = threadIdx.x & 63;
-    const uint16_t *src = qrow_head0 + (lane & 15) * kHeadDim + 32 * (lane >> 4);
+    const uint16_t *src = qrow_head0 + (lane & 15) * kHeadDim + (kBlocked ? 32 : 8) * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qb[s] = load16(src + 8 * s);
+    for (int s = 0; s < 4; ++s) qb[s] = load16(src + (kBlocked ? 8 : 32) * s);
 }
 
 // 2^x with the hardware instruction (v_exp_f32, ~1 ulp).  Results below the
@@ -88,15 +94,16 @@ __device__ __forceinline__ void stage_q(uint8_t *qt, const uint16_t *qrow_head0)
 }
 
 // The query B operand (as load_q) from an LDS tile.
+template <bool kBlocked>
 __device__ __forceinline__ void read_q(u32x4 (&qb)[4], const uint8_t *qt) {
     const int lane = threadIdx.x & 63;
-    const uint8_t *src = qt + (lane & 15) * kQRowBytes + 64 * (lane >> 4);
+    const uint8_t *src = qt + (lane & 15) * kQRowBytes + (kBlocked ? 64 : 16) * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const u32x4 *>(src + 16 * s);
+    for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const u32x4 *>(src + (kBlocked ? 16 : 64) * s);
 }
 
 // Registers of one 32-key chunk: K as MFMA A operands (key kbase + 16*mt +
-// lane%16, dims 32*(lane/16) + 8*s) and V pieces (keys kbase + 4*(lane/8) +
+// lane%16, dims 32*s + 8*(lane/16): the interleaved layout) and V pieces (keys kbase + 4*(lane/8) +
 // kk, 16-byte units lane%8 and lane%8 + 8).  A key past p is read from key p
 // instead (always in bounds): its score is masked to -inf, so its weight is 0.
 struct ChunkRegs {
@@ -115,9 +122,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, c
     const char *vb = reinterpret_cast<const char *>(vseq + (int64_t)kbase * tok);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const uint32_t off = (uint32_t)min(16 * mt + lr, last) * tok_bytes + 64u * lg;
+        const uint32_t off = (uint32_t)min(16 * mt + lr, last) * tok_bytes + 16u * lg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) c.ka[mt][s] = *reinterpret_cast<const u32x4 *>(kb + off + 16 * s);
+        for (int s = 0; s < 4; ++s) c.ka[mt][s] = *reinterpret_cast<const u32x4 *>(kb + off + 64 * s);
     }
     const int kg = lane >> 3, dc = lane & 7;
 #pragma unroll
@@ -456,7 +463,7 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     };
     auto fold = [&](const Regs &r, const Chunk &c) {
         u32x4 qb[4];
-        read_q(qb, qt + c.row * kQTileBytes);
+        read_q<KV8>(qb, qt + c.row * kQTileBytes);
         if constexpr (KV8) {
             stage_v8(r, vt, sct);
             wave_lds_sync();
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         const int b_raw = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
         const int64_t kv0 = seq_token0(a.b, u.s);
         u32x4 qb[4];
-        load_q(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+        load_q<KV8>(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
         const int b = u.ok ? b_raw : -1;
         const int kb0 = b * kBlock, kb1 = kb0 + 32;
         if (b >= 0 && kb0 <= u.p) {

@@ -297,19 +297,26 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
                 bq1 = load16(src + 8);
             }
             const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * lg;
-            u32x4 av[kWindowBlocks][4][2];
-#pragma unroll
-            for (int q = 0; q < kWindowBlocks; ++q) {
+            // Two register sets: block q+2 is requested as soon as block q
+            // is computed (past the last visible block, that block again).
+            auto ld = [&](int q, u32x4 (&av)[4][2]) {
                 const int bq = b_begin + min(q, nblk - 1);
-                window_load_block(av[q], ik_g, block_token0(a.b, s, kv0, bq), a.ik_tok, bq, L, lr);
-            }
-#pragma unroll
-            for (int q = 0; q < kWindowBlocks; ++q) {
-                if (q < nblk) {
-                    const float m = window_block_max(av[q], bq0, bq1, b_begin + q, prow, p_first);
-                    if (lg == q) mine = m;
-                }
-            }
+                window_load_block(av, ik_g, block_token0(a.b, s, kv0, bq), a.ik_tok, bq, L, lr);
+            };
+            u32x4 ra[4][2], rb[4][2];
+            ld(0, ra);
+            ld(1, rb);
+            static_assert(kWindowBlocks == 4, "the two-set ring below covers four blocks");
+            float m = window_block_max(ra, bq0, bq1, b_begin, prow, p_first);
+            if (lg == 0) mine = m;
+            ld(2, ra);
+            m = window_block_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
+            if (lg == 1 && 1 < nblk) mine = m;
+            ld(3, rb);
+            m = window_block_max(ra, bq0, bq1, b_begin + 2, prow, p_first);
+            if (lg == 2 && 2 < nblk) mine = m;
+            m = window_block_max(rb, bq0, bq1, b_begin + 3, prow, p_first);
+            if (lg == 3 && 3 < nblk) mine = m;
         }
         const int blk = b_begin + lg;
         if (rvalid && blk < b_end) {
