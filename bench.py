@@ -140,6 +140,15 @@ class Timed:
     def mean_ms(self):
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.ev.items()}
 
+    def quantiles_ms(self):
+        """(p10, median, p90) of each call's event times."""
+        out = {}
+        for k, v in self.ev.items():
+            ts = sorted(a.elapsed_time(b) for a, b in v)
+            at = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+            out[k] = (at(0.1), at(0.5), at(0.9))
+        return out
+
 
 def cpu_baseline(cases, threads):
     """Time the oracle as it stands on a bounded sample: 96 rows of the chunk
@@ -187,6 +196,9 @@ def main():
     ap.add_argument("--head-major", action="store_true",
                     help="contiguous key, value and index-key caches stored head-major ([heads, tokens, dim], "
                          "passed as [tokens, heads, dim] views with their strides) instead of token-major")
+    ap.add_argument("--locality", type=float, default=None, metavar="A",
+                    help="secondary workload, not the headline one: the chunk's indexer queries follow "
+                         "iq_r = A*iq_(r-1) + sqrt(1-A^2)*z_r (e.g. 0.95), so neighbouring rows share blocks")
     ap.add_argument("--kv8", action="store_true",
                     help="attention over the int8 key/value cache (codes + one fp32 scale per token and key "
                          "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
@@ -210,7 +222,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    cases = {"chunk": config("chunk"), "long": config("long")}
+    cases = {"chunk": config("chunk") if args.locality is None else config("chunk", locality=args.locality),
+             "long": config("long")}
     reps = {"chunk": 2, "long": 4}       # replicas: >= 512 MB rotated per workload
     modes = {"chunk": "prefill", "long": "decode"}
     fused = {"chunk": False, "long": not args.unfused}
@@ -288,6 +301,7 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     rows = sum(c.total_rows for c in cases.values())
     kms = timer.mean_ms()
+    kq = timer.quantiles_ms()
 
     kernels = []
     for name, case in cases.items():
@@ -303,12 +317,15 @@ def main():
                 ach = wk["bytes"] / (ms * 1e-3) / 1e9
                 ent = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s")
             ent["frac"] = ent["achieved"] / ent["peak"]
-            ent.update(kernel=f"{name}/{kname}", ms=ms, algorithmic_flops=wk["flops"],
-                       algorithmic_bytes=wk["bytes"])
+            p10, p50, p90 = kq[f"{name}/{kname}"]
+            ent.update(kernel=f"{name}/{kname}", ms=ms, ms_p10=p10, ms_median=p50, ms_p90=p90,
+                       algorithmic_flops=wk["flops"], algorithmic_bytes=wk["bytes"])
             kernels.append(ent)
     dom = max(kernels, key=lambda e: e["ms"])
     roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roofline.update(kernel=dom["kernel"], traffic=profiled_traffic(dom["kernel"]))
+    # the committed counter summaries describe the default workload and layout only
+    variant = args.kv8 or args.paged or args.head_major or args.locality is not None
+    roofline.update(kernel=dom["kernel"], traffic=None if variant else profiled_traffic(dom["kernel"]))
 
     t_chunk = sum(kms[f"chunk/{k}"] for k in steps_of["chunk"])
     t_long = sum(kms[f"long/{k}"] for k in steps_of["long"])
@@ -331,7 +348,9 @@ def main():
                    "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
                    "kv_layout": ("paged (64-token pages, random order)" if args.paged else
                                  "contiguous, head-major" if args.head_major else "contiguous, token-major"),
-                   "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16"},
+                   "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16",
+                   "index_queries": ("i.i.d. N(0,1) per row" if args.locality is None else
+                                     f"secondary workload: AR(1) across the chunk's rows, a = {args.locality}")},
         "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
         "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
         "roofline": roofline,

@@ -217,3 +217,18 @@ def test_decode_workspace_reuse():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
     units = batch.total_rows * case.n_kv_heads
     assert int(ws[:units * 4].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.gpu
+def test_correlated_rows_share_blocks():
+    """Rows whose indexer queries are AR(1)-correlated keep mostly the same
+    blocks, so the four rows of a walk share many entries (the secondary
+    workload): the merged walk must still give every row exactly its own
+    blocks' result."""
+    case = make_case("locality", [9000, 5000], [300, 77], 2, seed=131, locality=0.95)
+    ref_idx = oracle.run(case, np.arange(case.total_rows))["block_idx"]
+    shared = np.mean([len(set(ref_idx[r, 0]) & set(ref_idx[r + 1, 0])) for r in range(case.rows[0] - 1)])
+    say(f"[gpu] locality: neighbouring rows share {shared:.1f} of 16 blocks")
+    assert shared >= 8
+    full_check(case, "prefill")
+    full_check(case, "decode", rows=np.arange(0, case.total_rows, 7))
