@@ -21,6 +21,8 @@
 //                       the 16-row tile is the wave's whole row set, so ik is
 //                       streamed straight from HBM into MFMA operand registers
 //                       and the key axis is spread over the whole chip.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 #include "msa_select.h"
@@ -31,13 +33,12 @@ namespace msa {
 // 16*lg + 8*s + (0..7), i.e. each lane reads 32 contiguous bytes of a vector.
 
 // Block max of one 16-row x 64-key MFMA result (4 M-tiles), causal-masked
-// against the lane's row position when the block reaches past the wave's
-// first row.  need_mask is wave-uniform: blocks left of the diagonal take the
-// plain max tree.
-__device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0, int p_row,
-                                              bool need_mask) {
+// (kMask) against the lane's row position; blocks left of the wave's first
+// row take the plain max tree.
+template <bool kMask>
+__device__ __forceinline__ float block_max_64c(const floatx4 (&acc)[4], int key0, int p_row) {
     float m;
-    if (__builtin_expect(need_mask, 0)) {
+    if constexpr (kMask) {
         const int lg = (threadIdx.x & 63) >> 4;
         m = -INFINITY;
 #pragma unroll
@@ -53,6 +54,12 @@ __device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0,
         m = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     }
     return max_over_lane_groups(m);
+}
+
+// The same with the mask decided at run time (need_mask is wave-uniform).
+__device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0, int p_row, bool need_mask) {
+    return __builtin_expect(need_mask, 0) ? block_max_64c<true>(acc, key0, p_row)
+                                          : block_max_64c<false>(acc, key0, p_row);
 }
 
 constexpr int kTiledWaves = 4;
@@ -163,30 +170,37 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
         const bool need_mask = b * kBlock + kBlock - 1 > wave_p_min;
         // Row tile by row tile: the MFMAs of tile nt are independent of the
         // max-pool of tile nt-1, so the pool fills the MFMA pipeline's gaps.
+        // The mask decision is taken once per block, so each variant is
+        // straight-line code the scheduler can interleave.
         float m[NT];
-        floatx4 prev[4];
+        auto tiles = [&](auto masked) {
+            constexpr bool kMask = decltype(masked)::value;
+            floatx4 prev[4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            floatx4 cur[4];
+            for (int nt = 0; nt < NT; ++nt) {
+                floatx4 cur[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                floatx4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma_16x16x32(av[mt][0], bq[nt][0], c);
-                cur[mt] = mfma_16x16x32(av[mt][1], bq[nt][1], c);
+                for (int mt = 0; mt < 4; ++mt) {
+                    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                    c = mfma_16x16x32(av[mt][0], bq[nt][0], c);
+                    cur[mt] = mfma_16x16x32(av[mt][1], bq[nt][1], c);
+                }
+                if (nt == 1) {
+                    // Unconditional (clamped) so every step issues the same two
+                    // loads and the compiler can wait for exactly the older set:
+                    // block i+1 was requested two steps ago; buffer (i+1)%3 is
+                    // not read this step.
+                    sstore((i + 1) % 3, r);
+                    gload(min(b + 3, b_cmp_end - 1), r);
+                }
+                if (nt > 0) m[nt - 1] = block_max_64c<kMask>(prev, b * kBlock, prow[nt - 1]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) prev[mt] = cur[mt];
             }
-            if (nt == 1) {
-                // Unconditional (clamped) so every step issues the same two
-                // loads and the compiler can wait for exactly the older set:
-                // block i+1 was requested two steps ago; buffer (i+1)%3 is
-                // not read this step.
-                sstore((i + 1) % 3, r);
-                gload(min(b + 3, b_cmp_end - 1), r);
-            }
-            if (nt > 0) m[nt - 1] = block_max_64(prev, b * kBlock, prow[nt - 1], need_mask);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) prev[mt] = cur[mt];
-        }
-        m[NT - 1] = block_max_64(prev, b * kBlock, prow[NT - 1], need_mask);
+            m[NT - 1] = block_max_64c<kMask>(prev, b * kBlock, prow[NT - 1]);
+        };
+        if (__builtin_expect(need_mask, 0)) tiles(std::true_type{});
+        else tiles(std::false_type{});
         __syncthreads();
         emit(b, m);
     };
