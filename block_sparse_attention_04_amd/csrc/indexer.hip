@@ -145,15 +145,18 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
         *reinterpret_cast<u32x4 *>(dst + 16) = r.x1;
     };
 
-    // Block maxima go to an LDS tile [wave rows][blocks of the range] and
-    // leave in one coalesced flush at the end, so no global store sits
-    // between the loop's prefetch loads.
+    // Block maxima go to an LDS tile [blocks of the range][wave rows] and
+    // leave in one flush at the end, so no global store sits between the
+    // loop's prefetch loads.  After the cross-lane max every lane group holds
+    // all NT row tiles' maxima, so lane l writes row l (tile l/16): one
+    // full-wave, conflict-free write per block.
+    static_assert(NT * 16 == kWave, "one wave row per lane");
     float *out_tile = otile[wave];
     auto emit = [&](int b, const float (&m)[NT]) {
-        if (lg == 0) {
+        float v = m[0];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) out_tile[(nt * 16 + lr) * kTiledBlocks + (b - b_begin)] = m[nt];
-        }
+        for (int nt = 1; nt < NT; ++nt) v = lg == nt ? m[nt] : v;
+        out_tile[(b - b_begin) * kRowsWave + lane] = v;
     };
     const int nblk = b_cmp_end - b_begin;
     auto step = [&](int i, Stage &r) {
@@ -232,19 +235,25 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
         emit(b, m);
     }
     wave_lds_sync();
-    // Flush: 4 lanes per row, 16 bytes each (blocks_per_wg == kTiledBlocks).
+    // Flush: lane l writes its row's blocks, 4 at a time (one 16-byte store
+    // when the range is whole and rows are 16-byte aligned).
     const int nb_here = b_end - b_begin;
+    const bool vec = nb_here == kTiledBlocks && (a.bs_stride & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
+    const int rl = wrow0 + lane;
+    if (rl < rows_s) {
+        float *dst = a.scores + ((int64_t)(row0 + rl) * a.H + g) * a.bs_stride + b_begin;
 #pragma unroll
-    for (int it = 0; it < kRowsWave * kTiledBlocks / 4 / kWave; ++it) {
-        const int e = it * kWave + lane;              // float4 index within the wave tile
-        const int rr = e / (kTiledBlocks / 4), c4 = (e % (kTiledBlocks / 4)) * 4;
-        const int rl = wrow0 + rr;
-        if (rl < rows_s) {
-            float *dst = a.scores + ((int64_t)(row0 + rl) * a.H + g) * a.bs_stride + b_begin + c4;
-            const float *srcv = out_tile + rr * kTiledBlocks + c4;
+        for (int c4 = 0; c4 < kTiledBlocks; c4 += 4) {
+            floatx4 v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (c4 + q < nb_here) dst[q] = srcv[q];
+            for (int q = 0; q < 4; ++q) v[q] = out_tile[(c4 + q) * kRowsWave + lane];
+            if (vec) {
+                *reinterpret_cast<floatx4 *>(dst + c4) = v;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (c4 + q < nb_here) dst[c4 + q] = v[q];
+            }
         }
     }
 }
