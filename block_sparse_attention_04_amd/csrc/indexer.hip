@@ -34,9 +34,10 @@ namespace msa {
 
 // Block max of one 16-row x 64-key MFMA result (4 M-tiles), causal-masked
 // (kMask) against the lane's row position; blocks left of the wave's first
-// row take the plain max tree.
+// row take the plain max tree.  lane_max_64 is the lane's part (its 16 keys
+// of the row), block_max_64c the full max in every lane group.
 template <bool kMask>
-__device__ __forceinline__ float block_max_64c(const floatx4 (&acc)[4], int key0, int p_row) {
+__device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, int p_row) {
     float m;
     if constexpr (kMask) {
         const int lg = (threadIdx.x & 63) >> 4;
@@ -53,7 +54,12 @@ __device__ __forceinline__ float block_max_64c(const floatx4 (&acc)[4], int key0
             t[mt] = fmaxf(fmaxf(acc[mt][0], acc[mt][1]), fmaxf(acc[mt][2], acc[mt][3]));
         m = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     }
-    return max_over_lane_groups(m);
+    return m;
+}
+
+template <bool kMask>
+__device__ __forceinline__ float block_max_64c(const floatx4 (&acc)[4], int key0, int p_row) {
+    return max_over_lane_groups(lane_max_64<kMask>(acc, key0, p_row));
 }
 
 // The same with the mask decided at run time (need_mask is wave-uniform).
@@ -147,17 +153,12 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
 
     // Block maxima go to an LDS tile [blocks of the range][wave rows] and
     // leave in one flush at the end, so no global store sits between the
-    // loop's prefetch loads.  After the cross-lane max every lane group holds
-    // all NT row tiles' maxima, so lane l writes row l (tile l/16): one
+    // loop's prefetch loads.  The cross-lane step of the NT = 4 row tiles is
+    // one reduce-and-scatter that leaves lane l with row l (tile l/16): one
     // full-wave, conflict-free write per block.
     static_assert(NT * 16 == kWave, "one wave row per lane");
     float *out_tile = otile[wave];
-    auto emit = [&](int b, const float (&m)[NT]) {
-        float v = m[0];
-#pragma unroll
-        for (int nt = 1; nt < NT; ++nt) v = lg == nt ? m[nt] : v;
-        out_tile[(b - b_begin) * kRowsWave + lane] = v;
-    };
+    auto emit = [&](int b, float v) { out_tile[(b - b_begin) * kRowsWave + lane] = v; };
     const int nblk = b_cmp_end - b_begin;
     auto step = [&](int i, Stage &r) {
         const int b = b_begin + i;
@@ -196,16 +197,17 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
                     sstore((i + 1) % 3, r);
                     gload(min(b + 3, b_cmp_end - 1), r);
                 }
-                if (nt > 0) m[nt - 1] = block_max_64c<kMask>(prev, b * kBlock, prow[nt - 1]);
+                if (nt > 0) m[nt - 1] = lane_max_64<kMask>(prev, b * kBlock, prow[nt - 1]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) prev[mt] = cur[mt];
             }
-            m[NT - 1] = block_max_64c<kMask>(prev, b * kBlock, prow[NT - 1]);
+            m[NT - 1] = lane_max_64<kMask>(prev, b * kBlock, prow[NT - 1]);
         };
         if (__builtin_expect(need_mask, 0)) tiles(std::true_type{});
         else tiles(std::false_type{});
+        const float v = max_scatter_lane_groups(m[0], m[1], m[2], m[3]);
         __syncthreads();
-        emit(b, m);
+        emit(b, v);
     };
 
     Stage r0, r1;
@@ -228,12 +230,7 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
         step(i + 1, r0);
     }
     if (i < nblk) step(i, r1);
-    for (int b = b_cmp_end; b < b_end; ++b) {
-        float m[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) m[nt] = -INFINITY;
-        emit(b, m);
-    }
+    for (int b = b_cmp_end; b < b_end; ++b) emit(b, -INFINITY);
     wave_lds_sync();
     // Flush: lane l writes its row's blocks, 4 at a time (one 16-byte store
     // when the range is whole and rows are 16-byte aligned).

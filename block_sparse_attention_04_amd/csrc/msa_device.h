@@ -79,6 +79,20 @@ __device__ __forceinline__ float max_over_lane_groups(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Four values reduced over the 4 lane groups at once and scattered: lane
+// group g receives the maximum of a_g over the groups (for its lane % 16).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, v_permlane16_swap the odd 16-lane rows of the
+// first with the even rows of the second.
+__device__ __forceinline__ float max_scatter_lane_groups(float a0, float a1, float a2, float a3) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
+    const float m02 = fmaxf(__uint_as_float(s02[0]), __uint_as_float(s02[1]));   // groups 0,1: a0; 2,3: a2
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
+    const float m13 = fmaxf(__uint_as_float(s13[0]), __uint_as_float(s13[1]));   // groups 0,1: a1; 2,3: a3
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(m02), __float_as_uint(m13), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
 __device__ __forceinline__ float sum_over_lane_groups(float x) {
     const uint32_t u = __float_as_uint(x);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
