@@ -9,8 +9,10 @@
 //
 // The contraction runs on v_mfma_f32_16x16x32_bf16 with keys on the M axis and
 // query rows on the N axis (S^T = IK * IQ^T): each lane's accumulator then
-// holds 4 keys of one row, so the 64-key max-pool is 15 in-lane maxima and
-// two cross-lane steps, and no score ever leaves the registers.
+// holds 4 keys of one row, so the 64-key max-pool is 15 in-lane maxima per
+// lane and, for four such maxima at once (four row tiles, or four blocks),
+// three cross-lane swaps that leave each lane group with one of them; no
+// score ever leaves the registers.
 //
 // Two tilings of the same computation:
 //   index_scores_tiled  prompt chunks: a workgroup owns 256 rows x a key range;
@@ -32,10 +34,10 @@ namespace msa {
 // k-assignment shared by both operands: k-step s, lane group lg -> index dims
 // 16*lg + 8*s + (0..7), i.e. each lane reads 32 contiguous bytes of a vector.
 
-// Block max of one 16-row x 64-key MFMA result (4 M-tiles), causal-masked
-// (kMask) against the lane's row position; blocks left of the wave's first
-// row take the plain max tree.  lane_max_64 is the lane's part (its 16 keys
-// of the row), block_max_64c the full max in every lane group.
+// The lane's part of the block max of one 16-row x 64-key MFMA result (4
+// M-tiles): its 16 keys of its row, causal-masked (kMask) against the lane's
+// row position; blocks left of the wave's first row take the plain max tree.
+// The 4 lane groups' parts are combined by max_scatter_lane_groups.
 template <bool kMask>
 __device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, int p_row) {
     float m;
@@ -55,17 +57,6 @@ __device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, 
         m = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     }
     return m;
-}
-
-template <bool kMask>
-__device__ __forceinline__ float block_max_64c(const floatx4 (&acc)[4], int key0, int p_row) {
-    return max_over_lane_groups(lane_max_64<kMask>(acc, key0, p_row));
-}
-
-// The same with the mask decided at run time (need_mask is wave-uniform).
-__device__ __forceinline__ float block_max_64(const floatx4 (&acc)[4], int key0, int p_row, bool need_mask) {
-    return __builtin_expect(need_mask, 0) ? block_max_64c<true>(acc, key0, p_row)
-                                          : block_max_64c<false>(acc, key0, p_row);
 }
 
 constexpr int kTiledWaves = 4;
@@ -268,8 +259,10 @@ __device__ __forceinline__ void window_load_block(u32x4 (&av)[4][2], const uint1
     }
 }
 
-__device__ __forceinline__ float window_block_max(const u32x4 (&av)[4][2], u32x4 bq0, u32x4 bq1, int b,
-                                                 int prow, int p_first) {
+// The lane's part of block b's max for its row (prow), masked when the block
+// reaches past the window's first row p_first (wave-uniform).
+__device__ __forceinline__ float window_lane_max(const u32x4 (&av)[4][2], u32x4 bq0, u32x4 bq1, int b, int prow,
+                                                 int p_first) {
     floatx4 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -277,7 +270,9 @@ __device__ __forceinline__ float window_block_max(const u32x4 (&av)[4][2], u32x4
         c = mfma_16x16x32(av[mt][0], bq0, c);
         acc[mt] = mfma_16x16x32(av[mt][1], bq1, c);
     }
-    return block_max_64(acc, b * kBlock, prow, b * kBlock + kBlock - 1 > p_first);
+    const int key0 = b * kBlock;
+    return __builtin_expect(key0 + kBlock - 1 > p_first, 0) ? lane_max_64<true>(acc, key0, prow)
+                                                           : lane_max_64<false>(acc, key0, prow);
 }
 
 // Each wave owns 4 consecutive blocks: all their loads go out before the
@@ -327,16 +322,16 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
             ld(0, ra);
             ld(1, rb);
             static_assert(kWindowBlocks == 4, "the two-set ring below covers four blocks");
-            float m = window_block_max(ra, bq0, bq1, b_begin, prow, p_first);
-            if (lg == 0) mine = m;
+            const float m0 = window_lane_max(ra, bq0, bq1, b_begin, prow, p_first);
             ld(2, ra);
-            m = window_block_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
-            if (lg == 1 && 1 < nblk) mine = m;
+            const float m1 = window_lane_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
             ld(3, rb);
-            m = window_block_max(ra, bq0, bq1, b_begin + 2, prow, p_first);
-            if (lg == 2 && 2 < nblk) mine = m;
-            m = window_block_max(rb, bq0, bq1, b_begin + 3, prow, p_first);
-            if (lg == 3 && 3 < nblk) mine = m;
+            const float m2 = window_lane_max(ra, bq0, bq1, b_begin + 2, prow, p_first);
+            const float m3 = window_lane_max(rb, bq0, bq1, b_begin + 3, prow, p_first);
+            // lane group lg ends with block b_begin + lg (past the visible
+            // blocks: a re-read, discarded)
+            const float v = max_scatter_lane_groups(m0, m1, m2, m3);
+            if (lg < nblk) mine = v;
         }
         const int blk = b_begin + lg;
         if (rvalid && blk < b_end) {
