@@ -50,11 +50,14 @@ __device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, 
             for (int i = 0; i < 4; ++i)
                 m = fmaxf(m, key0 + 16 * mt + 4 * lg + i > p_row ? -INFINITY : acc[mt][i]);
     } else {
-        float t[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            t[mt] = fmaxf(fmaxf(acc[mt][0], acc[mt][1]), fmaxf(acc[mt][2], acc[mt][3]));
-        m = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+        // 16 values in 8 three-input maxima (v_max3_f32): five triples, two
+        // triples of those (with the 16th value), one last pair
+        const float u0 = fmaxf(fmaxf(acc[0][0], acc[0][1]), acc[0][2]);
+        const float u1 = fmaxf(fmaxf(acc[0][3], acc[1][0]), acc[1][1]);
+        const float u2 = fmaxf(fmaxf(acc[1][2], acc[1][3]), acc[2][0]);
+        const float u3 = fmaxf(fmaxf(acc[2][1], acc[2][2]), acc[2][3]);
+        const float u4 = fmaxf(fmaxf(acc[3][0], acc[3][1]), acc[3][2]);
+        m = fmaxf(fmaxf(fmaxf(u0, u1), u2), fmaxf(fmaxf(u3, u4), acc[3][3]));
     }
     return m;
 }
