@@ -17,7 +17,7 @@
 // Two tilings of the same computation:
 //   index_scores_tiled  prompt chunks: a workgroup owns 256 rows x a key range;
 //                       each 64-key tile of ik is staged once in LDS (a ring
-//                       of three, loads two tiles ahead) and reused by the 4
+//                       of four, one barrier per two tiles) and reused by the 4
 //                       waves' 64 rows each.
 //   index_scores_window decode steps and windows (<= 16 rows per sequence):
 //                       the 16-row tile is the wave's whole row set, so ik is
@@ -70,7 +70,7 @@ template <int NT>
 __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int blocks_per_wg) {
     constexpr int kRowsWave = 16 * NT;
     constexpr int kRowsWg = kRowsWave * kTiledWaves;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[3][kBlock * kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][kBlock * kLdsRow];
     __shared__ float otile[kTiledWaves][kRowsWave * kTiledBlocks];
 
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -114,8 +114,11 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     const int wave_p_min = p_base + wrow0;
 
     // Staging: thread t copies 32 bytes (piece t&3) of key t>>2 of the tile.
-    // Three LDS buffers and two register sets: block i+3 is requested while
-    // block i is computed, so each load has two block-times to arrive.
+    // Four LDS slots and two register sets: step i computes block i from slot
+    // i%4, stores block i+2 (requested two steps earlier) into slot (i+2)%4
+    // and requests block i+4.  A slot is written two steps before it is read
+    // and two steps after its previous read, so one barrier every two steps
+    // (after the odd ones) orders both.
     const int st_key = threadIdx.x >> 2, st_piece = threadIdx.x & 3;
     const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * st_piece;
     struct Stage {
@@ -154,9 +157,9 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     float *out_tile = otile[wave];
     auto emit = [&](int b, float v) { out_tile[(b - b_begin) * kRowsWave + lane] = v; };
     const int nblk = b_cmp_end - b_begin;
-    auto step = [&](int i, Stage &r) {
+    auto step = [&](int i, Stage &r, bool sync) {
         const int b = b_begin + i;
-        const uint8_t *buf = lds[i % 3];
+        const uint8_t *buf = lds[i & 3];
         // A operands of the block's 4 key tiles (both k-steps), read once.
         u32x4 av[4][2];
 #pragma unroll
@@ -186,10 +189,10 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
                 if (nt == 1) {
                     // Unconditional (clamped) so every step issues the same two
                     // loads and the compiler can wait for exactly the older set:
-                    // block i+1 was requested two steps ago; buffer (i+1)%3 is
+                    // block i+2 was requested two steps ago; slot (i+2)%4 is
                     // not read this step.
-                    sstore((i + 1) % 3, r);
-                    gload(min(b + 3, b_cmp_end - 1), r);
+                    sstore((i + 2) & 3, r);
+                    gload(min(b + 4, b_cmp_end - 1), r);
                 }
                 if (nt > 0) m[nt - 1] = lane_max_64<kMask>(prev, b * kBlock, prow[nt - 1]);
 #pragma unroll
@@ -200,30 +203,36 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
         if (__builtin_expect(need_mask, 0)) tiles(std::true_type{});
         else tiles(std::false_type{});
         const float v = max_scatter_lane_groups(m[0], m[1], m[2], m[3]);
-        __syncthreads();
+        if (sync) __syncthreads();
         emit(b, v);
     };
 
     Stage r0, r1;
-    if (nblk > 0) gload(b_begin, r0);
+    if (nblk > 0) {
+        gload(b_begin, r0);
+        gload(min(b_begin + 1, b_cmp_end - 1), r1);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {  // iq operands complete before the loop
         force_ready(bq[nt][0]);
         force_ready(bq[nt][1]);
     }
-    if (nblk > 0) sstore(0, r0);
-    gload(min(b_begin + 1, b_cmp_end - 1), r1);
+    if (nblk > 0) {
+        sstore(0, r0);
+        sstore(1, r1);
+    }
     gload(min(b_begin + 2, b_cmp_end - 1), r0);
+    gload(min(b_begin + 3, b_cmp_end - 1), r1);
     __syncthreads();
     // Both halves unconditional inside the loop (the odd last block after
     // it), so every path into a step has the same loads outstanding and each
     // step waits only for its own register set, never for the prefetch.
     int i = 0;
     for (; i + 1 < nblk; i += 2) {
-        step(i, r1);
-        step(i + 1, r0);
+        step(i, r0, false);
+        step(i + 1, r1, true);
     }
-    if (i < nblk) step(i, r1);
+    if (i < nblk) step(i, r0, false);
     for (int b = b_cmp_end; b < b_end; ++b) emit(b, -INFINITY);
     wave_lds_sync();
     // Flush: lane l writes its row's blocks, 4 at a time (one 16-byte store
