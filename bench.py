@@ -150,6 +150,52 @@ class Timed:
         return out
 
 
+def measured_peaks(torch, msa, dev):
+    """What this device sustains, beside the published peaks: the library's
+    streaming-read kernel over 2 GiB and its loop of independent bf16 MFMA
+    chains (include/msa_peaks.h), each the best of 5 timed launches."""
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    t_read = best_ms(lambda: msa.msa_peaks_stream_read(buf, sink))
+    del buf
+    wg, iters = 256 * 8, 4000
+    t_mfma = best_ms(lambda: msa.msa_peaks_mfma(sink, wg, iters))
+    flops = wg * 4 * iters * 4 * 16384
+    return {"hbm_read_GBs": nbytes / (t_read * 1e-3) / 1e9,
+            "bf16_mfma_TFLOPs": flops / (t_mfma * 1e-3) / 1e12,
+            "hbm_read_frac_of_published": nbytes / (t_read * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "bf16_mfma_frac_of_published": flops / (t_mfma * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "sclk": _sclk(),
+            "method": "msa_peaks_stream_read over 2 GiB; msa_peaks_mfma with 2,048 workgroups x 4 waves x "
+                      "4,000 rounds of 4 independent v_mfma_f32_16x16x32_bf16; best of 5 launches each"}
+
+
+def _sclk():
+    """The shader clock rocm-smi reports right after the MFMA loop, or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for line in out.splitlines():
+        if "sclk" in line:
+            return line.split(":", 2)[-1].strip()
+    return None
+
+
 def cpu_baseline(cases, threads):
     """Time the oracle as it stands on a bounded sample: 96 rows of the chunk
     and the decode row; scale to rows/s of the full step."""
@@ -204,6 +250,8 @@ def main():
                          "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the device's sustained HBM read and bf16 MFMA rates after timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters in a profiler run)")
@@ -356,6 +404,12 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, msa, dev)
+        res["measured_peaks"] = peaks
+        meas = peaks["hbm_read_GBs"] if roofline["unit"] == "GB/s" else peaks["bf16_mfma_TFLOPs"]
+        roofline["measured_peak"] = meas
+        roofline["frac_of_measured"] = roofline["achieved"] / meas
     if args.copy_calibration_mib:
         # an elementwise kernel that reads n bytes and writes n bytes once
         n = args.copy_calibration_mib << 20

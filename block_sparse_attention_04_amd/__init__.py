@@ -45,7 +45,7 @@ class _BatchC(ctypes.Structure):
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
            "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
-           "msa_last_error", "msa_version")
+           "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_mfma")
 
 
 class _KV8C(ctypes.Structure):
@@ -85,6 +85,10 @@ def lib():
             L.msa_last_error.restype = ctypes.c_char_p
             L.msa_version.argtypes = []
             L.msa_version.restype = ctypes.c_char_p
+            L.msa_peaks_stream_read.argtypes = [vp, i64, vp, vp]
+            L.msa_peaks_mfma.argtypes = [vp, i32, i32, vp]
+            L.msa_peaks_stream_read.restype = ctypes.c_int
+            L.msa_peaks_mfma.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -366,3 +370,17 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
     else:
         raise ValueError(mode)
     return out
+
+
+# Measurement kernels (include/msa_peaks.h), not part of the method.
+def msa_peaks_stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor buf once (the device's sustained
+    HBM read rate, timed by the caller).  sink: a device tensor of >= 1 uint32."""
+    _check(lib().msa_peaks_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def msa_peaks_mfma(sink, workgroups: int, iters: int, stream=None):
+    """workgroups x 4 waves x iters x 4 bf16 16x16x32 MFMAs (16,384 FLOP each):
+    the device's sustained dense bf16 rate, timed by the caller.  sink: a
+    device float32 tensor of >= 256 elements."""
+    _check(lib().msa_peaks_mfma(_ptr(sink), int(workgroups), int(iters), _stream(stream)))

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
-SOURCES = ["api.hip", "indexer.hip", "select.hip", "attention.hip", "kvcache.hip"]
+SOURCES = ["api.hip", "indexer.hip", "select.hip", "attention.hip", "kvcache.hip", "peaks.hip"]
 # Per-source extras.  indexer: MFMA accumulators in ordinary VGPRs, so the
 # max-pool reads them without v_accvgpr copies, and maxima skip NaN
 # canonicalisation (scores are finite or -inf) -- measured faster; the

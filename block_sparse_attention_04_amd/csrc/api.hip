@@ -25,6 +25,19 @@ int ok() {
     return MSA_OK;
 }
 
+}  // namespace
+
+// Library-internal: the message msa_last_error() returns (other sources of
+// the library report through it too).
+namespace msa {
+int report(int status, const char *msg) {
+    snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+    return status;
+}
+}  // namespace msa
+
+namespace {
+
 int check_shape(const msa_shape *sh) {
     if (!sh) return fail(MSA_ERR_INVALID, "shape is NULL");
     if (sh->n_kv_heads < 1) return fail(MSA_ERR_INVALID, "n_kv_heads=%d must be >= 1", sh->n_kv_heads);

@@ -98,6 +98,9 @@ struct QuantArgs {
     int H;
 };
 
+// Sets the message msa_last_error() returns (empty for success) and returns status.
+int report(int status, const char *msg);
+
 hipError_t launch_quantize_kv8(const QuantArgs &a, hipStream_t st);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);

@@ -2,6 +2,7 @@
 include/msa.h declares, and validates arguments before anything reaches the
 device.  No kernel is launched by these tests."""
 import ctypes
+import glob
 import os
 import re
 
@@ -12,18 +13,21 @@ import block_sparse_attention_04_amd as msa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH), reason="libmsa.so not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_four_steps():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for n in ("msa_index_scores", "msa_select_blocks", "msa_prefill", "msa_decode"):
         assert n in names
 
@@ -189,3 +193,18 @@ def test_paged_batch_checks():
     b.c.page_table = 1024
     b.c.pages_per_seq = 3                                           # 3 * 64 < 200 keys
     assert _call_index(sh, b, bs=4) == -1 and "pages_per_seq" in _err()
+
+
+def test_peaks_kernels_reject_bad_arguments():
+    """The measurement entry points validate before launching (no GPU needed)."""
+    L = msa.lib()
+    sink = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    assert L.msa_peaks_stream_read(None, 1024, sink, None) == -1
+    assert L.msa_peaks_stream_read(ctypes.c_void_p(16), 1000, sink, None) == -1     # not a multiple of 16
+    assert L.msa_peaks_stream_read(ctypes.c_void_p(24), 1024, sink, None) == -1     # misaligned
+    assert L.msa_peaks_stream_read(ctypes.c_void_p(16), 0, sink, None) == -1
+    assert L.msa_peaks_mfma(None, 1, 1, None) == -1
+    assert L.msa_peaks_mfma(sink, 0, 1, None) == -1
+    assert L.msa_peaks_mfma(sink, 1, 0, None) == -1
+    assert L.msa_peaks_mfma(sink, 1 << 21, 1, None) == -1
+    assert b"mfma" in L.msa_last_error()
