@@ -300,13 +300,17 @@ template <bool kSelect>
 __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t) {
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
-    const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
+    // blockIdx.x = key range * H + key head: the H workgroups of one key range
+    // are dispatched together, so tokens whose index keys sit side by side
+    // (token-major caches) are read by all heads at about the same time.
+    const int s = blockIdx.z, g = blockIdx.x % a.H, xr = blockIdx.x / a.H;
+    const int unit = s * a.H + g;                        // (sequence, key head)
     if (s >= a.b.n_seqs) return;
     const int row0 = a.b.cu_rows[s];
     const int rows_s = a.b.cu_rows[s + 1] - row0;
     const int L = a.b.seq_lens[s];
     if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;   // whole (s, g) alike
-    const int b_begin = (blockIdx.x * 4 + wave) * kWindowBlocks;
+    const int b_begin = (xr * 4 + wave) * kWindowBlocks;
     const int b_end = min(b_begin + kWindowBlocks, a.bs_stride);
     const int p_first = L - rows_s;
     if (b_begin < b_end) {
@@ -366,14 +370,14 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(t.count + blockIdx.z, 1u, __ATOMIC_RELAXED,
+            const unsigned prev = __hip_atomic_fetch_add(t.count + unit, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == gridDim.x - 1;
+            is_last = prev == gridDim.x / a.H - 1;
         }
         __syncthreads();
         if (!is_last) return;
         if (threadIdx.x == 0)   // leave the counter at zero for the next call
-            __hip_atomic_store(t.count + blockIdx.z, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(t.count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (t.wave_mode) {
             // one wave per row, rows wave, wave + 4, ...
             uint32_t *keys = dyn + wave * t.cap;
@@ -403,7 +407,7 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
     const int gz = a.b.n_seqs * a.H;
     if (a.b.max_rows <= 16) {
         const int per_wg = kWindowBlocks * 4;
-        dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, gz);
+        dim3 grid((a.bs_stride + per_wg - 1) / per_wg * a.H, 1, a.b.n_seqs);
         hipLaunchKernelGGL(index_scores_window<false>, grid, dim3(256), 0, st, a, SelectTail{});
     } else {
         constexpr int NT = 4;
@@ -416,7 +420,7 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
 
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st) {
     const int per_wg = kWindowBlocks * 4;
-    dim3 grid((a.bs_stride + per_wg - 1) / per_wg, 1, a.b.n_seqs * a.H);
+    dim3 grid((a.bs_stride + per_wg - 1) / per_wg * a.H, 1, a.b.n_seqs);
     const int nb_max = (a.b.max_seq_len + kBlock - 1) / kBlock;
     t.cap = ((nb_max + 63) / 64) * 64;                      // staged keys per row
     // one wave per row when a sequence has several rows and 4 stages fit 64 KiB
