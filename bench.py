@@ -150,6 +150,59 @@ class Timed:
         return out
 
 
+def other_configs(torch, msa, dev, steps=20):
+    """The other named workloads, for reference beside the headline line (not
+    part of `value`): the 2,048-token prefill, the batched decode of 4 x 32,768
+    keys and the four 16-row verify windows, each timed per library call with
+    HIP events (mean over `steps` passes after two warm-up passes)."""
+    from workloads import config
+    out = {}
+    for name, mode in (("tiny", "prefill"), ("decode", "decode"), ("windows", "decode")):
+        case = config(name)
+        t = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
+        batch = msa.Batch(case.seq_lens, case.rows, device=dev)
+        fused = mode == "decode"
+        o = msa.run_path(shape, batch, t, mode, fused=fused)
+        if fused:
+            calls = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
+                                                                   o["block_idx"], o["select_workspace"]))]
+        else:
+            calls = [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])),
+                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"]))]
+        if mode == "prefill":
+            calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
+                                                               o["out"], o["lse"])))
+        else:
+            calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
+                                                              o["out"], o["lse"], o["workspace"])))
+        timer = Timed(torch)
+        for i in range(steps + 2):
+            for kname, fn in calls:
+                if i < 2:
+                    fn()
+                else:
+                    timer.run(kname, fn)
+        torch.cuda.synchronize()
+        kms = timer.mean_ms()
+        work = algorithmic_work(case)
+        total = sum(kms.values())
+        ent = {"mode": mode, "rows": case.total_rows, "seq_lens": case.seq_lens, "kv_heads": case.n_kv_heads,
+               "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
+               "kernels": {k: {"ms": v} for k, v in kms.items()}}
+        for k, v in kms.items():
+            wk = work[k]
+            if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+                ent["kernels"][k].update(tflops=wk["flops"] / (v * 1e-3) / 1e12,
+                                         frac=wk["flops"] / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
+            else:
+                ent["kernels"][k].update(gbs=wk["bytes"] / (v * 1e-3) / 1e9,
+                                         frac=wk["bytes"] / (v * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        out[name] = ent
+        del t, o
+    return out
+
+
 def measured_peaks(torch, msa, dev):
     """What this device sustains, beside the published peaks: the library's
     streaming-read kernel over 2 GiB and its loop of independent bf16 MFMA
@@ -250,6 +303,8 @@ def main():
                          "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the reference timings of the other named workloads after the headline step")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the device's sustained HBM read and bf16 MFMA rates after timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -404,6 +459,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_others:
+        res["other_configs"] = other_configs(torch, msa, dev)
     if not args.no_peaks:
         peaks = measured_peaks(torch, msa, dev)
         res["measured_peaks"] = peaks
