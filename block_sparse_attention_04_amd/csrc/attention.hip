@@ -557,9 +557,13 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     if (unit >= (int64_t)a.b.total_rows * a.H) return;
     const Unit u = make_unit(a, unit);
     const int hq = a.H * kGroup;
-    float *part_unit = a.ws_part + unit * a.top_k * (int64_t)kPartialFloats;
+    float *part_unit = a.ws_part + unit * wg_per_unit * (int64_t)kPartialFloats;
     const int slot = split * 4 + wave;
-
+    // Each wave's partial (max, sum, unnormalised values) goes to LDS: m and l
+    // to wm/wl, the 16 x 128 values to the wave's V staging area, free once
+    // its folds are done.
+    __shared__ float wm[4][16], wl[4][16];
+    float *wo = reinterpret_cast<float *>(vt_all[wave]);
     if (slot < a.top_k) {
         Softmax st;
         softmax_init(st);
@@ -594,71 +598,111 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
             }
         }
         const float l = sum_over_lane_groups(st.l);
-        float *part = part_unit + slot * (int64_t)kPartialFloats;
         if (lg == 0) {
-            part[lr] = st.m;
-            part[16 + lr] = l;
+            wm[wave][lr] = st.m;
+            wl[wave][lr] = l;
         }
-        float *acc = part + 32 + lr * kHeadDim + 4 * lg;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(acc + 16 * dt) = st.o[dt];
-    }
-    // Publish this workgroup's partials, count it in; the last one merges.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.ws_count + unit, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        is_last = prev == (unsigned)(wg_per_unit - 1);
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(wo + lr * kHeadDim + 16 * dt + 4 * lg) = st.o[dt];
+    } else if (lane < 16) {
+        wm[wave][lane] = -INFINITY;
+        wl[wave][lane] = 0.f;
     }
     __syncthreads();
-    if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (threadIdx.x == 0)   // leave the counter at zero for the next call
-        __hip_atomic_store(a.ws_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!u.ok) return;
 
-    // Merge: thread = (head h, 8 dims), partials in slot order.  Loads go out
-    // in batches of 8 partials (no loop-carried load chains).
+    // Thread = (head h, dims d0..d0+7).  Combine the workgroup's four waves in
+    // slot order into one partial.
     const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-    float ms[kMaxTopK];
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        ms[s] = s < a.top_k ? part_unit[s * kPartialFloats + h] : -INFINITY;
-        M = fmaxf(M, ms[s]);
-    }
-    float accv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
     float Ls = 0.f;
+    float accv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
-        for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
-            if (s0 >= a.top_k) break;
-            float lv[8];
-            floatx4 x0[8], x1[8];
+        for (int w = 0; w < 4; ++w) {
+            const float mw = wm[w][h];
+            if (mw == -INFINITY) continue;   // an empty partial (no visible key, or no slot)
+            const float wgt = exp2f(mw - M);
+            Ls += wgt * wl[w][h];
+            const float *src = reinterpret_cast<const float *>(vt_all[w]) + h * kHeadDim + d0;
+            const floatx4 x0 = *reinterpret_cast<const floatx4 *>(src);
+            const floatx4 x1 = *reinterpret_cast<const floatx4 *>(src + 4);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                // an empty partial (no visible key) or a slot past top_k has weight 0;
-                // read slot 0 instead so every load stays in bounds and finite
-                const bool use = s0 + q < a.top_k && ms[s0 + q] != -INFINITY;
-                const float *ps = part_unit + (use ? s0 + q : 0) * kPartialFloats;
-                lv[q] = ps[16 + h];
-                x0[q] = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0);
-                x1[q] = *reinterpret_cast<const floatx4 *>(ps + 32 + h * kHeadDim + d0 + 4);
+            for (int i = 0; i < 4; ++i) {
+                accv[i] += wgt * x0[i];
+                accv[4 + i] += wgt * x1[i];
             }
+        }
+    }
+
+    if (wg_per_unit > 1) {
+        // Publish the workgroup's partial with device-scoped stores (written
+        // through to the device level), wait for them, then count the
+        // workgroup in: no release fence, which would write back the whole L2
+        // in each of the many workgroups.  The last one to arrive merges, in
+        // split order, reading the others' partials with device-scoped loads.
+        float *pw = part_unit + split * (int64_t)kPartialFloats;
+        if (d0 == 0) {
+            __hip_atomic_store(pw + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pw + 16 + h, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const bool use = s0 + q < a.top_k && ms[s0 + q] != -INFINITY;
-                if (!use) continue;
-                const float w = exp2f(ms[s0 + q] - M);
-                Ls += w * lv[q];
+        for (int i = 0; i < 8; ++i)
+            __hip_atomic_store(pw + 32 + h * kHeadDim + d0 + i, accv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(a.ws_count + unit, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == (unsigned)(wg_per_unit - 1);
+        }
+        __syncthreads();
+        if (!is_last) return;
+        if (threadIdx.x == 0)   // leave the counter at zero for the next call
+            __hip_atomic_store(a.ws_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!u.ok) return;
+        // every split's max first (one batch of loads), then its values
+        float ms[kMaxTopK / 4];
+        M = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    accv[i] += w * x0[q][i];
-                    accv[4 + i] += w * x1[q][i];
+        for (int w = 0; w < kMaxTopK / 4; ++w) {
+            ms[w] = w < wg_per_unit ? __hip_atomic_load(part_unit + w * kPartialFloats + h, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : -INFINITY;
+            M = fmaxf(M, ms[w]);
+        }
+        Ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) accv[i] = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w0 = 0; w0 < kMaxTopK / 4; w0 += 4) {
+                if (w0 >= wg_per_unit) break;
+                float lv[4], xv[4][8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // an empty partial or a split past the last has weight 0: read
+                    // split 0 instead so every load stays in bounds
+                    const bool use = w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY;
+                    const float *ps = part_unit + (use ? w0 + q : 0) * kPartialFloats;
+                    lv[q] = __hip_atomic_load(ps + 16 + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        xv[q][i] = __hip_atomic_load(ps + 32 + h * kHeadDim + d0 + i, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bool use = w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY;
+                    if (!use) continue;
+                    const float wgt = exp2f(ms[w0 + q] - M);
+                    Ls += wgt * lv[q];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) accv[i] += wgt * xv[q][i];
                 }
             }
         }
+    } else if (!u.ok) {
+        return;
     }
     const int hh = u.g * kGroup + h;
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;

@@ -57,7 +57,7 @@ struct AttnArgs {
     uint16_t *out;               // [total_rows, H*16, 128]
     float *lse;                  // [total_rows, H*16] or null
     unsigned *ws_count;          // decode: one arrival counter per (row, key head)
-    float *ws_part;              // decode: top_k partials per (row, key head)
+    float *ws_part;              // decode: one partial per workgroup of a (row, key head)
     // int8 cache (k8 non-null): codes with the kv_tok / kv_head strides, one
     // fp32 scale per (token, key head) with the s_tok / s_head strides
     const int8_t *k8, *v8;
@@ -77,13 +77,13 @@ inline size_t index_select_workspace_bytes(int64_t n_seqs, int H) {
     return (size_t)((n_seqs * H * 4 + 255) / 256 * 256);
 }
 
-// Decode partial: m[16], l[16], acc[16][128] (fp32) for one kept block.
+// Decode partial: m[16], l[16], acc[16][128] (fp32) for one workgroup's kept blocks.
 constexpr int kPartialFloats = 16 + 16 + 16 * 128;
 inline int decode_wg_per_unit(int top_k) { return (top_k + 3) / 4; }
 // Workspace: counters (one uint32 per unit, region rounded to 256 bytes), then partials.
 inline size_t decode_count_bytes(int64_t units) { return (size_t)((units * 4 + 255) / 256 * 256); }
 inline size_t decode_workspace_bytes(int64_t units, int top_k) {
-    return decode_count_bytes(units) + (size_t)units * top_k * kPartialFloats * sizeof(float);
+    return decode_count_bytes(units) + (size_t)units * decode_wg_per_unit(top_k) * kPartialFloats * sizeof(float);
 }
 
 // int8 cache writer: one bf16 [tokens, H, 128] tensor -> codes + scales.

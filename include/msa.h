@@ -245,9 +245,10 @@ size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
 /*
  * Step 4 for decode steps and verify windows: the same result as msa_prefill
  * (within rounding), computed as split-K over the kept keys.  Each kept block
- * (two 32-key pieces) is folded by its own wave into a partial (max, sum,
+ * (two 32-key pieces) is folded by its own wave; a workgroup's four waves
+ * (block slots 4w..4w+3) combine theirs in LDS into one partial (max, sum,
  * weighted values) in `workspace`; the last workgroup of a (row, key head) to
- * finish merges that row's partials, in block-slot order, with log-sum-exp
+ * finish merges that row's partials, in slot order, with log-sum-exp
  * weights.  The split depends only on top_k, never on the batch, so a row's
  * bits do not depend on the other rows: a verify window equals the same rows
  * decoded one at a time, bit for bit.

@@ -119,10 +119,13 @@ def test_pointer_stride_and_alignment_checks():
 def test_decode_workspace_size_and_checks():
     L = msa.lib()
     sh = msa.make_shape(4, top_k=16)
-    per_unit = 16 * (16 + 16 + 16 * 128) * 4      # top_k partials per (row, key head)
+    # one partial (max, sum, values of 16 heads x 128) per workgroup of four kept
+    # blocks, ceil(top_k / 4) per (row, key head)
+    per_unit = 4 * (16 + 16 + 16 * 128) * 4
     counters = lambda units: (units * 4 + 255) // 256 * 256
     assert msa.msa_decode_workspace_bytes(sh, 3) == counters(12) + 12 * per_unit
     assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 256 + 4 * 2080 * 4
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=5), 1) == 256 + 4 * 2 * 2080 * 4
     assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=40), 1) == 0
     b = FakeBatch(total_rows=4)
     need = msa.msa_decode_workspace_bytes(sh, 4)
