@@ -713,18 +713,27 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     if (a.lse && d0 == 0) a.lse[(int64_t)u.r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
+// Waves a prefill launch should have before it trades rows per wave for more
+// waves: two per SIMD of the 256 CUs.
+constexpr int64_t kPrefillFillWaves = 2048;
+
+template <int RW, bool KV8>
+static void launch_prefill_rw(const AttnArgs &a, hipStream_t st) {
+    const int gph = (a.b.total_rows + RW - 1) / RW;
+    const int64_t waves = (int64_t)gph * a.H;
+    hipLaunchKernelGGL((prefill_kernel<RW, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+}
+
 template <bool KV8>
 static void launch_prefill_t(const AttnArgs &a, hipStream_t st) {
-    // 4 rows per wave while their 4 * top_k entries fit the 64 lanes, else 2.
-    if (a.top_k <= 16) {
-        const int gph = (a.b.total_rows + 3) / 4;
-        const int64_t waves = (int64_t)gph * a.H;
-        hipLaunchKernelGGL((prefill_kernel<4, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
-    } else {
-        const int gph = (a.b.total_rows + 1) / 2;
-        const int64_t waves = (int64_t)gph * a.H;
-        hipLaunchKernelGGL((prefill_kernel<2, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
-    }
+    // 4 rows per wave while their 4 * top_k entries fit the 64 lanes, else 2;
+    // fewer while the grid would leave SIMDs idle (a short batch walks longer
+    // merged lists on fewer waves).  A row's result does not depend on it.
+    int rw = a.top_k <= 16 ? 4 : 2;
+    while (rw > 1 && (int64_t)((a.b.total_rows + rw - 1) / rw) * a.H < kPrefillFillWaves) rw /= 2;
+    if (rw == 4) launch_prefill_rw<4, KV8>(a, st);
+    else if (rw == 2) launch_prefill_rw<2, KV8>(a, st);
+    else launch_prefill_rw<1, KV8>(a, st);
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {

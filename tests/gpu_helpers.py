@@ -148,3 +148,17 @@ def _expand(case, rows, idx_rows, top_k):
         full[r, :, :k] = np.arange(int(nb[r]) - k, int(nb[r]), dtype=np.int32)
     full[np.asarray(rows)] = idx_rows
     return full
+
+
+def sample_rows(case, n_random=40, seed=5):
+    """Rows to compare for a large prefill case: the first and last rows of
+    each sequence, both sides of every 64-row block edge in the first 300 rows,
+    and a random sample."""
+    rows = set()
+    for s in range(case.n_seqs):
+        a, b = case.cu_rows[s], case.cu_rows[s + 1]
+        rows.update(range(a, min(a + 9, b)))
+        rows.update(range(max(a, b - 9), b))
+    rows.update(r for e in range(64, 300, 64) for r in (e - 1, e) if r < case.total_rows)
+    rows.update(np.random.default_rng(seed).choice(case.total_rows, n_random, replace=False).tolist())
+    return np.array(sorted(rows))

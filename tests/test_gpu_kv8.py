@@ -8,7 +8,7 @@ import torch
 
 import block_sparse_attention_04_amd as msa
 import oracle
-from gpu_helpers import check_lse, check_out, device_tensors, say, shape_of, _expand
+from gpu_helpers import check_lse, check_out, device_tensors, sample_rows, say, shape_of, _expand
 from workloads import make_case, to_pages
 
 pytestmark = pytest.mark.gpu
@@ -82,6 +82,23 @@ def test_kv8_attention_against_oracle(name, mode):
     m2 = check_out(o2.cpu(), fed_out, f"kv8/{name}/{mode}/fed")
     check_lse(l2.cpu(), fed_lse, f"kv8/{name}/{mode}/fed")
     say(f"[gpu] kv8 {name} {mode}: own {m1} fed {m2}")
+
+
+@pytest.mark.parametrize("name", ["walk4", "walk2_top32"])
+def test_kv8_prefill_rows_per_wave(name):
+    """The int8 prefill on batches large enough for 4 (or, at top_k = 32, 2)
+    rows per wave, against the oracle over the same int8 cache on sampled
+    rows (sequence starts and ends, block edges, random)."""
+    kw = {"walk4": dict(seq_lens=[2600, 700], rows=[2000, 100], n_kv_heads=4, seed=416),
+          "walk2_top32": dict(seq_lens=[2600, 2400], rows=[2000, 100], n_kv_heads=2, seed=417, top_k=32)}[name]
+    case = make_case(name, **kw)
+    kv8, (kc, vc, ks, vs) = kv8_of(case)
+    g = run(case, "prefill", kv8)
+    rows = sample_rows(case)
+    own_out, own_lse = oracle.attention_kv8(case, kc, vc, ks, vs, g["block_idx"].numpy()[rows], rows)
+    m = check_out(g["out"][rows], own_out, f"kv8/{name}/own-selection")
+    check_lse(g["lse"][rows], own_lse, f"kv8/{name}/own-selection")
+    say(f"[gpu] kv8 {name}: {m}")
 
 
 def test_kv8_prefill_and_decode_agree():

@@ -34,6 +34,8 @@ CASES = {
     # <= 16 rows: the streaming indexer, decode and the fused selection
     "window": (dict(seq_lens=[5000, 1, 64, 65, 3000], rows=[16, 1, 16, 7, 3], n_kv_heads=3, seed=302), "decode"),
     "shared_ik": (dict(seq_lens=[4000, 900], rows=[40, 8], n_kv_heads=4, seed=303, ik_shared=True), "prefill"),
+    # enough rows for the prefill to put four rows in each wave
+    "walk4": (dict(seq_lens=[2600, 700], rows=[2000, 100], n_kv_heads=4, seed=306), "prefill"),
 }
 
 

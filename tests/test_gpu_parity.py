@@ -7,7 +7,7 @@ import torch
 
 import block_sparse_attention_04_amd as msa
 import oracle
-from gpu_helpers import device_tensors, full_check, gpu_run, say, shape_of
+from gpu_helpers import device_tensors, full_check, gpu_run, sample_rows, say, shape_of
 from workloads import Case, config, make_case
 
 pytestmark = pytest.mark.gpu
@@ -224,11 +224,50 @@ def test_correlated_rows_share_blocks():
     """Rows whose indexer queries are AR(1)-correlated keep mostly the same
     blocks, so the four rows of a walk share many entries (the secondary
     workload): the merged walk must still give every row exactly its own
-    blocks' result."""
-    case = make_case("locality", [9000, 5000], [300, 77], 2, seed=131, locality=0.95)
-    ref_idx = oracle.run(case, np.arange(case.total_rows))["block_idx"]
-    shared = np.mean([len(set(ref_idx[r, 0]) & set(ref_idx[r + 1, 0])) for r in range(case.rows[0] - 1)])
+    blocks' result.  2,100 rows x 4 key heads: enough waves for four rows per
+    wave."""
+    case = make_case("locality", [9000, 5000], [2000, 100], 4, seed=131, locality=0.95)
+    ref_idx = oracle.run(case, np.arange(300))["block_idx"]
+    shared = np.mean([len(set(ref_idx[r, 0]) & set(ref_idx[r + 1, 0])) for r in range(299)])
     say(f"[gpu] locality: neighbouring rows share {shared:.1f} of 16 blocks")
     assert shared >= 8
-    full_check(case, "prefill")
-    full_check(case, "decode", rows=np.arange(0, case.total_rows, 7))
+    full_check(case, "prefill", rows=sample_rows(case))
+    full_check(case, "decode", rows=np.arange(0, case.total_rows, 37))
+
+
+# Prefill cases large enough for the launch to put 4 (or 2) rows in each wave;
+# smaller batches take one row per wave.
+WALK = {
+    "walk4": dict(seq_lens=[2600, 700], rows=[2000, 100], n_kv_heads=4, seed=150),
+    "walk2": dict(seq_lens=[2600, 700], rows=[2000, 100], n_kv_heads=2, seed=151),
+    "walk2_top32": dict(seq_lens=[2600, 2400], rows=[2000, 100], n_kv_heads=2, seed=152, top_k=32),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(WALK))
+def test_prefill_rows_per_wave(name):
+    """The merged multi-row walk (4 rows per wave, or 2 for top_k = 32 or on
+    fewer waves) against the oracle on rows at sequence starts and ends, block
+    edges and at random; and bit-identical to the one-row walk of the same rows
+    run as a batch too small to group rows."""
+    case = make_case(name, **WALK[name])
+    full_check(case, "prefill", rows=sample_rows(case))
+    # the same rows of sequence 1 on their own (100 rows: one row per wave)
+    t = device_tensors(case)
+    shape = shape_of(case)
+    big = msa.Batch(case.seq_lens, case.rows)
+    o_big = msa.run_path(shape, big, t, "prefill")
+    r1 = case.cu_rows[1]
+    n1 = case.rows[1]
+    L1 = case.seq_lens[1]
+    k0 = case.kv_start[1]
+    small = msa.Batch([L1], [n1])
+    sub = {"q": t["q"][r1:r1 + n1].contiguous(), "k": t["k"][k0:k0 + L1].contiguous(),
+           "v": t["v"][k0:k0 + L1].contiguous(), "iq": t["iq"][r1:r1 + n1].contiguous(),
+           "ik": t["ik"][k0:k0 + L1].contiguous()}
+    o_small = msa.run_path(shape, small, sub, "prefill")
+    torch.cuda.synchronize()
+    assert torch.equal(o_big["block_idx"][r1:r1 + n1], o_small["block_idx"])
+    assert torch.equal(o_big["out"][r1:r1 + n1], o_small["out"])
+    assert torch.equal(o_big["lse"][r1:r1 + n1], o_small["lse"])
