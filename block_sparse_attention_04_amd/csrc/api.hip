@@ -222,9 +222,6 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     if (need > msa::kMaxSelectBlocks)
         return fail(MSA_ERR_UNSUPPORTED, "max_seq_len=%d: selection supports at most %d blocks (%d keys)",
                     batch->max_seq_len, msa::kMaxSelectBlocks, msa::kMaxSelectBlocks * msa::kBlock);
-    if (batch->max_rows > 16)
-        return fail(MSA_ERR_UNSUPPORTED, "max_rows=%d: the fused path takes at most 16 rows per sequence "
-                    "(use msa_index_scores + msa_select_blocks)", batch->max_rows);
     const size_t ws_need = msa::index_select_workspace_bytes(batch->n_seqs, shape->n_kv_heads);
     if (!workspace || workspace_bytes < ws_need)
         return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws_need);
@@ -239,11 +236,26 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     a.ik_head = ik_head_stride;
     a.scores = block_scores;
     a.bs_stride = bs_stride;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (batch->max_rows > 1) {
+        // Several rows per sequence: the last workgroup would select them one
+        // after another, which costs more than a second launch that selects
+        // every (row, key head) in parallel.
+        if ((rc = launched(msa::launch_index_scores(a, st), "index_scores"))) return rc;
+        msa::SelectArgs s;
+        s.b = a.b;
+        s.H = a.H;
+        s.top_k = shape->top_k;
+        s.scores = block_scores;
+        s.bs_stride = bs_stride;
+        s.idx = block_idx;
+        return launched(msa::launch_select_blocks(s, st), "select_blocks");
+    }
     msa::SelectTail t{};
     t.top_k = shape->top_k;
     t.idx = block_idx;
     t.count = static_cast<unsigned *>(workspace);
-    return launched(msa::launch_index_select(a, t, static_cast<hipStream_t>(stream)), "index_select");
+    return launched(msa::launch_index_select(a, t, st), "index_select");
 }
 
 static int check_kv8(const msa_kv8 *kv, int n_kv_heads) {

@@ -378,27 +378,13 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         if (!is_last) return;
         if (threadIdx.x == 0)   // leave the counter at zero for the next call
             __hip_atomic_store(t.count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t.wave_mode) {
-            // one wave per row, rows wave, wave + 4, ...
-            uint32_t *keys = dyn + wave * t.cap;
-            for (int r = wave; r < rows_s; r += 4) {
-                const int row = row0 + r;
-                const int nb = (p_first + r) / kBlock + 1;
-                wave_lds_sync();   // the previous row's reads are done before restaging
-                stage_keys_coherent(keys, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, lane, kWave);
-                select_unit_wave(keys, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc.ck[wave],
-                                 sc.ci[wave]);
-            }
-        } else {
-            // the workgroup per row
-            for (int r = 0; r < rows_s; ++r) {
-                const int row = row0 + r;
-                const int nb = (p_first + r) / kBlock + 1;
-                __syncthreads();   // the previous row's reads are done before restaging
-                stage_keys_coherent(dyn, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, threadIdx.x,
-                                    256);
-                select_unit_wg(dyn, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc);
-            }
+        // the workgroup per row (the launcher sends one-row sequences here)
+        for (int r = 0; r < rows_s; ++r) {
+            const int row = row0 + r;
+            const int nb = (p_first + r) / kBlock + 1;
+            __syncthreads();   // the previous row's reads are done before restaging
+            stage_keys_coherent(dyn, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, threadIdx.x, 256);
+            select_unit_wg(dyn, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc);
         }
     }
 }
@@ -423,9 +409,7 @@ hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st)
     dim3 grid((a.bs_stride + per_wg - 1) / per_wg * a.H, 1, a.b.n_seqs);
     const int nb_max = (a.b.max_seq_len + kBlock - 1) / kBlock;
     t.cap = ((nb_max + 63) / 64) * 64;                      // staged keys per row
-    // one wave per row when a sequence has several rows and 4 stages fit 64 KiB
-    t.wave_mode = a.b.max_rows > 1 && t.cap * 16 <= 64 * 1024;
-    const size_t lds = (size_t)(t.wave_mode ? 4 : 1) * t.cap * sizeof(uint32_t);
+    const size_t lds = (size_t)t.cap * sizeof(uint32_t);
     hipLaunchKernelGGL(index_scores_window<true>, grid, dim3(256), lds, st, a, t);
     return hipGetLastError();
 }

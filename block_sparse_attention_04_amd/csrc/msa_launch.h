@@ -71,7 +71,6 @@ struct SelectTail {
     int32_t *idx;                // [total_rows, H, top_k]
     unsigned *count;             // one arrival counter per (sequence, key head); zero between calls
     int cap;                     // staged keys per row (set by the launcher)
-    int wave_mode;               // 1: one wave per row; 0: the workgroup per row (set by the launcher)
 };
 inline size_t index_select_workspace_bytes(int64_t n_seqs, int H) {
     return (size_t)((n_seqs * H * 4 + 255) / 256 * 256);

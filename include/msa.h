@@ -145,26 +145,30 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
                       int32_t *block_idx, void *stream);
 
 /*
- * Steps 1-3 fused, for decode steps and verify windows (at most 16 rows per
- * sequence): the index scores and max-pool of msa_index_scores, then the
- * selection of msa_select_blocks, in one launch.  The key axis of every
- * (sequence, key head) is spread over many workgroups; the last of them to
- * finish (an arrival counter in `workspace`) selects that sequence's rows, so
- * there is no second launch and the scores are read back while still in the
- * caches.  block_idx is bit-identical to msa_index_scores followed by
- * msa_select_blocks; block_scores is written as by msa_index_scores (it is
- * the exchange buffer).  The computation is the one of steps 1-3 (TensorFold
- * pull request 1388, commit adding the minimax_m3 family: index scores and a
- * top-16 block selection per row and key head); the pages keep the block
- * scores as a buffer of their own between the two steps (a later commit of the
- * same pull request shares its memory with other buffers).  Running both in
- * one launch is this library's addition, for decode latency.
+ * Steps 1-3 in one call, for decode steps and verify windows: the index
+ * scores and max-pool of msa_index_scores, then the selection of
+ * msa_select_blocks.  When every sequence has one row, both run in one
+ * launch: the key axis of every (sequence, key head) is spread over many
+ * workgroups and the last of them to finish (an arrival counter in
+ * `workspace`) selects the row, so there is no second launch and the scores
+ * are read back while still in the caches.  A batch with several rows in a
+ * sequence takes the two launches of msa_index_scores and msa_select_blocks
+ * (selecting the rows in parallel is faster than the last workgroup selecting
+ * them one by one).  Either way block_idx is bit-identical to
+ * msa_index_scores followed by msa_select_blocks, and block_scores is written
+ * as by msa_index_scores (it is the exchange buffer).  The computation is the
+ * one of steps 1-3 (TensorFold pull request 1388, commit adding the
+ * minimax_m3 family: index scores and a top-16 block selection per row and
+ * key head); the pages keep the block scores as a buffer of their own between
+ * the two steps (a later commit of the same pull request shares its memory
+ * with other buffers).  Running both in one launch is this library's
+ * addition, for decode latency.
  *   workspace   device, 256-byte aligned, msa_index_select_workspace_bytes()
  *               bytes: one arrival counter per (sequence, key head).  Must be
  *               zero before the first call; every call leaves it zero.  Calls
- *               that share a workspace must not overlap in time.
- * Errors: as msa_index_scores and msa_select_blocks; max_rows > 16 ->
- * MSA_ERR_UNSUPPORTED (use the two separate steps); a missing or short
+ *               that share a workspace must not overlap in time.  Required
+ *               (and checked) for every batch, used by one-row batches only.
+ * Errors: as msa_index_scores and msa_select_blocks; a missing or short
  * workspace -> MSA_ERR_WORKSPACE.
  */
 size_t msa_index_select_workspace_bytes(const msa_shape *shape, int32_t n_seqs);

@@ -1,7 +1,8 @@
 """GPU parity of msa_index_select (index scores, max-pool and selection in one
-launch, for decode steps and windows of at most 16 rows per sequence): its
-block_idx and block_scores must equal msa_index_scores + msa_select_blocks bit
-for bit, and the whole path through it must pass the same oracle checks."""
+call: one launch when every sequence has one row, else the two launches of
+msa_index_scores + msa_select_blocks): its block_idx and block_scores must
+equal msa_index_scores + msa_select_blocks bit for bit, and the whole path
+through it must pass the same oracle checks."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +21,12 @@ CASES = {
     "top5": dict(seq_lens=[3000, 1500], rows=[16, 3], n_kv_heads=2, seed=204, top_k=5),
     "top32": dict(seq_lens=[5000, 2100], rows=[16, 2], n_kv_heads=2, seed=205, top_k=32),
     "one_row": dict(seq_lens=[40000, 7000, 300], rows=[1, 1, 1], n_kv_heads=2, seed=206),
+    # one row per sequence (the one-launch path), ragged, with 1-, 64- and 65-key sequences
+    "one_row_ragged": dict(seq_lens=[5000, 1, 64, 65, 3000], rows=[1] * 5, n_kv_heads=3, seed=212),
+    "one_row_shared_ik": dict(seq_lens=[4000, 900], rows=[1, 1], n_kv_heads=4, seed=213, ik_shared=True),
+    "one_row_top1": dict(seq_lens=[1200, 800], rows=[1, 1], n_kv_heads=2, seed=214, top_k=1),
+    "one_row_top5": dict(seq_lens=[3000, 1500], rows=[1, 1], n_kv_heads=2, seed=215, top_k=5),
+    "one_row_top32": dict(seq_lens=[5000, 2100], rows=[1, 1], n_kv_heads=2, seed=216, top_k=32),
 }
 
 
@@ -57,7 +64,7 @@ def test_fused_full_configs(name):
 
 
 def test_fused_workspace_reuse_and_counters():
-    case = make_case("ws", [9000, 3000, 70], [5, 16, 2], 2, seed=207)
+    case = make_case("ws", [9000, 3000, 70], [1, 1, 1], 2, seed=207)
     shape = shape_of(case)
     batch = msa.Batch(case.seq_lens, case.rows)
     t = device_tensors(case)
@@ -73,16 +80,13 @@ def test_fused_workspace_reuse_and_counters():
     assert int(ws.view(torch.int32).abs().sum().item()) == 0
 
 
-def test_fused_rejects_prompt_chunks():
-    case = make_case("chunk", [3000], [17], 1, seed=208)
-    shape = shape_of(case)
-    batch = msa.Batch(case.seq_lens, case.rows)
-    t = device_tensors(case)
-    s = torch.empty(17, 1, batch.n_blocks, dtype=torch.float32, device="cuda")
-    i = torch.empty(17, 1, case.top_k, dtype=torch.int32, device="cuda")
-    with pytest.raises(msa.MsaError) as ei:
-        msa.msa_index_select(shape, batch, t["iq"], t["ik"], s, i)
-    assert ei.value.status == -2
+def test_prompt_chunks_take_two_launches():
+    """More than 16 rows in a sequence (a prompt chunk): the same results as
+    the two separate steps."""
+    case = make_case("chunk", [3000, 900], [300, 1], 2, seed=208)
+    a, b = _both(case)
+    assert torch.equal(a["block_scores"], b["block_scores"])
+    assert torch.equal(a["block_idx"], b["block_idx"])
 
 
 def test_max_context_one_row():
@@ -100,7 +104,7 @@ def test_fused_reused_buffers_see_new_scores():
     """The same block_scores / block_idx / workspace buffers across calls on
     different inputs: every call's selection must come from its own scores
     (the last workgroup reads what the others stored in this launch)."""
-    kw = dict(seq_lens=[40000, 9000, 2000], rows=[1, 16, 3], n_kv_heads=2)
+    kw = dict(seq_lens=[40000, 9000, 2000], rows=[1, 1, 1], n_kv_heads=2)
     cases = [make_case("reuseA", seed=210, **kw), make_case("reuseB", seed=211, **kw)]
     shape = shape_of(cases[0])
     batch = msa.Batch(cases[0].seq_lens, cases[0].rows)
