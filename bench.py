@@ -249,27 +249,62 @@ def _sclk():
     return None
 
 
-def cpu_baseline(cases, threads):
+def cpu_baseline(cases, threads, gpu=None):
     """Time the oracle as it stands on a bounded sample: 96 rows of the chunk
-    and the decode row; scale to rows/s of the full step."""
+    and the decode row; scale to rows/s of the full step.  With `gpu` (the
+    timed run's outputs on the host), the same oracle results also check them:
+    returns (baseline, validation)."""
     import numpy as np
     import oracle
     chunk, long_ = cases["chunk"], cases["long"]
     rng = np.random.default_rng(0)
     sample = np.sort(rng.choice(chunk.total_rows, 96, replace=False))
     t0 = time.perf_counter()
-    oracle.run(chunk, rows=sample, threads=threads)
+    ref_chunk = oracle.run(chunk, rows=sample, threads=threads)
     t_chunk_row = (time.perf_counter() - t0) / len(sample)
     t0 = time.perf_counter()
-    oracle.run(long_, threads=threads)
+    ref_long = oracle.run(long_, threads=threads)
     t_long = time.perf_counter() - t0
     step = t_chunk_row * chunk.total_rows + t_long
-    return {"value": (chunk.total_rows + long_.total_rows) / step, "unit": "rows/s", "cores": threads,
+    base = {"value": (chunk.total_rows + long_.total_rows) / step, "unit": "rows/s", "cores": threads,
             "kind": "oracle",
             "sample": f"96 random rows of the 4,096-row chunk ({t_chunk_row * 1e3:.1f} ms/row) and the "
                       f"262,144-key decode row ({t_long * 1e3:.0f} ms); step time extrapolated to "
                       f"4,096 + 1 rows = {step:.1f} s",
             "cpu": _cpu_model()}
+    if gpu is None:
+        return base, None
+    return base, validate(cases, {"chunk": (sample, ref_chunk), "long": (np.arange(long_.total_rows), ref_long)},
+                          gpu)
+
+
+# Tolerances of the parity tests: selection exact outside the near-tie band,
+# outputs within max-abs 2e-2 / mean-abs 2e-3, lse within 1e-3.
+GAP, MAX_ABS, MEAN_ABS, LSE_ABS = 1e-4, 2e-2, 2e-3, 1e-3
+
+
+def validate(cases, refs, gpu):
+    """The timed run's selection and outputs on the oracle's sample rows."""
+    import numpy as np
+    import oracle
+    out = {}
+    for name, (rows, ref) in refs.items():
+        g = gpu[name]
+        top_k = cases[name].top_k
+        gi = g["block_idx"][rows]
+        clear = oracle.selection_gap(ref["scores32"], ref["nb"], top_k) >= GAP
+        sel_ok = bool(((gi == ref["block_idx"]).all(axis=2) | ~clear).all())
+        rows_ok = clear.all(axis=1)
+        go = g["out"][rows][rows_ok].astype(np.float64)
+        d = np.abs(go - ref["out"][rows_ok]) if rows_ok.any() else np.zeros(1)
+        gl, rl = g["lse"][rows][rows_ok].astype(np.float64), ref["lse"][rows_ok]
+        dl = np.where(np.isneginf(gl) & np.isneginf(rl), 0.0, np.abs(gl - rl)) if rows_ok.any() else np.zeros(1)
+        ent = {"rows": int(len(rows)), "selection_exact": sel_ok, "near_tie_units": int((~clear).sum()),
+               "out_max_abs": float(d.max()), "out_mean_abs": float(d.mean()), "lse_max_abs": float(dl.max())}
+        ent["pass"] = bool(sel_ok and ent["out_max_abs"] <= MAX_ABS and ent["out_mean_abs"] <= MEAN_ABS
+                           and ent["lse_max_abs"] <= LSE_ABS)
+        out[name] = ent
+    return out
 
 
 def _cpu_model():
@@ -477,8 +512,17 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
+        # the timed run's outputs (every input replica holds the same values)
+        gpu = {}
+        for name in cases:
+            o = state[name][3]
+            gpu[name] = {"block_idx": o["block_idx"].cpu().numpy(), "out": o["out"].float().cpu().numpy(),
+                         "lse": o["lse"].cpu().numpy()}
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cases, args.cpu_threads)
+        base, val = cpu_baseline(cases, args.cpu_threads, None if args.kv8 else gpu)
+        res["cpu_baseline"] = base
+        if val is not None:
+            res["validation"] = val
     print(json.dumps(res))
 
 
