@@ -489,6 +489,10 @@ def main():
                    "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16",
                    "index_queries": ("i.i.d. N(0,1) per row" if args.locality is None else
                                      f"secondary workload: AR(1) across the chunk's rows, a = {args.locality}")},
+        "inputs": {"generator": "torch.Generator (CPU) seeded per workload, randn in fp32 rounded to bf16",
+                   "torch": torch.__version__,
+                   "seeds": {n: c.seed for n, c in cases.items()},
+                   "sha256": {n: c.digests() for n, c in cases.items()}},
         "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
         "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
         "roofline": roofline,
