@@ -376,8 +376,10 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 // kept block is read once for all of them) and an online-softmax state.  The
 // rows' kept blocks are merged into one list sorted by block index and walked
 // 32 keys at a time, the next chunk's K/V loads in flight while the current
-// one is folded into its row's state.  Each row still sees its own blocks in
-// ascending order, so its bits depend only on its blocks.  Walking the merged
+// one is folded.  A block kept by several of the rows (their shared local
+// block, or any block on correlated rows) is loaded once and folded into each
+// of them.  Each row still sees its own blocks in ascending order, so its bits
+// depend only on its blocks.  Walking the merged
 // list keeps every resident wave of a key head near the same key position at
 // the same time, so rows that keep the same block read it while it is still
 // in L2: with independent per-row walks, two rows reach a shared block at
@@ -426,29 +428,46 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     const int e_lo = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)tok_l);
     const int e_hi = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)((uint64_t)tok_l >> 32));
     const int n_ent = (int)__popcll(__ballot(key != kInvalidKey));
+    // Entries that read the same K/V (same first token: one block of one
+    // sequence, or a page shared by sequences) are adjacent after the sort and
+    // form a group; bit k of `starts` marks the entry that opens a group.
+    const int prev_lo = __shfl_up(e_lo, 1), prev_hi = __shfl_up(e_hi, 1);
+    const uint64_t starts = __ballot(lane < n_ent && (lane == 0 || prev_lo != e_lo || prev_hi != e_hi));
+    auto group_end = [&](int k) -> int {       // one past the last entry of the group opened by k
+        const uint64_t rest = k + 1 < kWave ? starts >> (k + 1) : 0ull;
+        return rest ? k + 1 + __builtin_ctzll(rest) : n_ent;
+    };
 
-    // A chunk of the walk: entry k (wave-uniform values), half hh of its block.
+    // A chunk of the walk: half hh of the block of the group opened by entry
+    // k (wave-uniform values); p_max: the largest position among its rows.
     struct Chunk {
-        int kb, row, p;
+        int kb, k, end, p_max;
         int64_t tok;      // token of the chunk's first key
     };
     auto chunk_at = [&](int k, int hh) -> Chunk {
         Chunk c;
-        const int e = __builtin_amdgcn_readlane(e_key, k);
-        c.row = e & 3;
-        c.kb = (e >> 2) * kBlock + 32 * hh;
-        c.p = __builtin_amdgcn_readlane(e_p, k);
+        c.k = k;
+        c.end = group_end(k);
+        c.kb = (__builtin_amdgcn_readlane(e_key, k) >> 2) * kBlock + 32 * hh;
         c.tok = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
                           (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) + 32 * hh;
+        int pm = __builtin_amdgcn_readlane(e_p, k);
+        for (int j = k + 1; j < c.end; ++j) pm = max(pm, __builtin_amdgcn_readlane(e_p, j));
+        c.p_max = pm;
         return c;
     };
     int k = 0, half = 0;
-    auto next_chunk = [&](Chunk &c) -> bool {   // advances (k, half) to the next visible chunk
+    auto next_chunk = [&](Chunk &c) -> bool {   // advances (k, half) to the next chunk some row sees
         for (;;) {
-            half ^= 1;
-            if (half == 0 && ++k >= n_ent) return false;
+            if (half == 0) {
+                half = 1;
+            } else {
+                half = 0;
+                k = group_end(k);
+                if (k >= n_ent) return false;
+            }
             c = chunk_at(k, half);
-            if (c.kb <= c.p) return true;
+            if (c.kb <= c.p_max) return true;
         }
     };
     using Regs = typename std::conditional<KV8, ChunkRegs8, ChunkRegs>::type;
@@ -456,24 +475,30 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
         if constexpr (KV8) {
             const int64_t soff = c.tok * a.s_tok + (int64_t)g * a.s_head;
-            load_chunk8(r, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, c.p - c.kb);
+            load_chunk8(r, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, c.p_max - c.kb);
         } else {
-            load_chunk(r, a.k + off, a.v + off, a.kv_tok, 0, c.p - c.kb);
+            load_chunk(r, a.k + off, a.v + off, a.kv_tok, 0, c.p_max - c.kb);
         }
     };
+    // Fold one loaded chunk into every row of its group that sees it (keys
+    // past a row's own position are masked in its fold).
     auto fold = [&](const Regs &r, const Chunk &c) {
-        u32x4 qb[4];
-        read_q<KV8>(qb, qt + c.row * kQTileBytes);
+        u32x4 ka8[2][4];
         if constexpr (KV8) {
             stage_v8(r, vt, sct);
-            wave_lds_sync();
-            u32x4 ka[2][4];
-            k_operands8(r, ka);
-            fold_rows<RW, true>(st, c.row, qb, ka, c.kb, c.p, a.scale_log2, vt, sct);
+            k_operands8(r, ka8);
         } else {
             stage_v(r, vt);
-            wave_lds_sync();
-            fold_rows<RW, false>(st, c.row, qb, r.ka, c.kb, c.p, a.scale_log2, vt, nullptr);
+        }
+        wave_lds_sync();
+        for (int j = c.k; j < c.end; ++j) {
+            const int row = __builtin_amdgcn_readlane(e_key, j) & 3;
+            const int p = __builtin_amdgcn_readlane(e_p, j);
+            if (c.kb > p) continue;
+            u32x4 qb[4];
+            read_q<KV8>(qb, qt + row * kQTileBytes);
+            if constexpr (KV8) fold_rows<RW, true>(st, row, qb, ka8, c.kb, p, a.scale_log2, vt, sct);
+            else fold_rows<RW, false>(st, row, qb, r.ka, c.kb, p, a.scale_log2, vt, nullptr);
         }
         wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
     };
