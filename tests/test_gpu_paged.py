@@ -93,3 +93,31 @@ def test_shared_prefix_pages_and_chunk_resume():
     paged = run(case, t, msa.Batch(case.seq_lens, case.rows, page_table=pt), "prefill")
     for n in ("block_scores", "block_idx", "out", "lse"):
         assert torch.equal(dense[n], paged[n]), n
+
+
+def test_shared_pages_across_sequences_in_one_walk():
+    """Two 1,050-row chunks resumed on one shared 2,048-key prefix, with enough
+    rows (x 4 key heads) for four rows per prefill wave: the wave holding rows
+    1,048-1,051 mixes the two sequences, and a prefix page both kept is one
+    group of the walk (loaded once, folded into rows of both sequences).
+    Equal to the contiguous layout with the prefix duplicated."""
+    P, n = 2048, 1050
+    case = make_case("xprefix", [P + n, P + n], [n, n], 4, seed=306)
+    s1 = case.kv_start[1]
+    for name in ("k", "v", "ik"):
+        getattr(case, name)[s1:s1 + P] = getattr(case, name)[:P]
+    dense = run(case, device_tensors(case), msa.Batch(case.seq_lens, case.rows), "prefill")
+    pool, pt = page_pool(case, seed=306, shared=(0, 1, P // B))
+    t = dict(device_tensors(case), **pool)
+    paged = run(case, t, msa.Batch(case.seq_lens, case.rows, page_table=pt), "prefill")
+    for name in ("block_scores", "block_idx", "out", "lse"):
+        assert torch.equal(dense[name], paged[name]), name
+    # the boundary wave's rows of the two sequences keep common prefix pages
+    idx = paged["block_idx"].numpy()
+    common = 0
+    for h in range(case.n_kv_heads):
+        a = {int(pt[0, b]) for r in (n - 2, n - 1) for b in idx[r, h] if 0 <= b < P // B}
+        c = {int(pt[1, b]) for r in (n, n + 1) for b in idx[r, h] if 0 <= b < P // B}
+        common += len(a & c)
+    say(f"[gpu] prefix pages kept by both sequences in the boundary wave: {common}")
+    assert common > 0
