@@ -30,17 +30,18 @@ __device__ __forceinline__ int wave_sum_int(int x) {
     return x;
 }
 
-// Largest T with #{lanes: v >= T} >= k (the k-th largest of 64 values),
-// two bits per step: three independent ballots decide bits (b+1, b).
+// Largest T with #{lanes: v >= T} >= k (the k-th largest of 64 values), one
+// bit per step (one ballot each: fewer vector instructions than wider steps).
+// With kLowBit > 0 only bits 31..kLowBit are decided: the result is the k-th
+// largest of the values with their low kLowBit bits cleared -- a lower bound
+// on the exact one, in fewer steps.
+template <int kLowBit = 0>
 __device__ __forceinline__ uint32_t kth_largest_wave(uint32_t v, int k) {
     uint32_t t = 0u;
 #pragma unroll
-    for (int shift = 30; shift >= 0; shift -= 2) {
-        const uint32_t c1 = t | (1u << shift), c2 = t | (2u << shift), c3 = t | (3u << shift);
-        const int n3 = __popcll(__ballot(v >= c3));
-        const int n2 = __popcll(__ballot(v >= c2));
-        const int n1 = __popcll(__ballot(v >= c1));
-        t = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : t;
+    for (int bit = 31; bit >= kLowBit; --bit) {
+        const uint32_t c = t | (1u << bit);
+        t = __popcll(__ballot(v >= c)) >= k ? c : t;
     }
     return t;
 }
@@ -67,7 +68,9 @@ __device__ __forceinline__ void wave_top(const uint32_t *keys, int n, int need, 
     uint32_t lmax = 0u;
 #pragma unroll 8
     for (int j = lane; j < n; j += kWave) lmax = max(lmax, keys[j]);
-    const uint32_t t0 = kth_largest_wave(lmax, need);
+    // T0: a lower bound on T (need lanes hold a key >= it), decided on the
+    // top 16 bits only; keys in T0's 2^16-wide bucket just add candidates.
+    const uint32_t t0 = kth_largest_wave<16>(lmax, need);
 
     int c = 0;
     for (int j0 = 0; j0 < n; j0 += kWave) {

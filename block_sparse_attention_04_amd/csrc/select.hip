@@ -12,8 +12,9 @@
 // One wave per (row, key head).  Scores become order-preserving 32-bit keys
 // (so every comparison is exact integer work); the (top_k-1)-th largest key T
 // is found with ballot counts:
-//   1. T0 = the (top_k-1)-th largest of the 64 per-lane maxima -- a lower
-//      bound on T, since top_k-1 lanes hold a value >= T0;
+//   1. T0 = the (top_k-1)-th largest of the 64 per-lane maxima, decided on
+//      their top 16 bits -- a lower bound on T, since top_k-1 lanes hold a
+//      value >= T0;
 //   2. the candidates >= T0 (usually a few dozen) are compacted into LDS and
 //      T is found among them by a 32-step bitwise search over one key per
 //      lane; if more than 64 candidates tie above T0, the same search runs
