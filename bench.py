@@ -150,46 +150,61 @@ class Timed:
         return out
 
 
-def other_configs(torch, msa, dev, steps=20):
+# The other named workloads: (name, mode, input replicas rotated so the 256 MB
+# Infinity Cache cannot hold a call's working set across calls, timed passes).
+OTHER_CONFIGS = (("tiny", "prefill", 1, 50), ("decode", "decode", 8, 200), ("windows", "decode", 3, 200))
+
+
+def other_configs(torch, msa, dev):
     """The other named workloads, for reference beside the headline line (not
     part of `value`): the 2,048-token prefill, the batched decode of 4 x 32,768
     keys and the four 16-row verify windows, each timed per library call with
-    HIP events (mean over `steps` passes after two warm-up passes)."""
+    HIP events (mean and p10 / median / p90 over the timed passes, after two
+    warm-up passes per replica)."""
     from workloads import config
     out = {}
-    for name, mode in (("tiny", "prefill"), ("decode", "decode"), ("windows", "decode")):
+    for name, mode, n_rep, steps in OTHER_CONFIGS:
         case = config(name)
-        t = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
+        reps = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(n_rep - 1)]
         shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
         batch = msa.Batch(case.seq_lens, case.rows, device=dev)
         fused = mode == "decode"
-        o = msa.run_path(shape, batch, t, mode, fused=fused)
-        if fused:
-            calls = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
+        o = msa.run_path(shape, batch, base, mode, fused=fused)
+
+        def calls(t):
+            if fused:
+                c = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
                                                                    o["block_idx"], o["select_workspace"]))]
-        else:
-            calls = [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])),
-                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"]))]
-        if mode == "prefill":
-            calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
+            else:
+                c = [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
+                                                                   o["block_scores"])),
+                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
+                                                                     o["block_idx"]))]
+            if mode == "prefill":
+                c.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
                                                                o["out"], o["lse"])))
-        else:
-            calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
+            else:
+                c.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
                                                               o["out"], o["lse"], o["workspace"])))
+            return c
+
         timer = Timed(torch)
-        for i in range(steps + 2):
-            for kname, fn in calls:
-                if i < 2:
+        warm = 2 * n_rep
+        for i in range(steps + warm):
+            for kname, fn in calls(reps[i % n_rep]):
+                if i < warm:
                     fn()
                 else:
                     timer.run(kname, fn)
         torch.cuda.synchronize()
-        kms = timer.mean_ms()
+        kms, kq = timer.mean_ms(), timer.quantiles_ms()
         work = algorithmic_work(case)
         total = sum(kms.values())
         ent = {"mode": mode, "rows": case.total_rows, "seq_lens": case.seq_lens, "kv_heads": case.n_kv_heads,
-               "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
-               "kernels": {k: {"ms": v} for k, v in kms.items()}}
+               "replicas": n_rep, "steps": steps, "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
+               "kernels": {k: {"ms": v, "ms_p10": kq[k][0], "ms_median": kq[k][1], "ms_p90": kq[k][2]}
+                           for k, v in kms.items()}}
         for k, v in kms.items():
             wk = work[k]
             if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
@@ -199,7 +214,7 @@ def other_configs(torch, msa, dev, steps=20):
                 ent["kernels"][k].update(gbs=wk["bytes"] / (v * 1e-3) / 1e9,
                                          frac=wk["bytes"] / (v * 1e-3) / 1e9 / PEAK_HBM_GBS)
         out[name] = ent
-        del t, o
+        del base, reps, o
     return out
 
 
@@ -320,7 +335,7 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed steps for at least this much wall time before the warm-up steps, so the "
