@@ -155,12 +155,13 @@ class Timed:
 OTHER_CONFIGS = (("tiny", "prefill", 1, 50), ("decode", "decode", 8, 200), ("windows", "decode", 3, 200))
 
 
-def other_configs(torch, msa, dev):
+def other_configs(torch, msa, dev, keep=None):
     """The other named workloads, for reference beside the headline line (not
     part of `value`): the 2,048-token prefill, the batched decode of 4 x 32,768
     keys and the four 16-row verify windows, each timed per library call with
     HIP events (mean and p10 / median / p90 over the timed passes, after two
-    warm-up passes per replica)."""
+    warm-up passes per replica).  keep: a dict that receives each workload's
+    case and host copies of its outputs, for the oracle leg."""
     from workloads import config
     out = {}
     for name, mode, n_rep, steps in OTHER_CONFIGS:
@@ -214,7 +215,36 @@ def other_configs(torch, msa, dev):
                 ent["kernels"][k].update(gbs=wk["bytes"] / (v * 1e-3) / 1e9,
                                          frac=wk["bytes"] / (v * 1e-3) / 1e9 / PEAK_HBM_GBS)
         out[name] = ent
+        if keep is not None:
+            keep[name] = (case, {"block_idx": o["block_idx"].cpu().numpy(), "out": o["out"].float().cpu().numpy(),
+                                 "lse": o["lse"].cpu().numpy()})
         del base, reps, o
+    return out
+
+
+# Oracle sample per other workload: rows timed and checked (all rows of the
+# small decode batches, a spread of rows elsewhere).
+OTHER_SAMPLES = {"tiny": 64, "decode": None, "windows": 16}
+
+
+def other_cpu_baselines(kept, threads):
+    """The oracle on a sample of each other workload: its rows/s on the host
+    cores (scaled to the whole workload) and the same check of the GPU outputs
+    as the headline validation."""
+    import numpy as np
+    import oracle
+    out = {}
+    for name, (case, gpu) in kept.items():
+        n = OTHER_SAMPLES.get(name)
+        rows = (np.arange(case.total_rows) if n is None or n >= case.total_rows
+                else np.unique(np.linspace(0, case.total_rows - 1, n).round().astype(np.int64)))
+        t0 = time.perf_counter()
+        ref = oracle.run(case, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        per_row = dt / len(rows)
+        out[name] = {"cpu_baseline": {"value": 1.0 / per_row, "unit": "rows/s", "cores": threads, "kind": "oracle",
+                                      "sample": f"{len(rows)} of {case.total_rows} rows ({dt:.2f} s)"},
+                     "validation": validate({name: case}, {name: (rows, ref)}, {name: gpu})[name]}
     return out
 
 
@@ -529,7 +559,8 @@ def main():
         "kernels": kernels,
     }
     if not args.no_others:
-        res["other_configs"] = other_configs(torch, msa, dev)
+        kept = {} if not args.no_cpu_baseline else None
+        res["other_configs"] = other_configs(torch, msa, dev, keep=kept)
     if not args.no_peaks:
         peaks = measured_peaks(torch, msa, dev)
         res["measured_peaks"] = peaks
@@ -557,6 +588,9 @@ def main():
         res["cpu_baseline"] = base
         if val is not None:
             res["validation"] = val
+        if not args.no_others:
+            for name, ent in other_cpu_baselines(kept, args.cpu_threads).items():
+                res["other_configs"][name].update(ent)
     print(json.dumps(res))
 
 
