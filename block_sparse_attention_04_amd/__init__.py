@@ -331,7 +331,7 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
              stream=None, fused: bool = False, kv8: KV8 | None = None) -> dict:
     """Enqueue the whole path -- index scores, selection, attention -- on
     device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
-    fused: steps 1-3 through msa_index_select (at most 16 rows per sequence).
+    fused: steps 1-3 through msa_index_select.
     kv8: attend over this int8 cache instead of t["k"], t["v"].
     Output buffers are allocated unless given in `out`."""
     out = {} if out is None else out

@@ -562,21 +562,122 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per
     prefill_group<RW, KV8>(a, g, r0, vt_all[wave], qt_all[wave], sc_all[wave]);
 }
 
-// Decode: the kept list of a (row, key head) is split into top_k partials of
-// one block (two 32-key chunks) each; wave `slot` folds partial `slot`, with
-// both chunks' loads in flight together, and writes (max, sum, weighted
-// values) to the workspace.  Workgroups of 4 waves take 4 consecutive slots;
-// the last workgroup of a unit to finish (a per-unit counter) merges all its
-// partials, in slot order, with log-sum-exp weights.  The partials and their
-// merge order depend only on top_k, so a row's bits never depend on the rest
-// of the batch or on which workgroup finished last.
+// Decode.  The kept list of a (row, key head) is folded one block (two 32-key
+// chunks, both in flight together) per state; the states of 4 consecutive
+// slots combine into a partial (max, sum, weighted values), and the partials
+// merge in slot order with log-sum-exp weights.  That tree depends only on
+// top_k, and both decode kernels below compute it with the same helpers, in
+// the same order: a row's bits never depend on the rest of the batch, on the
+// kernel the launch picks, or on which workgroup finished last.
+
+// One kept block (index b_raw) of unit u folded into st.
+template <bool KV8>
+__device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit &u, int64_t kv0,
+                                                  const u32x4 (&qb)[4], int b_raw, Softmax &st, uint8_t *vt,
+                                                  float *sct) {
+    const int b = u.ok ? b_raw : -1;
+    const int kb0 = b * kBlock, kb1 = kb0 + 32;
+    if (b < 0 || kb0 > u.p) return;
+    const int64_t t0 = block_token0(a.b, u.s, kv0, b);     // the block's first key
+    const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+    if constexpr (KV8) {
+        const int64_t soff = t0 * a.s_tok + (int64_t)u.g * a.s_head;
+        const int64_t off1 = off + 32 * a.kv_tok, soff1 = soff + 32 * a.s_tok;
+        ChunkRegs8 ca, cb;
+        load_chunk8(ca, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, u.p - kb0);
+        if (kb1 <= u.p)
+            load_chunk8(cb, a.k8 + off1, a.v8 + off1, a.ks + soff1, a.vs + soff1, a.kv_tok, a.s_tok, u.p - kb1);
+        fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt, sct);
+        if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt, sct);
+    } else {
+        const uint16_t *kblk = a.k + off, *vblk = a.v + off;
+        ChunkRegs ca, cb;
+        load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
+        if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
+        fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt, nullptr);
+        if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt, nullptr);
+    }
+}
+
+// A wave's state to LDS: max and sum per head to wm/wl, the 16 x 128
+// unnormalised values to the wave's V tile (free once its folds are done).
+__device__ __forceinline__ void decode_stash(const Softmax &st, float *wm, float *wl, uint8_t *vt) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    const float l = sum_over_lane_groups(st.l);
+    if (lg == 0) {
+        wm[lr] = st.m;
+        wl[lr] = l;
+    }
+    float *wo = reinterpret_cast<float *>(vt);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(wo + lr * kHeadDim + 16 * dt + 4 * lg) = st.o[dt];
+}
+
+// The partial of the 4 stashed states w0..w0+3 (slot order) for head h, dims
+// d0..d0+N-1.  Empty states (no visible key, or no slot) have max -inf and
+// weight 0.
+template <int N>
+__device__ __forceinline__ void combine_group(const float (*wm)[16], const float (*wl)[16],
+                                              const uint8_t (*vt)[8192], int w0, int h, int d0, float &M,
+                                              float &Ls, float (&acc)[N]) {
+    M = fmaxf(fmaxf(wm[w0][h], wm[w0 + 1][h]), fmaxf(wm[w0 + 2][h], wm[w0 + 3][h]));
+    Ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    if (M == -INFINITY) return;
+#pragma unroll
+    for (int w = w0; w < w0 + 4; ++w) {
+        const float mw = wm[w][h];
+        if (mw == -INFINITY) continue;
+        const float wgt = exp2f(mw - M);
+        Ls += wgt * wl[w][h];
+        const float *src = reinterpret_cast<const float *>(vt[w]) + h * kHeadDim + d0;
+#pragma unroll
+        for (int i0 = 0; i0 < N; i0 += 4) {
+            const floatx4 x = *reinterpret_cast<const floatx4 *>(src + i0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i0 + i] += wgt * x[i];
+        }
+    }
+}
+
+// One partial (max mp > -inf, sum lp, values xp) merged into (Ls, acc) under
+// the overall max M.
+template <int N>
+__device__ __forceinline__ void merge_partial(float M, float mp, float lp, const float (&xp)[N], float &Ls,
+                                              float (&acc)[N]) {
+    const float wgt = exp2f(mp - M);
+    Ls += wgt * lp;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] += wgt * xp[i];
+}
+
+// Normalise and store head h, dims d0..d0+N-1 of unit u, and its lse.
+template <int N>
+__device__ __forceinline__ void decode_write(const AttnArgs &a, const Unit &u, int h, int d0, float M, float Ls,
+                                             const float (&acc)[N]) {
+    const int hq = a.H * kGroup, hh = u.g * kGroup + h;
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    uint16_t *dst = a.out + ((int64_t)u.r * hq + hh) * kHeadDim + d0;
+    if constexpr (N == 8) *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    else *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+    if (a.lse && d0 == 0) a.lse[(int64_t)u.r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+// Split-K decode, for launches with few units: workgroup `split` of a unit
+// folds slots 4*split .. +3 (one per wave) and combines them into partial
+// `split`; with several partials each workgroup publishes its partial and the
+// last to arrive (a per-unit counter) merges them.
 template <bool KV8>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
     __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
+    __shared__ float wm[4][16], wl[4][16];
     __shared__ int is_last;
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int lg = lane >> 4, lr = lane & 15;
     const int64_t unit = blockIdx.x / wg_per_unit;
     const int split = blockIdx.x % wg_per_unit;
     if (unit >= (int64_t)a.b.total_rows * a.H) return;
@@ -584,11 +685,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     const int hq = a.H * kGroup;
     float *part_unit = a.ws_part + unit * wg_per_unit * (int64_t)kPartialFloats;
     const int slot = split * 4 + wave;
-    // Each wave's partial (max, sum, unnormalised values) goes to LDS: m and l
-    // to wm/wl, the 16 x 128 values to the wave's V staging area, free once
-    // its folds are done.
-    __shared__ float wm[4][16], wl[4][16];
-    float *wo = reinterpret_cast<float *>(vt_all[wave]);
     if (slot < a.top_k) {
         Softmax st;
         softmax_init(st);
@@ -598,66 +694,18 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         const int64_t kv0 = seq_token0(a.b, u.s);
         u32x4 qb[4];
         load_q<KV8>(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
-        const int b = u.ok ? b_raw : -1;
-        const int kb0 = b * kBlock, kb1 = kb0 + 32;
-        if (b >= 0 && kb0 <= u.p) {
-            const int64_t t0 = block_token0(a.b, u.s, kv0, b);     // the block's first key
-            const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
-            if constexpr (KV8) {
-                const int64_t soff = t0 * a.s_tok + (int64_t)u.g * a.s_head;
-                const int64_t off1 = off + 32 * a.kv_tok, soff1 = soff + 32 * a.s_tok;
-                ChunkRegs8 ca, cb;
-                load_chunk8(ca, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, u.p - kb0);
-                if (kb1 <= u.p)
-                    load_chunk8(cb, a.k8 + off1, a.v8 + off1, a.ks + soff1, a.vs + soff1, a.kv_tok, a.s_tok,
-                                u.p - kb1);
-                fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave], sc_all[wave]);
-                if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave], sc_all[wave]);
-            } else {
-                const uint16_t *kblk = a.k + off, *vblk = a.v + off;
-                ChunkRegs ca, cb;
-                load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
-                if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
-                fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt_all[wave], nullptr);
-                if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt_all[wave], nullptr);
-            }
-        }
-        const float l = sum_over_lane_groups(st.l);
-        if (lg == 0) {
-            wm[wave][lr] = st.m;
-            wl[wave][lr] = l;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(wo + lr * kHeadDim + 16 * dt + 4 * lg) = st.o[dt];
+        decode_fold_block<KV8>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
+        decode_stash(st, wm[wave], wl[wave], vt_all[wave]);
     } else if (lane < 16) {
         wm[wave][lane] = -INFINITY;
         wl[wave][lane] = 0.f;
     }
     __syncthreads();
 
-    // Thread = (head h, dims d0..d0+7).  Combine the workgroup's four waves in
-    // slot order into one partial.
+    // thread = (head h, dims d0..d0+7)
     const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-    float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
-    float Ls = 0.f;
-    float accv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = wm[w][h];
-            if (mw == -INFINITY) continue;   // an empty partial (no visible key, or no slot)
-            const float wgt = exp2f(mw - M);
-            Ls += wgt * wl[w][h];
-            const float *src = reinterpret_cast<const float *>(vt_all[w]) + h * kHeadDim + d0;
-            const floatx4 x0 = *reinterpret_cast<const floatx4 *>(src);
-            const floatx4 x1 = *reinterpret_cast<const floatx4 *>(src + 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                accv[i] += wgt * x0[i];
-                accv[4 + i] += wgt * x1[i];
-            }
-        }
-    }
+    float M, Ls, accv[8];
+    combine_group<8>(wm, wl, vt_all, 0, h, d0, M, Ls, accv);
 
     if (wg_per_unit > 1) {
         // Publish the workgroup's partial with device-scoped stores (written
@@ -716,26 +764,76 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
                                                      __HIP_MEMORY_SCOPE_AGENT);
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const bool use = w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY;
-                    if (!use) continue;
-                    const float wgt = exp2f(ms[w0 + q] - M);
-                    Ls += wgt * lv[q];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) accv[i] += wgt * xv[q][i];
-                }
+                for (int q = 0; q < 4; ++q)
+                    if (w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY)
+                        merge_partial<8>(M, ms[w0 + q], lv[q], xv[q], Ls, accv);
             }
         }
     } else if (!u.ok) {
         return;
     }
-    const int hh = u.g * kGroup + h;
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    u32x4 wv;
+    decode_write<8>(a, u, h, d0, M, Ls, accv);
+}
+
+// Decode with one workgroup per unit, for launches with many units: 8 waves
+// fold 8 slots at a time (pass p: slots 8p + wave), each into a state of its
+// own; after each pass the workgroup forms that pass's two partials, kept in
+// registers, and merges all partials at the end.  Nothing leaves the CU until
+// the output, and the arithmetic is decode_kernel's, step for step.
+template <bool KV8>
+__global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
+    constexpr int kW = 8;
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[kW][8192];
+    __shared__ __attribute__((aligned(16))) float sc_all[kW][KV8 ? 64 : 4];
+    __shared__ float wm[kW][16], wl[kW][16];
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int64_t unit = blockIdx.x;
+    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+    const Unit u = make_unit(a, unit);
+    const int hq = a.H * kGroup;
+    const int64_t kv0 = seq_token0(a.b, u.s);
+    u32x4 qb[4];
+    load_q<KV8>(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
+    const int n_part = (a.top_k + 3) / 4;   // partials of 4 slots
+    // thread = (head h, dims d0..d0+3)
+    const int h = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
+    float pm[kMaxTopK / 4], pl[kMaxTopK / 4], px[kMaxTopK / 4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = pack_bf16x2(accv[2 * i] * inv, accv[2 * i + 1] * inv);
-    *reinterpret_cast<u32x4 *>(a.out + ((int64_t)u.r * hq + hh) * kHeadDim + d0) = wv;
-    if (a.lse && d0 == 0) a.lse[(int64_t)u.r * hq + hh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    for (int pass = 0; pass < kMaxTopK / kW; ++pass) {
+        if (pass * kW >= a.top_k) break;
+        if (pass > 0) __syncthreads();   // the previous pass's partials have read the tiles
+        const int slot = pass * kW + wave;
+        if (slot < a.top_k) {
+            Softmax st;
+            softmax_init(st);
+            const int b_raw = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
+            decode_fold_block<KV8>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
+            decode_stash(st, wm[wave], wl[wave], vt_all[wave]);
+        } else if (lane < 16) {
+            wm[wave][lane] = -INFINITY;
+            wl[wave][lane] = 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kW / 4; ++j)
+            if (pass * (kW / 4) + j < n_part)
+                combine_group<4>(wm, wl, vt_all, 4 * j, h, d0, pm[pass * (kW / 4) + j], pl[pass * (kW / 4) + j],
+                                 px[pass * (kW / 4) + j]);
+    }
+    if (!u.ok) return;
+    if (n_part == 1) {
+        decode_write<4>(a, u, h, d0, pm[0], pl[0], px[0]);
+        return;
+    }
+    float M = -INFINITY, Ls = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kMaxTopK / 4; ++w) M = fmaxf(M, w < n_part ? pm[w] : -INFINITY);
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kMaxTopK / 4; ++w)
+            if (w < n_part && pm[w] != -INFINITY) merge_partial<4>(M, pm[w], pl[w], px[w], Ls, acc);
+    }
+    decode_write<4>(a, u, h, d0, M, Ls, acc);
 }
 
 // Waves a prefill launch should have before it trades rows per wave for more
@@ -767,8 +865,21 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Units from which a decode launch takes one workgroup per unit: below, the
+// split over several workgroups per unit spreads a small batch over more CUs;
+// above, the one-workgroup kernel avoids publishing and re-reading partials
+// (measured at top_k 16: split faster at 64 units, 18.3 against 20.2 us; one
+// workgroup faster at 128, 20.9 against 26.7 us, and at the 256 units of four
+// 16-row windows, 23.7 against 42.7 us).
+constexpr int64_t kDecodeUnitKernelMin = 80;
+
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
+    if (units >= kDecodeUnitKernelMin) {
+        if (a.k8) hipLaunchKernelGGL(decode_unit_kernel<true>, dim3((unsigned)units), dim3(512), 0, st, a);
+        else hipLaunchKernelGGL(decode_unit_kernel<false>, dim3((unsigned)units), dim3(512), 0, st, a);
+        return hipGetLastError();
+    }
     const int wg = decode_wg_per_unit(a.top_k);
     if (a.k8) hipLaunchKernelGGL(decode_kernel<true>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
     else hipLaunchKernelGGL(decode_kernel<false>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);

@@ -249,13 +249,15 @@ size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
 /*
  * Step 4 for decode steps and verify windows: the same result as msa_prefill
  * (within rounding), computed as split-K over the kept keys.  Each kept block
- * (two 32-key pieces) is folded by its own wave; a workgroup's four waves
- * (block slots 4w..4w+3) combine theirs in LDS into one partial (max, sum,
- * weighted values) in `workspace`; the last workgroup of a (row, key head) to
- * finish merges that row's partials, in slot order, with log-sum-exp
- * weights.  The split depends only on top_k, never on the batch, so a row's
- * bits do not depend on the other rows: a verify window equals the same rows
- * decoded one at a time, bit for bit.
+ * (two 32-key pieces) is folded into a state of its own; the states of block
+ * slots 4w..4w+3 combine into partial w (max, sum, weighted values), and the
+ * partials merge in slot order with log-sum-exp weights.  With fewer than 80
+ * (row, key head) units in the batch, each unit's slots are spread over
+ * ceil(top_k/4) workgroups that publish their partials in `workspace`, and the
+ * last to finish merges them; with more, one workgroup per unit does it all on
+ * chip.  Both compute the same tree in the same order, and the tree depends
+ * only on top_k, so a row's bits do not depend on the other rows: a verify
+ * window equals the same rows decoded one at a time, bit for bit.
  *   workspace        device memory of >= msa_decode_workspace_bytes() bytes,
  *                    256-byte aligned.  Its first part holds one arrival
  *                    counter per (row, key head): it must be zero before the

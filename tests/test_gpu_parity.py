@@ -271,3 +271,27 @@ def test_prefill_rows_per_wave(name):
     assert torch.equal(o_big["block_idx"][r1:r1 + n1], o_small["block_idx"])
     assert torch.equal(o_big["out"][r1:r1 + n1], o_small["out"])
     assert torch.equal(o_big["lse"][r1:r1 + n1], o_small["lse"])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("top_k", [1, 5, 16, 32])
+def test_decode_kernels_agree(top_k):
+    """128 (row, key head) units take the one-workgroup-per-unit decode; each
+    sequence alone (32 units) the split over workgroups.  Both must give the
+    same bits, and the large batch must pass the oracle checks."""
+    case = make_case(f"dk{top_k}", [9000, 5000, 3000, 700], [8, 8, 8, 8], 4, seed=160 + top_k, top_k=top_k)
+    full_check(case, "decode")
+    t = device_tensors(case)
+    shape = shape_of(case)
+    big = msa.run_path(shape, msa.Batch(case.seq_lens, case.rows), t, "decode")
+    for s in range(case.n_seqs):
+        r0, r1 = case.cu_rows[s], case.cu_rows[s + 1]
+        k0, L = case.kv_start[s], case.seq_lens[s]
+        sub = {"q": t["q"][r0:r1].contiguous(), "iq": t["iq"][r0:r1].contiguous(),
+               "k": t["k"][k0:k0 + L].contiguous(), "v": t["v"][k0:k0 + L].contiguous(),
+               "ik": t["ik"][k0:k0 + L].contiguous()}
+        one = msa.run_path(shape, msa.Batch([L], [r1 - r0]), sub, "decode")
+        torch.cuda.synchronize()
+        assert torch.equal(big["block_idx"][r0:r1], one["block_idx"]), s
+        assert torch.equal(big["out"][r0:r1], one["out"]), s
+        assert torch.equal(big["lse"][r0:r1], one["lse"]), s
