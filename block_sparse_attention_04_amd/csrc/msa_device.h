@@ -22,10 +22,6 @@ constexpr int kMaxSelectBlocks = 16384;  // selection stages a row's block score
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-    return __uint_as_float(bits16 << 16);
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
@@ -109,11 +105,6 @@ __device__ __forceinline__ void force_ready(const u32x4 &x) { asm volatile("" ::
 __device__ __forceinline__ void force_ready(int x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Make LDS writes of this wave visible to its own later LDS reads (and keep
 // the compiler from moving LDS accesses across this point).
