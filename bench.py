@@ -22,6 +22,7 @@ workloads as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -192,6 +193,7 @@ def other_configs(torch, msa, dev, keep=None):
 
         timer = Timed(torch)
         warm = 2 * n_rep
+        gc.disable()   # a collection between an event and its call would show up as kernel time
         for i in range(steps + warm):
             for kname, fn in calls(reps[i % n_rep]):
                 if i < warm:
@@ -199,11 +201,14 @@ def other_configs(torch, msa, dev, keep=None):
                 else:
                     timer.run(kname, fn)
         torch.cuda.synchronize()
+        gc.enable()
         kms, kq = timer.mean_ms(), timer.quantiles_ms()
         work = algorithmic_work(case)
         total = sum(kms.values())
+        total_median = sum(q[1] for q in kq.values())
         ent = {"mode": mode, "rows": case.total_rows, "seq_lens": case.seq_lens, "kv_heads": case.n_kv_heads,
                "replicas": n_rep, "steps": steps, "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
+               "ms_median": total_median, "rows_per_s_median": case.total_rows / (total_median * 1e-3),
                "kernels": {k: {"ms": v, "ms_p10": kq[k][0], "ms_median": kq[k][1], "ms_p90": kq[k][2]}
                            for k, v in kms.items()}}
         for k, v in kms.items():
@@ -498,6 +503,7 @@ def main():
             torch.cuda.synchronize()
     # untimed pass with an event pair around every call: each kernel's duration
     n_call_steps = max(1, min(args.steps, 50))
+    gc.disable()   # a collection between an event and its call would show up as kernel time
     for i in range(n_call_steps):
         step(i, "all")
     torch.cuda.synchronize()
@@ -512,6 +518,7 @@ def main():
         step(i, True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     ms_step = elapsed / args.steps * 1e3
     rows = sum(c.total_rows for c in cases.values())
     # the dominant kernel: its launches inside the timed steps
