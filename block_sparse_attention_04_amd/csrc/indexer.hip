@@ -292,10 +292,12 @@ __device__ __forceinline__ float window_lane_max(const u32x4 (&av)[4][2], u32x4 
 // is discarded), and lane group lg ends up holding block b_begin + lg.
 constexpr int kWindowBlocks = 4;
 
-// kSelect: the fused index-and-select variant.  Every workgroup of a
-// (sequence, key head) counts itself in on an agent-scope counter after its
-// scores are stored (release); the last one (acquire) selects the sequence's
-// rows from the scores all of them wrote, resets the counter and leaves.
+// kSelect: the fused index-and-select variant (launched for one-row
+// sequences).  Every workgroup of a (sequence, key head) stores its scores
+// with device-scoped stores and, once they have completed, counts itself in on
+// a device-scoped counter; the last one reads the scores back with
+// device-scoped loads, selects the sequence's rows, resets the counter and
+// leaves.
 template <bool kSelect>
 __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t) {
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
