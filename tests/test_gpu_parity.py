@@ -17,6 +17,9 @@ SMALL = {
     "ragged_tiled": dict(seq_lens=[700, 1500, 300, 64], rows=[300, 5, 300, 64], n_kv_heads=2, seed=101),
     # <= 16 rows per sequence: the streaming indexer; includes a 1-key sequence
     "ragged_window": dict(seq_lens=[5000, 1, 64, 65, 3000], rows=[16, 1, 16, 7, 3], n_kv_heads=3, seed=102),
+    # the same with key heads in fours: a workgroup scores 4 heads of one key range
+    "ragged_window_h4": dict(seq_lens=[5000, 1, 64, 65, 3000], rows=[16, 1, 16, 7, 3], n_kv_heads=4, seed=108),
+    "ragged_window_h8": dict(seq_lens=[2000, 257, 1100], rows=[9, 16, 2], n_kv_heads=8, seed=109),
     # one index key shared by the key heads (head stride 0)
     "shared_ik": dict(seq_lens=[2000, 900], rows=[40, 8], n_kv_heads=4, seed=103, ik_shared=True),
     # indexer inputs scaled by 1/8 (exact), as in the tiny configuration
