@@ -2,12 +2,18 @@
 
 One step = the whole path on the two workloads the metric is quoted on:
   chunk: one 4,096-row prompt chunk on a 65,536-token cached prefix (69,632
-         keys), 4 key heads x 16 query heads: index scores -> block
-         selection -> msa_prefill;
-  long:  one decode row at 262,144 keys, 4 key heads x 16 query heads:
-         msa_index_select (index scores and block selection in one launch)
-         -> msa_decode (split-K, last-arriver combine); --unfused runs the
-         two separate steps instead.
+         keys), 4 key heads x 16 query heads: the chunk's 4,096 new keys
+         written into the tiled cache (msa_pack_kv_tiled) -> index scores ->
+         block selection -> msa_prefill_tiled;
+  long:  one decode row at 262,144 keys, 4 key heads x 16 query heads: the
+         row's new key written into the tiled cache -> msa_index_select
+         (index scores and block selection in one launch) ->
+         msa_decode_tiled (split-K, last-arriver combine); --unfused runs the
+         two separate selection steps instead.
+The key/value cache is the library's tiled bf16 layout (the cached prefix
+is packed before timing, as earlier steps would have written it; each step
+writes its own new keys); --kv-layout strided attends over the plain
+[tokens, heads, 128] cache instead (msa_prefill / msa_decode, no cache write).
 value = rows per second of the step (4,097 rows).  Inputs are resident in HBM
 before timing; the timed region enqueues K steps back to back, bracketed by a
 device synchronisation on both sides.  Inputs rotate over replicas so the
@@ -39,7 +45,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 def algorithmic_work(case, kv8=False):
     """Per-launch algorithmic FLOPs and bytes of each step for one workload
-    (kv8: the int8 cache, 128 + 4 bytes per key and key head for K and for V)."""
+    (kv8: the int8 cache, 128 + 4 bytes per key and key head for K and for V;
+    write_cache: the step's new keys' K and V read once and written once)."""
     import numpy as np
     H, G, D, dI, B, k = case.n_kv_heads, case.group, case.head_dim, case.index_dim, case.block, case.top_k
     pairs = 0           # causal (row, key) pairs per key head
@@ -66,6 +73,7 @@ def algorithmic_work(case, kv8=False):
     # kept K/V blocks, counted once per distinct (sequence, key head, block)
     attn_bytes += kept_kv_bytes(case) * (132 if kv8 else 256) // 256
     w["attention"] = dict(flops=4 * D * kept * H * G, bytes=attn_bytes)
+    w["write_cache"] = dict(flops=0, bytes=rows * H * D * 2 * 2 * 2)
     return w
 
 
@@ -389,6 +397,9 @@ def main():
     ap.add_argument("--kv8", action="store_true",
                     help="attention over the int8 key/value cache (codes + one fp32 scale per token and key "
                          "head, written by msa_quantize_kv8 before timing); the selection is unchanged")
+    ap.add_argument("--kv-layout", choices=("tiled", "strided"), default="tiled",
+                    help="tiled: the library's tiled bf16 cache (msa_kv_tiled; each step packs its own new "
+                         "keys into it); strided: the plain [tokens, heads, 128] cache")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
     ap.add_argument("--no-others", action="store_true",
@@ -401,6 +412,9 @@ def main():
     args = ap.parse_args()
     if args.paged and args.head_major:
         ap.error("--head-major applies to the contiguous layout only")
+    if args.kv8 or args.head_major:
+        args.kv_layout = "strided"   # their own layouts of the strided cache
+    tiled = args.kv_layout == "tiled"
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding by key head is described in the design notes)", file=sys.stderr)
@@ -418,7 +432,11 @@ def main():
     reps = {"chunk": 2, "long": 4}       # replicas: >= 512 MB rotated per workload
     modes = {"chunk": "prefill", "long": "decode"}
     fused = {"chunk": False, "long": not args.unfused}
-    steps_of = {n: (("index_select", "attention") if fused[n] else ("index_scores", "select_blocks", "attention"))
+    # the paged pools' new keys are not one token range: there the whole pool
+    # is packed before timing and the steps write nothing
+    write = tiled and not args.paged
+    steps_of = {n: (("write_cache",) if write else ()) +
+                   (("index_select", "attention") if fused[n] else ("index_scores", "select_blocks", "attention"))
                 for n in modes}
     state = {}
     for name, case in cases.items():
@@ -439,8 +457,13 @@ def main():
                 vc, vs = msa.msa_quantize_kv8(shape, t["v"])
                 t["kv8"] = msa.KV8(kc, vc, ks, vs)
                 del t["k"], t["v"]
+        if tiled:
+            for t in inputs:   # the cached prefix, written before timing (set-up)
+                t["kvt"] = msa.KVTiled.empty(t["k"].shape[0], case.n_kv_heads, dev)
+                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"])
         batch = msa.Batch(case.seq_lens, case.rows, device=dev, page_table=page_table)
-        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name], kv8=inputs[0].get("kv8"))
+        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name], kv8=inputs[0].get("kv8"),
+                            kvt=inputs[0].get("kvt"))
         state[name] = (shape, batch, inputs, outs)
     torch.cuda.synchronize()
 
@@ -456,12 +479,17 @@ def main():
         for name in ("chunk", "long"):
             shape, batch, inputs, o = state[name]
             t = inputs[i % len(inputs)]
+            calls = []
+            if write:   # the step's new keys (the last total_rows tokens) into the tiles
+                n_tok = t["k"].shape[0]
+                calls.append(("write_cache", lambda: msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"],
+                                                                           n_tok - batch.total_rows, n_tok)))
             if fused[name]:
-                calls = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"],
+                calls += [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"],
                                                                        o["block_scores"], o["block_idx"],
                                                                        o["select_workspace"]))]
             else:
-                calls = [
+                calls += [
                     ("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
                                                                   o["block_scores"])),
                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
@@ -470,6 +498,9 @@ def main():
             if modes[name] == "prefill" and args.kv8:
                 calls.append(("attention", lambda: msa.msa_prefill_kv8(shape, batch, t["q"], t["kv8"],
                                                                        o["block_idx"], o["out"], o["lse"])))
+            elif modes[name] == "prefill" and tiled:
+                calls.append(("attention", lambda: msa.msa_prefill_tiled(shape, batch, t["q"], t["kvt"],
+                                                                         o["block_idx"], o["out"], o["lse"])))
             elif modes[name] == "prefill":
                 calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"],
                                                                    o["block_idx"], o["out"], o["lse"])))
@@ -477,6 +508,10 @@ def main():
                 calls.append(("attention", lambda: msa.msa_decode_kv8(shape, batch, t["q"], t["kv8"],
                                                                       o["block_idx"], o["out"], o["lse"],
                                                                       o["workspace"])))
+            elif tiled:
+                calls.append(("attention", lambda: msa.msa_decode_tiled(shape, batch, t["q"], t["kvt"],
+                                                                        o["block_idx"], o["out"], o["lse"],
+                                                                        o["workspace"])))
             else:
                 calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"],
                                                                   o["block_idx"], o["out"], o["lse"],
@@ -573,7 +608,10 @@ def main():
                    "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
                    "kv_layout": ("paged (64-token pages, random order)" if args.paged else
                                  "contiguous, head-major" if args.head_major else "contiguous, token-major"),
-                   "kv_cache": "int8 codes + fp32 scale per (token, key head)" if args.kv8 else "bf16",
+                   "kv_cache": ("int8 codes + fp32 scale per (token, key head)" if args.kv8 else
+                                "bf16, tiled (64-key tiles in matrix-core operand order; each step writes its "
+                                "new keys into it" + (")" if write else "; pool packed before timing)")
+                                if tiled else "bf16"),
                    "index_queries": ("i.i.d. N(0,1) per row" if args.locality is None else
                                      f"secondary workload: AR(1) across the chunk's rows, a = {args.locality}")},
         "inputs": {"generator": "torch.Generator (CPU) seeded per workload, randn in fp32 rounded to bf16",

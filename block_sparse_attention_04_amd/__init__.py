@@ -44,6 +44,7 @@ class _BatchC(ctypes.Structure):
 
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
            "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
+           "msa_pack_kv_tiled", "msa_prefill_tiled", "msa_decode_tiled",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
            "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_mfma")
 
@@ -52,6 +53,11 @@ class _KV8C(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
                 ("v_scale", ctypes.c_void_p), ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
                 ("scale_tok_stride", ctypes.c_int64), ("scale_head_stride", ctypes.c_int64)]
+
+
+class _KVTiledC(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
 
 
 def lib():
@@ -73,8 +79,13 @@ def lib():
             L.msa_quantize_kv8.argtypes = [SP, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp]
             L.msa_prefill_kv8.argtypes = [SP, BP, vp, KP, vp, vp, vp, vp]
             L.msa_decode_kv8.argtypes = [SP, BP, vp, KP, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            TP = ctypes.POINTER(_KVTiledC)
+            L.msa_pack_kv_tiled.argtypes = [SP, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp]
+            L.msa_prefill_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
+            L.msa_decode_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp, ctypes.c_size_t, vp]
             for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
-                      "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8"):
+                      "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8", "msa_pack_kv_tiled",
+                      "msa_prefill_tiled", "msa_decode_tiled"):
                 getattr(L, n).restype = ctypes.c_int
             for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
                 getattr(L, n).argtypes = [SP, i32]
@@ -327,12 +338,86 @@ def msa_decode_kv8(shape: Shape, batch: Batch, q, kv: KV8, block_idx, out, lse=N
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+TILE_ELEMS = 64 * 128   # one key head's K (or V) of one 64-key block
+
+
+class KVTiled:
+    """A tiled bf16 key/value cache (include/msa.h, msa_kv_tiled): K and V
+    tiles as bf16 device tensors [blocks, H, 8192] with a contiguous last axis
+    (tile (t, g) holds key head g of tokens 64t .. 64t+63), kept alive here."""
+
+    def __init__(self, k_tiles, v_tiles):
+        for x, name in ((k_tiles, "k tiles"), (v_tiles, "v tiles")):
+            _need(x, torch.bfloat16, name, contiguous=False)
+            if x.dim() != 3 or x.shape[2] != TILE_ELEMS or x.stride(2) != 1:
+                raise ValueError(f"{name} must be [blocks, heads, {TILE_ELEMS}] with a contiguous last axis")
+        if k_tiles.shape != v_tiles.shape or k_tiles.stride() != v_tiles.stride():
+            raise ValueError("k and v tiles must share shape and strides")
+        self.k, self.v = k_tiles, v_tiles
+        self.c = _KVTiledC(k_tiles.data_ptr(), v_tiles.data_ptr(), k_tiles.stride(0), k_tiles.stride(1))
+
+    @staticmethod
+    def empty(n_tokens: int, n_kv_heads: int, device="cuda", fill: float | None = None) -> "KVTiled":
+        """Tiles for tokens 0 .. n_tokens-1 (block-major); `fill` sets every
+        element first (the attention never reads keys no row can see)."""
+        nb = max(1, (int(n_tokens) + 63) // 64)
+        mk = (lambda: torch.empty(nb, n_kv_heads, TILE_ELEMS, dtype=torch.bfloat16, device=device)) \
+            if fill is None else \
+            (lambda: torch.full((nb, n_kv_heads, TILE_ELEMS), fill, dtype=torch.bfloat16, device=device))
+        return KVTiled(mk(), mk())
+
+
+def msa_pack_kv_tiled(shape: Shape, k, v, tiles: KVTiled, tok_begin: int = 0, tok_end: int | None = None,
+                      stream=None):
+    """Write tokens tok_begin .. tok_end-1 of the strided cache (k, v:
+    [tokens, H, 128]) into their tiles; other keys of those tiles are kept."""
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(v, torch.bfloat16, "v", contiguous=False)
+    tok, head = _strides_tok_head(k, "k")
+    if _strides_tok_head(v, "v") != (tok, head):
+        raise ValueError("k and v must share strides")
+    tok_end = k.shape[0] if tok_end is None else tok_end
+    if not 0 <= tok_begin < tok_end <= min(k.shape[0], v.shape[0]):
+        raise ValueError(f"token range [{tok_begin}, {tok_end}) outside k/v of {k.shape[0]} tokens")
+    if (tok_end - 1) // 64 >= tiles.k.shape[0] or k.shape[1] != tiles.k.shape[1]:
+        raise ValueError("the tiles do not cover the token range or the key heads")
+    c = tiles.c
+    _check(lib().msa_pack_kv_tiled(ctypes.byref(shape), int(tok_begin), int(tok_end), _ptr(k), _ptr(v), tok, head,
+                                   ctypes.c_void_p(c.k), ctypes.c_void_p(c.v), c.block_stride, c.head_stride,
+                                   _stream(stream)))
+
+
+def msa_prefill_tiled(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out, lse=None, stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().msa_prefill_tiled(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
+                                   _ptr(block_idx), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def msa_decode_tiled(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out, lse=None, workspace=None,
+                     stream=None):
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    if workspace is None:
+        workspace = decode_workspace(shape, batch.total_rows, q.device)
+    _check(lib().msa_decode_tiled(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
+                                  _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: dict | None = None,
-             stream=None, fused: bool = False, kv8: KV8 | None = None) -> dict:
+             stream=None, fused: bool = False, kv8: KV8 | None = None, kvt: KVTiled | None = None) -> dict:
     """Enqueue the whole path -- index scores, selection, attention -- on
     device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
     fused: steps 1-3 through msa_index_select.
     kv8: attend over this int8 cache instead of t["k"], t["v"].
+    kvt: attend over this tiled cache instead of t["k"], t["v"].
     Output buffers are allocated unless given in `out`."""
     out = {} if out is None else out
     dev = t["q"].device
@@ -356,6 +441,8 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
     if mode == "prefill":
         if kv8 is not None:
             msa_prefill_kv8(shape, batch, t["q"], kv8, out["block_idx"], out["out"], out["lse"], stream)
+        elif kvt is not None:
+            msa_prefill_tiled(shape, batch, t["q"], kvt, out["block_idx"], out["out"], out["lse"], stream)
         else:
             msa_prefill(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"], stream)
     elif mode == "decode":
@@ -364,6 +451,9 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
         if kv8 is not None:
             msa_decode_kv8(shape, batch, t["q"], kv8, out["block_idx"], out["out"], out["lse"],
                            out["workspace"], stream)
+        elif kvt is not None:
+            msa_decode_tiled(shape, batch, t["q"], kvt, out["block_idx"], out["out"], out["lse"],
+                             out["workspace"], stream)
         else:
             msa_decode(shape, batch, t["q"], t["k"], t["v"], out["block_idx"], out["out"], out["lse"],
                        out["workspace"], stream)

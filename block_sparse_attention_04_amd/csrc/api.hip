@@ -314,6 +314,7 @@ static int attn_common(const msa_shape *shape, const msa_batch *batch, const voi
     a->vs = kv8 ? kv8->v_scale : nullptr;
     a->s_tok = kv8 ? kv8->scale_tok_stride : 0;
     a->s_head = kv8 ? kv8->scale_head_stride : 0;
+    a->tiled = false;
     return MSA_OK;
 }
 
@@ -335,6 +336,21 @@ size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows) {
     return msa::decode_workspace_bytes((int64_t)total_rows * shape->n_kv_heads, shape->top_k);
 }
 
+// Workspace checks and the decode launch, for arguments attn_common accepted.
+static int decode_launch(msa::AttnArgs &a, const msa_batch *batch, const msa_shape *shape, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    int rc;
+    const int64_t units = (int64_t)batch->total_rows * shape->n_kv_heads;
+    const size_t need = msa::decode_workspace_bytes(units, shape->top_k);
+    if (!workspace || workspace_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if ((rc = check_device())) return rc;
+    a.ws_count = static_cast<unsigned *>(workspace);
+    a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::decode_count_bytes(units));
+    return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
 static int decode_common(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
                          const void *v, int64_t kv_tok_stride, int64_t kv_head_stride, const int32_t *block_idx,
                          void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
@@ -345,15 +361,7 @@ static int decode_common(const msa_shape *shape, const msa_batch *batch, const v
                          &empty, kv8);
     if (rc) return rc;
     if (empty) return ok();
-    const int64_t units = (int64_t)batch->total_rows * shape->n_kv_heads;
-    const size_t need = msa::decode_workspace_bytes(units, shape->top_k);
-    if (!workspace || workspace_bytes < need)
-        return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
-    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
-    if ((rc = check_device())) return rc;
-    a.ws_count = static_cast<unsigned *>(workspace);
-    a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::decode_count_bytes(units));
-    return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+    return decode_launch(a, batch, shape, workspace, workspace_bytes, stream);
 }
 
 int msa_decode(const msa_shape *shape, const msa_batch *batch, const void *q, const void *k,
@@ -381,6 +389,85 @@ int msa_prefill_kv8(const msa_shape *shape, const msa_batch *batch, const void *
     if (empty) return ok();
     if ((rc = check_device())) return rc;
     return launched(msa::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill_kv8");
+}
+
+static int check_tiles(const void *k, const void *v, int64_t block_stride, int64_t head_stride, int n_kv_heads) {
+    if (!k || !v) return fail(MSA_ERR_INVALID, "k/v tiles must not be NULL");
+    if (!aligned16(k) || !aligned16(v) || block_stride % 8 || head_stride % 8)
+        return fail(MSA_ERR_INVALID, "tiles must be 16-byte aligned");
+    if (block_stride < msa::kTileElems || head_stride < 0 || (n_kv_heads > 1 && head_stride < msa::kTileElems))
+        return fail(MSA_ERR_INVALID, "tile strides (%lld, %lld) overlap a %d-element tile", (long long)block_stride,
+                    (long long)head_stride, msa::kTileElems);
+    return MSA_OK;
+}
+
+static int tiled_common(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                        const int32_t *block_idx, void *out, float *lse, msa::AttnArgs *a, bool *empty) {
+    int rc;
+    if (!kv) return fail(MSA_ERR_INVALID, "kv is NULL");
+    if ((rc = check_shape(shape))) return rc;
+    if ((rc = check_tiles(kv->k, kv->v, kv->block_stride, kv->head_stride, shape->n_kv_heads))) return rc;
+    // the strided checks do not apply to tile strides: give attn_common a
+    // valid strided description, then replace it with the tiles
+    if ((rc = attn_common(shape, batch, q, kv->k, kv->v, msa::kHeadDim * shape->n_kv_heads, msa::kHeadDim,
+                          block_idx, out, lse, a, empty)))
+        return rc;
+    a->kv_tok = kv->block_stride;
+    a->kv_head = kv->head_stride;
+    a->tiled = true;
+    return MSA_OK;
+}
+
+int msa_prefill_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                      const int32_t *block_idx, void *out, float *lse, void *stream) {
+    msa::AttnArgs a;
+    bool empty = false;
+    int rc = tiled_common(shape, batch, q, kv, block_idx, out, lse, &a, &empty);
+    if (rc) return rc;
+    if (empty) return ok();
+    if ((rc = check_device())) return rc;
+    return launched(msa::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill_tiled");
+}
+
+int msa_decode_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                     const int32_t *block_idx, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    msa::AttnArgs a;
+    bool empty = false;
+    int rc = tiled_common(shape, batch, q, kv, block_idx, out, lse, &a, &empty);
+    if (rc) return rc;
+    if (empty) return ok();
+    return decode_launch(a, batch, shape, workspace, workspace_bytes, stream);
+}
+
+int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end, const void *k, const void *v,
+                      int64_t kv_tok_stride, int64_t kv_head_stride, void *k_tiles, void *v_tiles,
+                      int64_t block_stride, int64_t head_stride, void *stream) {
+    int rc;
+    if ((rc = check_shape(shape))) return rc;
+    if (tok_begin < 0 || tok_end <= tok_begin)
+        return fail(MSA_ERR_INVALID, "token range [%lld, %lld) is empty or negative", (long long)tok_begin,
+                    (long long)tok_end);
+    const int H = shape->n_kv_heads;
+    if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, H))) return rc;
+    if ((rc = check_tiles(k_tiles, v_tiles, block_stride, head_stride, H))) return rc;
+    msa::PackTiledArgs a;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.tok = kv_tok_stride;
+    a.head = kv_head_stride;
+    a.kt = static_cast<uint16_t *>(k_tiles);
+    a.vt = static_cast<uint16_t *>(v_tiles);
+    a.t_blk = block_stride;
+    a.t_head = head_stride;
+    a.tok_begin = tok_begin;
+    a.tok_end = tok_end;
+    a.n_blocks = (tok_end - 1) / 64 - tok_begin / 64 + 1;
+    a.H = H;
+    if (a.n_blocks * H * 2048 / 256 > (int64_t)0x7fffffff)
+        return fail(MSA_ERR_UNSUPPORTED, "token range too large for one call");
+    if ((rc = check_device())) return rc;
+    return launched(msa::launch_pack_kv_tiled(a, static_cast<hipStream_t>(stream)), "pack_kv_tiled");
 }
 
 int msa_quantize_kv8(const msa_shape *shape, int64_t n_tokens, const void *x, int64_t tok_stride,

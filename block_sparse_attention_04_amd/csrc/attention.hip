@@ -148,6 +148,38 @@ __device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
     }
 }
 
+// Registers of one 32-key chunk from a tiled cache (kt, vt: the chunk's 4,096
+// elements of its block's K and V tiles).  The K tile holds the 8 operands
+// ka[mt][s] in order and the V tile the 8 V^T operands of fold_rows' PV
+// product (d-tile dt in vr[dt / 2][dt % 2]), each as 64 lane-ordered 16-byte
+// pieces, so every load reads 1 KiB of contiguous memory.  Keys past `last`
+// (the chunk's largest visible key offset) may never have been written: their
+// scores are masked in fold_rows, and their V elements are cleared here (their
+// weight is 0, but 0 times an unwritten NaN would not be).
+__device__ __forceinline__ void load_chunk_tiled(ChunkRegs &c, const uint16_t *kt, const uint16_t *vt,
+                                                 int last) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c.ka[mt][s] = load16(kt + 8 * ((4 * mt + s) * kWave + lane));
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) c.vr[dt >> 1][dt & 1] = load16(vt + 8 * (dt * kWave + lane));
+    if (last < 31) {
+        // dword w of a V^T operand: keys k0 (low half) and k0 + 1 (high half)
+        uint32_t m[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int k0 = (w < 2 ? 4 * lg : 16 + 4 * lg) + 2 * (w & 1);
+            m[w] = (k0 <= last ? 0x0000ffffu : 0u) | (k0 + 1 <= last ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) c.vr[dt >> 1][dt & 1][w] &= m[w];
+    }
+}
+
 // Raw registers of one 32-key chunk of an int8 cache: K codes (key kbase +
 // 16*mt + lane%16, dims 32*(lane/16) + 16*h .. +15), V codes (key kbase +
 // 4*(lane/8) + kk, dims 8*(lane%8 + 8*hf) .. +7) and one scale per lane:
@@ -224,10 +256,12 @@ __device__ __forceinline__ void stage_v8(const ChunkRegs8 &c, uint8_t *vt, float
 // KV8 (int8 cache): every key's score is scaled by its key scale and every
 // weight by its value scale before the PV product (the sum of weights is
 // unscaled), with the scales from the wave's scale tile `sct`.
-template <int RW, bool KV8>
+// kVR (tiled cache): the V^T operands come ready from registers (vr, as
+// load_chunk_tiled leaves them) instead of the LDS tile.
+template <int RW, bool KV8, bool kVR = false>
 __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x4 (&qb)[4],
                                           const u32x4 (&ka)[2][4], int kbase, int p, float scale_log2,
-                                          const uint8_t *vt, const float *sct) {
+                                          const uint8_t *vt, const float *sct, const u32x4 (*vr)[2] = nullptr) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     floatx4 sacc[2];
 #pragma unroll
@@ -309,15 +343,20 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
     // addresses the 8-byte piece (dims 16*dt + 4*(t%4) .. +3) of key 4*lg + t/4
     // (and key + 16); the swizzle only flips address bits 5..7, so the piece
     // for d-tile dt sits at the dt = 0 offset XOR (dt << 5).
-    const int vkey = 4 * lg + (lr >> 2);
-    const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
     u32x4 va[8];
+    if constexpr (kVR) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const int rd = rd0 ^ (dt << 5);
-        const uint2 lo = lds_read_tr16(vt + rd);
-        const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
-        va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        for (int dt = 0; dt < 8; ++dt) va[dt] = vr[dt >> 1][dt & 1];
+    } else {
+        const int vkey = 4 * lg + (lr >> 2);
+        const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const int rd = rd0 ^ (dt << 5);
+            const uint2 lo = lds_read_tr16(vt + rd);
+            const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
+            va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i)
@@ -335,6 +374,13 @@ __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], co
     wave_lds_sync();
     fold_rows<1, false>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, c.ka, kbase, p, scale_log2, vt, nullptr);
     wave_lds_sync();   // reads finish before the next chunk overwrites the tile
+}
+
+// The same from a tiled cache's registers (no V tile, no LDS).
+__device__ __forceinline__ void fold_chunk_tiled(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
+                                                 int kbase, int p, float scale_log2) {
+    fold_rows<1, false, true>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, c.ka, kbase, p, scale_log2, nullptr,
+                              nullptr, c.vr);
 }
 
 __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs8 &c,
@@ -386,7 +432,9 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 // different ranks of their own lists, long after L2 has turned over.
 constexpr int kInvalidKey = 1 << 25;   // above every block index of an int32 position
 
-template <int RW, bool KV8>
+// kTiled: K/V from a tiled cache (kv_tok / kv_head are the tiles' block and
+// head strides); the chunk's V^T operands stay in registers.
+template <int RW, bool KV8, bool kTiled>
 __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, uint8_t *vt, uint8_t *qt,
                                               float *sct) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
@@ -472,6 +520,11 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     };
     using Regs = typename std::conditional<KV8, ChunkRegs8, ChunkRegs>::type;
     auto load = [&](Regs &r, const Chunk &c) {
+        if constexpr (kTiled) {   // block c.tok / 64, half (c.tok / 32) % 2
+            const int64_t off = (c.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head + ((c.tok >> 5) & 1) * 4096;
+            load_chunk_tiled(r, a.k + off, a.v + off, c.p_max - c.kb);
+            return;
+        }
         const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
         if constexpr (KV8) {
             const int64_t soff = c.tok * a.s_tok + (int64_t)g * a.s_head;
@@ -487,10 +540,10 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         if constexpr (KV8) {
             stage_v8(r, vt, sct);
             k_operands8(r, ka8);
-        } else {
+        } else if constexpr (!kTiled) {
             stage_v(r, vt);
         }
-        wave_lds_sync();
+        if constexpr (!kTiled) wave_lds_sync();
         for (int j = c.k; j < c.end; ++j) {
             const int row = __builtin_amdgcn_readlane(e_key, j) & 3;
             const int p = __builtin_amdgcn_readlane(e_p, j);
@@ -498,9 +551,11 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
             u32x4 qb[4];
             read_q<KV8>(qb, qt + row * kQTileBytes);
             if constexpr (KV8) fold_rows<RW, true>(st, row, qb, ka8, c.kb, p, a.scale_log2, vt, sct);
+            else if constexpr (kTiled)
+                fold_rows<RW, false, true>(st, row, qb, r.ka, c.kb, p, a.scale_log2, nullptr, nullptr, r.vr);
             else fold_rows<RW, false>(st, row, qb, r.ka, c.kb, p, a.scale_log2, vt, nullptr);
         }
-        wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
+        if constexpr (!kTiled) wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
     };
 
     force_ready(e_key);
@@ -549,9 +604,9 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
 
 // Groups are enumerated head-major (consecutive groups: consecutive rows of one
 // key head), one per wave.
-template <int RW, bool KV8>
+template <int RW, bool KV8, bool kTiled>
 __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled ? 16 : 8192];
     __shared__ __attribute__((aligned(16))) uint8_t qt_all[4][RW * kQTileBytes];
     __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
     const int wave = uniform(threadIdx.x >> 6);
@@ -559,7 +614,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per
     if (grp >= (int64_t)groups_per_head * a.H) return;
     const int g = (int)(grp / groups_per_head);
     const int r0 = (int)(grp % groups_per_head) * RW;
-    prefill_group<RW, KV8>(a, g, r0, vt_all[wave], qt_all[wave], sc_all[wave]);
+    prefill_group<RW, KV8, kTiled>(a, g, r0, vt_all[wave], qt_all[wave], sc_all[wave]);
 }
 
 // Decode.  The kept list of a (row, key head) is folded one block (two 32-key
@@ -571,7 +626,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per
 // kernel the launch picks, or on which workgroup finished last.
 
 // One kept block (index b_raw) of unit u folded into st.
-template <bool KV8>
+template <bool KV8, bool kTiled>
 __device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit &u, int64_t kv0,
                                                   const u32x4 (&qb)[4], int b_raw, Softmax &st, uint8_t *vt,
                                                   float *sct) {
@@ -579,6 +634,15 @@ __device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit 
     const int kb0 = b * kBlock, kb1 = kb0 + 32;
     if (b < 0 || kb0 > u.p) return;
     const int64_t t0 = block_token0(a.b, u.s, kv0, b);     // the block's first key
+    if constexpr (kTiled) {   // the tile of block t0 / 64
+        const int64_t off = (t0 >> 6) * a.kv_tok + (int64_t)u.g * a.kv_head;
+        ChunkRegs ca, cb;
+        load_chunk_tiled(ca, a.k + off, a.v + off, u.p - kb0);
+        if (kb1 <= u.p) load_chunk_tiled(cb, a.k + off + 4096, a.v + off + 4096, u.p - kb1);
+        fold_chunk_tiled(st, qb, ca, kb0, u.p, a.scale_log2);
+        if (kb1 <= u.p) fold_chunk_tiled(st, qb, cb, kb1, u.p, a.scale_log2);
+        return;
+    }
     const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
     if constexpr (KV8) {
         const int64_t soff = t0 * a.s_tok + (int64_t)u.g * a.s_head;
@@ -671,7 +735,7 @@ __device__ __forceinline__ void decode_write(const AttnArgs &a, const Unit &u, i
 // folds slots 4*split .. +3 (one per wave) and combines them into partial
 // `split`; with several partials each workgroup publishes its partial and the
 // last to arrive (a per-unit counter) merges them.
-template <bool KV8>
+template <bool KV8, bool kTiled>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
     __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
@@ -694,7 +758,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         const int64_t kv0 = seq_token0(a.b, u.s);
         u32x4 qb[4];
         load_q<KV8>(qb, a.q + ((int64_t)u.r * hq + u.g * kGroup) * kHeadDim);
-        decode_fold_block<KV8>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
+        decode_fold_block<KV8, kTiled>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
         decode_stash(st, wm[wave], wl[wave], vt_all[wave]);
     } else if (lane < 16) {
         wm[wave][lane] = -INFINITY;
@@ -780,7 +844,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
 // own; after each pass the workgroup forms that pass's two partials, kept in
 // registers, and merges all partials at the end.  Nothing leaves the CU until
 // the output, and the arithmetic is decode_kernel's, step for step.
-template <bool KV8>
+template <bool KV8, bool kTiled>
 __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
     constexpr int kW = 8;
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[kW][8192];
@@ -807,7 +871,7 @@ __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
             Softmax st;
             softmax_init(st);
             const int b_raw = a.idx[((int64_t)u.r * a.H + u.g) * a.top_k + slot];
-            decode_fold_block<KV8>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
+            decode_fold_block<KV8, kTiled>(a, u, kv0, qb, b_raw, st, vt_all[wave], sc_all[wave]);
             decode_stash(st, wm[wave], wl[wave], vt_all[wave]);
         } else if (lane < 16) {
             wm[wave][lane] = -INFINITY;
@@ -840,28 +904,30 @@ __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
 // waves: two per SIMD of the 256 CUs.
 constexpr int64_t kPrefillFillWaves = 2048;
 
-template <int RW, bool KV8>
+template <int RW, bool KV8, bool kTiled>
 static void launch_prefill_rw(const AttnArgs &a, hipStream_t st) {
     const int gph = (a.b.total_rows + RW - 1) / RW;
     const int64_t waves = (int64_t)gph * a.H;
-    hipLaunchKernelGGL((prefill_kernel<RW, KV8>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, gph);
+    hipLaunchKernelGGL((prefill_kernel<RW, KV8, kTiled>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a,
+                       gph);
 }
 
-template <bool KV8>
+template <bool KV8, bool kTiled>
 static void launch_prefill_t(const AttnArgs &a, hipStream_t st) {
     // 4 rows per wave while their 4 * top_k entries fit the 64 lanes, else 2;
     // fewer while the grid would leave SIMDs idle (a short batch walks longer
     // merged lists on fewer waves).  A row's result does not depend on it.
     int rw = a.top_k <= 16 ? 4 : 2;
     while (rw > 1 && (int64_t)((a.b.total_rows + rw - 1) / rw) * a.H < kPrefillFillWaves) rw /= 2;
-    if (rw == 4) launch_prefill_rw<4, KV8>(a, st);
-    else if (rw == 2) launch_prefill_rw<2, KV8>(a, st);
-    else launch_prefill_rw<1, KV8>(a, st);
+    if (rw == 4) launch_prefill_rw<4, KV8, kTiled>(a, st);
+    else if (rw == 2) launch_prefill_rw<2, KV8, kTiled>(a, st);
+    else launch_prefill_rw<1, KV8, kTiled>(a, st);
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
-    if (a.k8) launch_prefill_t<true>(a, st);
-    else launch_prefill_t<false>(a, st);
+    if (a.k8) launch_prefill_t<true, false>(a, st);
+    else if (a.tiled) launch_prefill_t<false, true>(a, st);
+    else launch_prefill_t<false, false>(a, st);
     return hipGetLastError();
 }
 
@@ -876,13 +942,17 @@ constexpr int64_t kDecodeUnitKernelMin = 80;
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;
     if (units >= kDecodeUnitKernelMin) {
-        if (a.k8) hipLaunchKernelGGL(decode_unit_kernel<true>, dim3((unsigned)units), dim3(512), 0, st, a);
-        else hipLaunchKernelGGL(decode_unit_kernel<false>, dim3((unsigned)units), dim3(512), 0, st, a);
+        const dim3 grid((unsigned)units), block(512);
+        if (a.k8) hipLaunchKernelGGL((decode_unit_kernel<true, false>), grid, block, 0, st, a);
+        else if (a.tiled) hipLaunchKernelGGL((decode_unit_kernel<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_unit_kernel<false, false>), grid, block, 0, st, a);
         return hipGetLastError();
     }
     const int wg = decode_wg_per_unit(a.top_k);
-    if (a.k8) hipLaunchKernelGGL(decode_kernel<true>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
-    else hipLaunchKernelGGL(decode_kernel<false>, dim3((unsigned)(units * wg)), dim3(256), 0, st, a, wg);
+    const dim3 grid((unsigned)(units * wg)), block(256);
+    if (a.k8) hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, st, a, wg);
+    else if (a.tiled) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, st, a, wg);
+    else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, st, a, wg);
     return hipGetLastError();
 }
 

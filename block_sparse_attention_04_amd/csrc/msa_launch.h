@@ -51,8 +51,9 @@ struct AttnArgs {
     int H, top_k;
     float scale_log2;            // softmax scale * log2(e)
     const uint16_t *q;           // [total_rows, H*16, 128]
-    const uint16_t *k, *v;       // strided, dims contiguous
-    int64_t kv_tok, kv_head;
+    const uint16_t *k, *v;       // strided, dims contiguous; or tiled (below)
+    int64_t kv_tok, kv_head;     // tiled: elements between tiles of consecutive blocks / key heads
+    bool tiled;                  // k, v are tiled caches (tile of block t0 / 64, operand order)
     const int32_t *idx;          // [total_rows, H, top_k]
     uint16_t *out;               // [total_rows, H*16, 128]
     float *lse;                  // [total_rows, H*16] or null
@@ -97,10 +98,24 @@ struct QuantArgs {
     int H;
 };
 
+// Tiled cache writer: tokens [tok_begin, tok_end) of strided k / v into the
+// tiles of blocks tok_begin / 64 .. (tok_end - 1) / 64 (n_blocks of them).
+constexpr int kTileElems = 64 * 128;   // one key head's K (or V) of one block
+
+struct PackTiledArgs {
+    const uint16_t *k, *v;
+    int64_t tok, head;           // element strides of k / v
+    uint16_t *kt, *vt;
+    int64_t t_blk, t_head;       // element strides of the tiles
+    int64_t tok_begin, tok_end, n_blocks;
+    int H;
+};
+
 // Sets the message msa_last_error() returns (empty for success) and returns status.
 int report(int status, const char *msg);
 
 hipError_t launch_quantize_kv8(const QuantArgs &a, hipStream_t st);
+hipError_t launch_pack_kv_tiled(const PackTiledArgs &a, hipStream_t st);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);

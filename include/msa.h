@@ -242,6 +242,55 @@ int msa_decode_kv8(const msa_shape *shape, const msa_batch *batch, const void *q
                    const int32_t *block_idx, void *out, float *lse, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/*
+ * Tiled bf16 key/value cache (opt-in layout; the same values as the strided
+ * bf16 cache, and msa_prefill_tiled / msa_decode_tiled return bit for bit
+ * what msa_prefill / msa_decode return on it).  The pages leave the cache
+ * layout to the kernel; this one stores each key/value block in the order the
+ * attention's matrix-core operands read it, so every 64-lane load of a kept
+ * block reads 1 KiB of contiguous memory.  Tile (block t, key head g) holds
+ * key head g of tokens 64t .. 64t+63: a K tile at k + t*block_stride +
+ * g*head_stride and a V tile at the same offset from v, 8,192 bf16 each.
+ * Within a tile, chunk c = 0, 1 (keys 32c .. 32c+31 of the block) fills
+ * elements 4096c .. 4096c+4095 as 512 pieces of 8 elements, piece q at 8q:
+ *   K: q = 256*mt + 64*s + l -> key 32c + 16*mt + l%16, dims 32*s + 8*(l/16) + 0..7
+ *   V: q = 64*dt + l         -> dim 16*dt + l%16 of keys 32c + 4*(l/16) + 0..3,
+ *                               then of keys 32c + 16 + 4*(l/16) + 0..3
+ * (mt < 2, s < 4, dt < 8, l < 64).  Tokens are numbered as for the strided
+ * cache (kv_start or the page table), and a block must start a tile: in the
+ * contiguous layout every kv_start[s] is a multiple of 64 (a precondition,
+ * like cu_rows); in the paged layout page p is tile p.  Keys of a tile that
+ * no row can see need not be written (they are never used, NaN included).
+ */
+typedef struct msa_kv_tiled {
+    const void *k, *v;       /* tiles, 16-byte aligned */
+    int64_t block_stride;    /* elements between tiles of consecutive blocks: a multiple of 8, >= 8192 */
+    int64_t head_stride;     /* elements between key heads' tiles: a multiple of 8, >= 8192 if n_kv_heads > 1 */
+} msa_kv_tiled;
+
+/*
+ * Write tokens tok_begin .. tok_end-1 of a strided bf16 cache (k and v as in
+ * msa_prefill) into their tiles (blocks tok_begin/64 .. (tok_end-1)/64 of
+ * k_tiles / v_tiles, strides as in msa_kv_tiled);
+ * other keys of those tiles keep their contents, so a cache is extended a
+ * prompt chunk or a decode token at a time.  Errors: MSA_ERR_INVALID for a
+ * NULL pointer, an empty or negative range, or strides as msa_prefill and
+ * msa_kv_tiled reject them.
+ */
+int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end,
+                      const void *k, const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
+                      void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
+                      void *stream);
+
+/* msa_prefill over a tiled cache (other arguments and errors as msa_prefill). */
+int msa_prefill_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                      const int32_t *block_idx, void *out, float *lse, void *stream);
+
+/* msa_decode over a tiled cache (other arguments, workspace and errors as msa_decode). */
+int msa_decode_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                     const int32_t *block_idx, void *out, float *lse, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace msa_decode needs for total_rows rows (host
  * function; 0 for an invalid shape). */
 size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);

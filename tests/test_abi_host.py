@@ -210,3 +210,36 @@ def test_peaks_kernels_reject_bad_arguments():
     assert L.msa_peaks_mfma(sink, 1, 0, None) == -1
     assert L.msa_peaks_mfma(sink, 1 << 21, 1, None) == -1
     assert b"mfma" in L.msa_last_error()
+
+
+def test_tiled_cache_checks():
+    L = msa.lib()
+    sh = msa.make_shape(2)
+    b = FakeBatch()
+    kv = lambda k=4096, v=8192, bs=2 * 8192, hs=8192: msa._KVTiledC(k, v, bs, hs)
+    call = lambda c, out=65536: L.msa_prefill_tiled(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(1 << 20),
+                                                    ctypes.byref(c), ctypes.c_void_p(32768),
+                                                    ctypes.c_void_p(out) if out else None, None, None)
+    assert L.msa_prefill_tiled(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(1 << 20), None,
+                               ctypes.c_void_p(32768), ctypes.c_void_p(65536), None, None) == -1
+    assert call(kv(k=0)) == -1 and "NULL" in _err()
+    assert call(kv(v=8192 + 8)) == -1 and "aligned" in _err()
+    assert call(kv(bs=8192 + 4)) == -1 and "aligned" in _err()
+    assert call(kv(bs=4096)) == -1 and "tile" in _err()
+    assert call(kv(hs=4096)) == -1 and "tile" in _err()           # two heads' tiles overlap
+    assert call(kv(), out=0) == -1
+    one = msa.make_shape(1)
+    assert L.msa_prefill_tiled(ctypes.byref(one), ctypes.byref(b.c), ctypes.c_void_p(1 << 20),
+                               ctypes.byref(kv(hs=0)), ctypes.c_void_p(32768), ctypes.c_void_p(65536),
+                               None, None) in (0, -4)               # valid: only the device check may fail
+    need = msa.msa_decode_workspace_bytes(sh, 4)
+    assert L.msa_decode_tiled(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(1 << 20), ctypes.byref(kv()),
+                              ctypes.c_void_p(32768), ctypes.c_void_p(65536), None, ctypes.c_void_p(131072),
+                              need - 1, None) == -3
+    pack = lambda t0, t1, tok=256, bs=2 * 8192: L.msa_pack_kv_tiled(
+        ctypes.byref(sh), t0, t1, ctypes.c_void_p(4096), ctypes.c_void_p(8192), tok, 128,
+        ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), bs, 8192, None)
+    assert pack(5, 5) == -1 and "range" in _err()
+    assert pack(-1, 5) == -1
+    assert pack(0, 100, tok=64) == -1 and "kv strides" in _err()
+    assert pack(0, 100, bs=8) == -1 and "tile" in _err()
