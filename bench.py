@@ -164,13 +164,15 @@ class Timed:
 OTHER_CONFIGS = (("tiny", "prefill", 1, 50), ("decode", "decode", 8, 200), ("windows", "decode", 3, 200))
 
 
-def other_configs(torch, msa, dev, keep=None):
+def other_configs(torch, msa, dev, keep=None, tiled=True):
     """The other named workloads, for reference beside the headline line (not
     part of `value`): the 2,048-token prefill, the batched decode of 4 x 32,768
     keys and the four 16-row verify windows, each timed per library call with
     HIP events (mean and p10 / median / p90 over the timed passes, after two
     warm-up passes per replica).  keep: a dict that receives each workload's
-    case and host copies of its outputs, for the oracle leg."""
+    case and host copies of its outputs, for the oracle leg.  tiled: attend
+    over the tiled cache (every sequence of these workloads starts on a
+    64-token boundary), each pass writing its new keys into it first."""
     from workloads import config
     out = {}
     for name, mode, n_rep, steps in OTHER_CONFIGS:
@@ -180,20 +182,39 @@ def other_configs(torch, msa, dev, keep=None):
         shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
         batch = msa.Batch(case.seq_lens, case.rows, device=dev)
         fused = mode == "decode"
-        o = msa.run_path(shape, batch, base, mode, fused=fused)
+        use_tiles = tiled and all(k0 % 64 == 0 for k0 in case.kv_start)
+        new_keys = [(k0 + L - n, k0 + L) for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows)]
+        if use_tiles:
+            for t in reps:
+                t["kvt"] = msa.KVTiled.empty(t["k"].shape[0], case.n_kv_heads, dev)
+                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"])
+        o = msa.run_path(shape, batch, base, mode, fused=fused, kvt=base.get("kvt"))
+
+        def write(t):   # one token range, or every sequence's new keys in one launch
+            if len(new_keys) == 1:
+                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"], *new_keys[0])
+            else:
+                msa.msa_pack_kv_tiled_rows(shape, batch, t["k"], t["v"], t["kvt"])
 
         def calls(t):
+            c = [("write_cache", lambda: write(t))] if use_tiles else []
             if fused:
-                c = [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
+                c += [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
                                                                    o["block_idx"], o["select_workspace"]))]
             else:
-                c = [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
-                                                                   o["block_scores"])),
+                c += [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
+                                                                    o["block_scores"])),
                      ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
                                                                      o["block_idx"]))]
-            if mode == "prefill":
+            if mode == "prefill" and use_tiles:
+                c.append(("attention", lambda: msa.msa_prefill_tiled(shape, batch, t["q"], t["kvt"], o["block_idx"],
+                                                                     o["out"], o["lse"])))
+            elif mode == "prefill":
                 c.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
                                                                o["out"], o["lse"])))
+            elif use_tiles:
+                c.append(("attention", lambda: msa.msa_decode_tiled(shape, batch, t["q"], t["kvt"], o["block_idx"],
+                                                                    o["out"], o["lse"], o["workspace"])))
             else:
                 c.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
                                                               o["out"], o["lse"], o["workspace"])))
@@ -215,6 +236,7 @@ def other_configs(torch, msa, dev, keep=None):
         total = sum(kms.values())
         total_median = sum(q[1] for q in kq.values())
         ent = {"mode": mode, "rows": case.total_rows, "seq_lens": case.seq_lens, "kv_heads": case.n_kv_heads,
+               "kv_cache": "bf16, tiled (new keys written in each pass)" if use_tiles else "bf16, strided",
                "replicas": n_rep, "steps": steps, "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
                "ms_median": total_median, "rows_per_s_median": case.total_rows / (total_median * 1e-3),
                "kernels": {k: {"ms": v, "ms_p10": kq[k][0], "ms_median": kq[k][1], "ms_p90": kq[k][2]}
@@ -628,7 +650,7 @@ def main():
     }
     if not args.no_others:
         kept = {} if not args.no_cpu_baseline else None
-        res["other_configs"] = other_configs(torch, msa, dev, keep=kept)
+        res["other_configs"] = other_configs(torch, msa, dev, keep=kept, tiled=tiled)
     if not args.no_peaks:
         peaks = measured_peaks(torch, msa, dev)
         res["measured_peaks"] = peaks

@@ -44,7 +44,7 @@ class _BatchC(ctypes.Structure):
 
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
            "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
-           "msa_pack_kv_tiled", "msa_prefill_tiled", "msa_decode_tiled",
+           "msa_pack_kv_tiled", "msa_pack_kv_tiled_rows", "msa_prefill_tiled", "msa_decode_tiled",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
            "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_mfma")
 
@@ -81,10 +81,12 @@ def lib():
             L.msa_decode_kv8.argtypes = [SP, BP, vp, KP, vp, vp, vp, vp, ctypes.c_size_t, vp]
             TP = ctypes.POINTER(_KVTiledC)
             L.msa_pack_kv_tiled.argtypes = [SP, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp]
+            L.msa_pack_kv_tiled_rows.argtypes = [SP, BP, vp, vp, i64, i64, vp, vp, i64, i64, vp]
             L.msa_prefill_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
             L.msa_decode_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp, ctypes.c_size_t, vp]
             for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
                       "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8", "msa_pack_kv_tiled",
+                      "msa_pack_kv_tiled_rows",
                       "msa_prefill_tiled", "msa_decode_tiled"):
                 getattr(L, n).restype = ctypes.c_int
             for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
@@ -385,6 +387,22 @@ def msa_pack_kv_tiled(shape: Shape, k, v, tiles: KVTiled, tok_begin: int = 0, to
     _check(lib().msa_pack_kv_tiled(ctypes.byref(shape), int(tok_begin), int(tok_end), _ptr(k), _ptr(v), tok, head,
                                    ctypes.c_void_p(c.k), ctypes.c_void_p(c.v), c.block_stride, c.head_stride,
                                    _stream(stream)))
+
+
+def msa_pack_kv_tiled_rows(shape: Shape, batch: Batch, k, v, tiles: KVTiled, stream=None):
+    """Write the batch's own keys (each sequence's last rows_s tokens) from the
+    strided cache (k, v: [tokens, H, 128]) into their tiles, in one launch."""
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(v, torch.bfloat16, "v", contiguous=False)
+    tok, head = _strides_tok_head(k, "k")
+    if _strides_tok_head(v, "v") != (tok, head):
+        raise ValueError("k and v must share strides")
+    if k.shape[1] != tiles.k.shape[1] or (k.shape[0] + 63) // 64 > tiles.k.shape[0]:
+        raise ValueError("the tiles do not cover k's tokens or key heads")
+    c = tiles.c
+    _check(lib().msa_pack_kv_tiled_rows(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(k), _ptr(v), tok, head,
+                                        ctypes.c_void_p(c.k), ctypes.c_void_p(c.v), c.block_stride, c.head_stride,
+                                        _stream(stream)))
 
 
 def msa_prefill_tiled(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out, lse=None, stream=None):

@@ -470,6 +470,33 @@ int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end
     return launched(msa::launch_pack_kv_tiled(a, static_cast<hipStream_t>(stream)), "pack_kv_tiled");
 }
 
+int msa_pack_kv_tiled_rows(const msa_shape *shape, const msa_batch *batch, const void *k, const void *v,
+                           int64_t kv_tok_stride, int64_t kv_head_stride, void *k_tiles, void *v_tiles,
+                           int64_t block_stride, int64_t head_stride, void *stream) {
+    int rc;
+    bool empty = false;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
+    if (empty) return ok();
+    const int H = shape->n_kv_heads;
+    if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, H))) return rc;
+    if ((rc = check_tiles(k_tiles, v_tiles, block_stride, head_stride, H))) return rc;
+    if ((int64_t)batch->total_rows * H * 64 / 256 > (int64_t)0x7fffffff)
+        return fail(MSA_ERR_UNSUPPORTED, "batch too large for one call");
+    if ((rc = check_device())) return rc;
+    msa::PackRowsArgs a;
+    a.b = to_dev(batch);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.tok = kv_tok_stride;
+    a.head = kv_head_stride;
+    a.kt = static_cast<uint16_t *>(k_tiles);
+    a.vt = static_cast<uint16_t *>(v_tiles);
+    a.t_blk = block_stride;
+    a.t_head = head_stride;
+    a.H = H;
+    return launched(msa::launch_pack_kv_rows(a, static_cast<hipStream_t>(stream)), "pack_kv_tiled_rows");
+}
+
 int msa_quantize_kv8(const msa_shape *shape, int64_t n_tokens, const void *x, int64_t tok_stride,
                      int64_t head_stride, int8_t *codes, int64_t code_tok_stride, int64_t code_head_stride,
                      float *scales, int64_t scale_tok_stride, int64_t scale_head_stride, void *stream) {

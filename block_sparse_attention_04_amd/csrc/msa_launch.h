@@ -111,11 +111,22 @@ struct PackTiledArgs {
     int H;
 };
 
+// Tiled cache writer for a batch's own keys (key p of every row).
+struct PackRowsArgs {
+    BatchDev b;
+    const uint16_t *k, *v;
+    int64_t tok, head;
+    uint16_t *kt, *vt;
+    int64_t t_blk, t_head;
+    int H;
+};
+
 // Sets the message msa_last_error() returns (empty for success) and returns status.
 int report(int status, const char *msg);
 
 hipError_t launch_quantize_kv8(const QuantArgs &a, hipStream_t st);
 hipError_t launch_pack_kv_tiled(const PackTiledArgs &a, hipStream_t st);
+hipError_t launch_pack_kv_rows(const PackRowsArgs &a, hipStream_t st);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);

@@ -282,6 +282,18 @@ int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end
                       void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
                       void *stream);
 
+/*
+ * Write the batch's own keys -- the key at every row's position p, i.e. each
+ * sequence's last rows_s tokens, numbered through kv_start or the page table
+ * as in msa_prefill -- from a strided bf16 cache into their tiles, in one
+ * launch for the whole batch (a decode step's new keys, one per sequence).
+ * Strides and errors as msa_pack_kv_tiled; batch errors as msa_prefill.
+ */
+int msa_pack_kv_tiled_rows(const msa_shape *shape, const msa_batch *batch,
+                           const void *k, const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
+                           void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
+                           void *stream);
+
 /* msa_prefill over a tiled cache (other arguments and errors as msa_prefill). */
 int msa_prefill_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
                       const int32_t *block_idx, void *out, float *lse, void *stream);

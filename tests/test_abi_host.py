@@ -243,3 +243,9 @@ def test_tiled_cache_checks():
     assert pack(-1, 5) == -1
     assert pack(0, 100, tok=64) == -1 and "kv strides" in _err()
     assert pack(0, 100, bs=8) == -1 and "tile" in _err()
+    rows = lambda k=4096, kt=1 << 20: L.msa_pack_kv_tiled_rows(
+        ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(k) if k else None, ctypes.c_void_p(8192), 256, 128,
+        ctypes.c_void_p(kt) if kt else None, ctypes.c_void_p(1 << 21), 2 * 8192, 8192, None)
+    assert rows(k=0) == -1 and "NULL" in _err()
+    assert rows(kt=0) == -1 and "tiles" in _err()
+    assert rows() in (0, -4)                                        # valid: only the device check may fail

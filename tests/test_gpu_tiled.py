@@ -157,3 +157,37 @@ def test_decode_step_appends_one_token():
     dense = run(case, t, msa.Batch(case.seq_lens, case.rows), "decode")
     for n in ("block_idx", "out", "lse"):
         assert torch.equal(dense[n], got[n]), n
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_pack_rows_writes_the_rows_keys(layout):
+    """msa_pack_kv_tiled_rows writes exactly the batch's own keys: tiles packed
+    from a cache whose row keys are zeroed, then given the rows' keys, equal
+    tiles packed whole from the real cache."""
+    kw = CASES["window"]
+    case = make_case("rows", **kw)
+    t = device_tensors(case)
+    if layout == "paged":
+        pool, pt = to_pages(case, seed=12, extra_pages=2)
+        t.update({n: x.cuda() for n, x in pool.items()})
+        batch = msa.Batch(case.seq_lens, case.rows, page_table=pt)
+        tok = lambda s, j: int(pt[s, j // 64]) * 64 + j % 64
+    else:
+        t, starts = aligned_copy(case, t)
+        batch = msa.Batch(case.seq_lens, case.rows, kv_start=starts)
+        tok = lambda s, j: starts[s] + j
+    kz, vz = t["k"].clone(), t["v"].clone()
+    for s, (L, n) in enumerate(zip(case.seq_lens, case.rows)):
+        for j in range(L - n, L):
+            kz[tok(s, j)] = 0
+            vz[tok(s, j)] = 0
+    shape = shape_of(case)
+    T = t["k"].shape[0]
+    want = msa.KVTiled.empty(T, case.n_kv_heads, "cuda", fill=float("nan"))
+    got = msa.KVTiled.empty(T, case.n_kv_heads, "cuda", fill=float("nan"))
+    msa.msa_pack_kv_tiled(shape, t["k"], t["v"], want)
+    msa.msa_pack_kv_tiled(shape, kz, vz, got)
+    msa.msa_pack_kv_tiled_rows(shape, batch, t["k"], t["v"], got)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(got.k), u16(want.k))
+    assert np.array_equal(u16(got.v), u16(want.v))
