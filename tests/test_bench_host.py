@@ -36,6 +36,14 @@ def test_algorithmic_work_of_the_long_row():
     assert w["attention"]["bytes"] >= 16 * 64 * 4 * 256 * 2
 
 
+def test_cache_write_bytes():
+    """A step's cache write reads and writes each new key's K and V once:
+    rows x key heads x (128 bf16 of K + 128 of V) x (read + write)."""
+    for name, rows in (("chunk", 4096), ("long", 1)):
+        w = bench.algorithmic_work(config(name))
+        assert w["write_cache"] == {"flops": 0, "bytes": rows * 4 * (256 + 256) * 2}
+
+
 @pytest.fixture(scope="module")
 def small():
     c = make_case("v", [3000], [200], 2, seed=5)
