@@ -464,7 +464,7 @@ int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end
     a.tok_end = tok_end;
     a.n_blocks = (tok_end - 1) / 64 - tok_begin / 64 + 1;
     a.H = H;
-    if (a.n_blocks * H > (int64_t)0x7fffffff)
+    if (a.n_blocks * H * 2 > (int64_t)0x7fffffff)
         return fail(MSA_ERR_UNSUPPORTED, "token range too large for one call");
     if ((rc = check_device())) return rc;
     return launched(msa::launch_pack_kv_tiled(a, static_cast<hipStream_t>(stream)), "pack_kv_tiled");

@@ -53,49 +53,49 @@ __global__ __launch_bounds__(256) void quantize_kv8_kernel(QuantArgs a) {
 //      dims 32*s + 8*(lane/16) + 0..7 (the attention's QK^T A operands);
 //   V: q = 64*dt + lane -> dim 16*dt + lane%16 of keys 32c + 4*(lane/16) + 0..3,
 //      then 32c + 16 + 4*(lane/16) + 0..3 (its PV A operands).
-// One workgroup per (block, key head) tile pair.  K pieces are 16-byte copies;
-// the block's V rows are first staged in LDS with coalesced 16-byte loads,
-// then each V piece gathers its 8 keys of one dim from there.  Pieces (for V,
-// elements) of tokens outside the range are left as they are.
+// One workgroup per (block, key head, 32-key chunk).  K pieces are 16-byte
+// copies; the chunk's V rows are first staged in LDS with coalesced 16-byte
+// loads, then each V piece gathers its 8 keys of one dim from there.  Pieces
+// (for V, elements) of tokens outside the range are left as they are.
 constexpr int kPackRow = 128 + 8;   // staged V row (elements), padded against bank conflicts
 
 __global__ __launch_bounds__(256) void pack_kv_tiled_kernel(PackTiledArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t vs[64 * kPackRow];
-    const int g = blockIdx.x % a.H;
-    const int64_t tb = a.tok_begin / 64 + blockIdx.x / a.H;   // the tile's block
-    const int64_t key0 = tb * 64;                             // token of its first key
-    const int64_t tile = tb * a.t_blk + (int64_t)g * a.t_head;
+    __shared__ __attribute__((aligned(16))) uint16_t vs[32 * kPackRow];
+    const int c = blockIdx.x & 1;                             // the chunk of the tile
+    const int64_t bh = blockIdx.x >> 1;
+    const int g = (int)(bh % a.H);
+    const int64_t tb = a.tok_begin / 64 + bh / a.H;           // the tile's block
+    const int64_t key0 = tb * 64 + 32 * c;                    // token of the chunk's first key
+    const int64_t chunk = tb * a.t_blk + (int64_t)g * a.t_head + 4096 * c;
     auto in_range = [&](int64_t t) { return t >= a.tok_begin && t < a.tok_end; };
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
         const int i = r * 256 + threadIdx.x;
-        // V row `key`, 16-byte unit pc, into LDS
+        // V row `key` of the chunk, 16-byte unit pc, into LDS
         const int key = i >> 4, pc = i & 15;
-        const int64_t t = key0 + key;
-        if (in_range(t))
+        if (in_range(key0 + key))
             *reinterpret_cast<u32x4 *>(vs + key * kPackRow + 8 * pc) =
-                load16(a.v + t * a.tok + (int64_t)g * a.head + 8 * pc);
-        // K piece i: chunk c, operand (mt, s), lane
-        const int c = i >> 9, mt = (i >> 8) & 1, s = (i >> 6) & 3, lane = i & 63;
-        const int64_t tk = key0 + 32 * c + 16 * mt + (lane & 15);
+                load16(a.v + (key0 + key) * a.tok + (int64_t)g * a.head + 8 * pc);
+        // K piece i of the chunk: operand (mt, s), lane
+        const int mt = (i >> 8) & 1, s = (i >> 6) & 3, lane = i & 63;
+        const int64_t tk = key0 + 16 * mt + (lane & 15);
         if (in_range(tk))
-            *reinterpret_cast<u32x4 *>(a.kt + tile + 8 * i) =
+            *reinterpret_cast<u32x4 *>(a.kt + chunk + 8 * i) =
                 load16(a.k + tk * a.tok + (int64_t)g * a.head + 32 * s + 8 * (lane >> 4));
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        // V piece q: chunk c, d-tile dt, lane
+    for (int r = 0; r < 2; ++r) {
+        // V piece q of the chunk: d-tile dt, lane
         const int q = r * 256 + threadIdx.x;
-        const int c = q >> 9, lane = q & 63, lg = lane >> 4;
+        const int lane = q & 63, lg = lane >> 4;
         const int dim = 16 * ((q >> 6) & 7) + (lane & 15);
-        const int k_lo = 32 * c + 4 * lg, k_hi = k_lo + 16;   // keys of elements 0..3 and 4..7
+        const int k_lo = 4 * lg, k_hi = k_lo + 16;              // keys of elements 0..3 and 4..7
         const bool lo_in = in_range(key0 + k_lo) && in_range(key0 + k_lo + 3);
         const bool hi_in = in_range(key0 + k_hi) && in_range(key0 + k_hi + 3);
         auto meets = [&](int k) { return key0 + k < a.tok_end && key0 + k + 3 >= a.tok_begin; };
-        const bool any_in = meets(k_lo) || meets(k_hi);
-        if (!any_in) continue;
-        uint16_t *dst = a.vt + tile + 8 * q;
+        if (!meets(k_lo) && !meets(k_hi)) continue;
+        uint16_t *dst = a.vt + chunk + 8 * q;
         u32x4 w = lo_in && hi_in ? zero16() : load16(dst);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void pack_kv_tiled_kernel(PackTiledArgs a) {
 }
 
 hipError_t launch_pack_kv_tiled(const PackTiledArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(pack_kv_tiled_kernel, dim3((unsigned)(a.n_blocks * a.H)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(pack_kv_tiled_kernel, dim3((unsigned)(a.n_blocks * a.H * 2)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
