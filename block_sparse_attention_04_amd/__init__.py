@@ -45,6 +45,7 @@ class _BatchC(ctypes.Structure):
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
            "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
            "msa_pack_kv_tiled", "msa_pack_kv_tiled_rows", "msa_prefill_tiled", "msa_decode_tiled",
+           "msa_decode_tiled_noalloc",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
            "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_mfma")
 
@@ -84,10 +85,11 @@ def lib():
             L.msa_pack_kv_tiled_rows.argtypes = [SP, BP, vp, vp, i64, i64, vp, vp, i64, i64, vp]
             L.msa_prefill_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
             L.msa_decode_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            L.msa_decode_tiled_noalloc.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
             for n in ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
                       "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8", "msa_pack_kv_tiled",
                       "msa_pack_kv_tiled_rows",
-                      "msa_prefill_tiled", "msa_decode_tiled"):
+                      "msa_prefill_tiled", "msa_decode_tiled", "msa_decode_tiled_noalloc"):
                 getattr(L, n).restype = ctypes.c_int
             for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
                 getattr(L, n).argtypes = [SP, i32]
@@ -427,6 +429,21 @@ def msa_decode_tiled(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out,
     _check(lib().msa_decode_tiled(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
                                   _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # MSA_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def msa_decode_tiled_noalloc(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out, lse=None, stream=None):
+    """msa_decode_tiled with the library's static per-device workspace: the
+    call allocates nothing (calls overlapping in time on one device race)."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(block_idx, torch.int32, "block_idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().msa_decode_tiled_noalloc(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(q), ctypes.byref(kv.c),
+                                          _ptr(block_idx), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: dict | None = None,

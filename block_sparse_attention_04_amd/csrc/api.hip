@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -347,7 +349,7 @@ static int decode_launch(msa::AttnArgs &a, const msa_batch *batch, const msa_sha
     if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
     if ((rc = check_device())) return rc;
     a.ws_count = static_cast<unsigned *>(workspace);
-    a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::decode_count_bytes(units));
+    a.ws_part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::kDecodeCountBytes);
     return launched(msa::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
 }
 
@@ -438,6 +440,91 @@ int msa_decode_tiled(const msa_shape *shape, const msa_batch *batch, const void 
     if (rc) return rc;
     if (empty) return ok();
     return decode_launch(a, batch, shape, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- msa_decode_tiled_noalloc: the decode workspace in a static device array ----
+//
+// `scratch` is this library's decode workspace for callers that cannot
+// allocate: one copy per device, held until the process ends.  In host code
+// its name is only a stand-in for the symbol; the device address of each
+// GPU's copy comes from hipGetSymbolAddress on that device (first call there)
+// and is the only thing ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MSA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxScratchDevices];     // device address of `scratch` per device
+bool g_scratch_clean[kMaxScratchDevices];       // its counters are known to be zero
+
+__global__ void zero_words(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch address (looked up once per device); on the
+// first call there, or after a failed launch, its counters are cleared on
+// `st` first by a fill kernel (not a memset, so the call can be captured).
+int scratch_for_call(hipStream_t st, uint8_t **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MSA_ERR_HIP, "no usable HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<uint8_t *>(ptr);
+        g_scratch_clean[dev] = false;
+    }
+    if (!g_scratch_clean[dev]) {
+        constexpr int n = (int)(msa::kDecodeCountBytes / 4);
+        hipLaunchKernelGGL(zero_words, dim3(1), dim3(n), 0, st, reinterpret_cast<uint32_t *>(g_scratch_ptr[dev]), n);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return fail(MSA_ERR_HIP, "clearing the static workspace failed: %s", hipGetErrorString(e));
+        g_scratch_clean[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSA_OK;
+}
+
+void scratch_mark_dirty() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch_clean[dev] = false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_decode_tiled_noalloc(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
+                             const int32_t *block_idx, void *out, float *lse, void *stream) {
+    static_assert(MSA_DECODE_NOALLOC_SCRATCH_BYTES >= msa::kDecodeCountBytes, "scratch below its counters");
+    msa::AttnArgs a;
+    bool empty = false;
+    int rc = tiled_common(shape, batch, q, kv, block_idx, out, lse, &a, &empty);
+    if (rc) return rc;
+    if (empty) return ok();
+    const int64_t units = (int64_t)batch->total_rows * shape->n_kv_heads;
+    const size_t need = msa::decode_workspace_bytes(units, shape->top_k);
+    if (need > MSA_DECODE_NOALLOC_SCRATCH_BYTES)
+        return fail(MSA_ERR_WORKSPACE, "batch needs %zu bytes of decode workspace, above the %zu-byte static one",
+                    need, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = nullptr;
+    if ((rc = scratch_for_call(st, &ws))) return rc;
+    a.ws_count = reinterpret_cast<unsigned *>(ws);
+    a.ws_part = reinterpret_cast<float *>(ws + msa::kDecodeCountBytes);
+    rc = launched(msa::launch_decode(a, st), "decode_tiled_noalloc");
+    if (rc) scratch_mark_dirty();
+    return rc;
 }
 
 int msa_pack_kv_tiled(const msa_shape *shape, int64_t tok_begin, int64_t tok_end, const void *k, const void *v,

@@ -931,13 +931,12 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Units from which a decode launch takes one workgroup per unit: below, the
-// split over several workgroups per unit spreads a small batch over more CUs;
-// above, the one-workgroup kernel avoids publishing and re-reading partials
-// (measured at top_k 16: split faster at 64 units, 18.3 against 20.2 us; one
-// workgroup faster at 128, 20.9 against 26.7 us, and at the 256 units of four
-// 16-row windows, 23.7 against 42.7 us).
-constexpr int64_t kDecodeUnitKernelMin = 80;
+// kDecodeUnitKernelMin: below it, the split over several workgroups per unit
+// spreads a small batch over more CUs; from it, the one-workgroup kernel
+// avoids publishing and re-reading partials (measured at top_k 16: split
+// faster at 64 units, 18.3 against 20.2 us; one workgroup faster at 128, 20.9
+// against 26.7 us, and at the 256 units of four 16-row windows, 23.7 against
+// 42.7 us).
 
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.b.total_rows * a.H;

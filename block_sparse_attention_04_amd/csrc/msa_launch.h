@@ -80,10 +80,19 @@ inline size_t index_select_workspace_bytes(int64_t n_seqs, int H) {
 // Decode partial: m[16], l[16], acc[16][128] (fp32) for one workgroup's kept blocks.
 constexpr int kPartialFloats = 16 + 16 + 16 * 128;
 inline int decode_wg_per_unit(int top_k) { return (top_k + 3) / 4; }
-// Workspace: counters (one uint32 per unit, region rounded to 256 bytes), then partials.
-inline size_t decode_count_bytes(int64_t units) { return (size_t)((units * 4 + 255) / 256 * 256); }
+// Units from which a decode launch takes one workgroup per unit (no
+// workspace); below it, a unit's slots are split over several workgroups that
+// exchange partials through the workspace.
+constexpr int64_t kDecodeUnitKernelMin = 80;
+// Workspace: a fixed region of arrival counters (one uint32 per unit of the
+// split kernel), then the partials.  The counters' place does not depend on
+// the batch, so a workspace reused by batches of other sizes keeps its
+// zeroed counters apart from every partial.
+constexpr size_t kDecodeCountBytes = 512;
+static_assert(kDecodeUnitKernelMin * 4 <= (int64_t)kDecodeCountBytes, "counter region too small");
 inline size_t decode_workspace_bytes(int64_t units, int top_k) {
-    return decode_count_bytes(units) + (size_t)units * decode_wg_per_unit(top_k) * kPartialFloats * sizeof(float);
+    if (units >= kDecodeUnitKernelMin) return kDecodeCountBytes;
+    return kDecodeCountBytes + (size_t)units * decode_wg_per_unit(top_k) * kPartialFloats * sizeof(float);
 }
 
 // int8 cache writer: one bf16 [tokens, H, 128] tensor -> codes + scales.

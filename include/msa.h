@@ -52,7 +52,8 @@
  *
  * Ownership and threading: the caller allocates and owns every buffer,
  * including the decode workspace.  The library allocates nothing, keeps no
- * state between calls, never synchronises the device and only enqueues work
+ * state between calls (msa_decode_tiled_noalloc's static workspace, below, is
+ * the one exception), never synchronises the device and only enqueues work
  * on `stream` (a hipStream_t; NULL is the default stream).  Calls are
  * thread-safe.
  *
@@ -304,8 +305,34 @@ int msa_decode_tiled(const msa_shape *shape, const msa_batch *batch, const void 
                      size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace msa_decode needs for total_rows rows (host
- * function; 0 for an invalid shape). */
+ * function; 0 for an invalid shape).  Batches of 80 or more (row, key head)
+ * units need only the 512-byte counter region; below that, 512 bytes plus
+ * 8,320 bytes per partial (ceil(top_k/4) partials per unit): at most about
+ * 5.3 MB for any batch. */
 size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
+
+/*
+ * msa_decode_tiled for callers that cannot allocate device memory (code
+ * under stream capture, serving loops that forbid allocation): the same
+ * kernels and the same results, bit for bit, with the decode workspace
+ * taken from a static device array of MSA_DECODE_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of a caller buffer.  Each device holds its own
+ * copy from the library's load until the process ends.  The call allocates
+ * nothing; on its first call on a device (and after a failed launch) it
+ * clears the array's counters with a small kernel on `stream` (a kernel, not
+ * a memset).
+ *   Limit: a batch whose msa_decode_workspace_bytes exceeds the array is
+ *   rejected with MSA_ERR_WORKSPACE (with the current kernels no batch
+ *   does: the most any batch needs is about 5.3 MB).
+ *   Concurrency: every call on one device shares that device's array, which
+ *   keeps the last call's contents; calls that overlap in time on one device
+ *   (other streams, other threads) race and give undefined results.
+ * Other arguments and errors as msa_decode_tiled.
+ */
+#define MSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int msa_decode_tiled_noalloc(const msa_shape *shape, const msa_batch *batch, const void *q,
+                             const msa_kv_tiled *kv, const int32_t *block_idx, void *out, float *lse,
+                             void *stream);
 
 /*
  * Step 4 for decode steps and verify windows: the same result as msa_prefill
@@ -320,12 +347,14 @@ size_t msa_decode_workspace_bytes(const msa_shape *shape, int32_t total_rows);
  * only on top_k, so a row's bits do not depend on the other rows: a verify
  * window equals the same rows decoded one at a time, bit for bit.
  *   workspace        device memory of >= msa_decode_workspace_bytes() bytes,
- *                    256-byte aligned.  Its first part holds one arrival
- *                    counter per (row, key head): it must be zero before the
- *                    first call that uses this workspace (allocate it zeroed),
- *                    and every completed call leaves it zero again.  If a
- *                    launch fails, zero it again before reuse.  Calls that
- *                    share a workspace must not run concurrently.
+ *                    256-byte aligned.  Its first 512 bytes hold the
+ *                    arrival counters: they must be zero before the first
+ *                    call that uses this workspace (allocate it zeroed), and
+ *                    every completed call leaves them zero again, whatever
+ *                    the batch size, so one workspace serves batches of any
+ *                    size it covers.  If a launch fails, zero it again before
+ *                    reuse.  Calls that share a workspace must not run
+ *                    concurrently.
  * Other arguments as msa_prefill.
  */
 int msa_decode(const msa_shape *shape, const msa_batch *batch,

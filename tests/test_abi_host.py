@@ -121,12 +121,17 @@ def test_decode_workspace_size_and_checks():
     sh = msa.make_shape(4, top_k=16)
     # one partial (max, sum, values of 16 heads x 128) per workgroup of four kept
     # blocks, ceil(top_k / 4) per (row, key head)
+    # blocks, ceil(top_k / 4) per (row, key head), after a fixed 512-byte
+    # counter region; from 80 units on (one workgroup per unit) only the counters
     per_unit = 4 * (16 + 16 + 16 * 128) * 4
-    counters = lambda units: (units * 4 + 255) // 256 * 256
-    assert msa.msa_decode_workspace_bytes(sh, 3) == counters(12) + 12 * per_unit
-    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 256 + 4 * 2080 * 4
-    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=5), 1) == 256 + 4 * 2 * 2080 * 4
+    assert msa.msa_decode_workspace_bytes(sh, 3) == 512 + 12 * per_unit
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=1), 1) == 512 + 4 * 2080 * 4
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=5), 1) == 512 + 4 * 2 * 2080 * 4
     assert msa.msa_decode_workspace_bytes(msa.make_shape(4, top_k=40), 1) == 0
+    assert msa.msa_decode_workspace_bytes(sh, 19) == 512 + 76 * per_unit      # 76 units: split
+    assert msa.msa_decode_workspace_bytes(sh, 20) == 512                      # 80 units: one workgroup each
+    # the largest any batch needs (79 units at top_k 32) fits the static workspace
+    assert msa.msa_decode_workspace_bytes(msa.make_shape(79, top_k=32), 1) <= msa.NOALLOC_SCRATCH_BYTES
     b = FakeBatch(total_rows=4)
     need = msa.msa_decode_workspace_bytes(sh, 4)
     args = lambda ws, nbytes, hs=128, out=65536: (
@@ -249,3 +254,24 @@ def test_tiled_cache_checks():
     assert rows(k=0) == -1 and "NULL" in _err()
     assert rows(kt=0) == -1 and "tiles" in _err()
     assert rows() in (0, -4)                                        # valid: only the device check may fail
+
+
+def test_decode_noalloc_argument_checks():
+    """msa_decode_tiled_noalloc validates like msa_decode_tiled before it
+    touches the device (its static workspace is looked up only afterwards)."""
+    L = msa.lib()
+    sh = msa.make_shape(4, top_k=16)
+    b = FakeBatch(total_rows=4)
+    kv = msa._KVTiledC(1 << 20, 2 << 20, 8192 * 4, 8192)
+    call = lambda q=4096, kvp=ctypes.byref(kv), idx=32768, out=65536: L.msa_decode_tiled_noalloc(
+        ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(q) if q else None, kvp,
+        ctypes.c_void_p(idx) if idx else None, ctypes.c_void_p(out) if out else None, None, None)
+    assert call(q=0) == -1 and "NULL" in _err()
+    assert call(kvp=None) == -1 and "kv" in _err()
+    assert call(out=0) == -1
+    assert call(q=4096 + 8) == -1 and "aligned" in _err()
+    bad = msa._KVTiledC(1 << 20, 2 << 20, 8192 * 4, 4096)     # head stride overlaps a tile
+    assert call(kvp=ctypes.byref(bad)) == -1 and "tile strides" in _err()
+    assert L.msa_decode_tiled_noalloc(ctypes.byref(msa.make_shape(4, top_k=33)), ctypes.byref(b.c),
+                                      ctypes.c_void_p(4096), ctypes.byref(kv), ctypes.c_void_p(32768),
+                                      ctypes.c_void_p(65536), None, None) == -2
