@@ -1,6 +1,6 @@
 """Benchmark of the MSA hot path on one MI355X.
 
-One step = the whole path on the two workloads the metric is quoted on:
+Headline step = the whole path on the two workloads the metric is quoted on:
   chunk: one 4,096-row prompt chunk on a 65,536-token cached prefix (69,632
          keys), 4 key heads x 16 query heads: the chunk's 4,096 new keys
          written into the tiled cache (msa_pack_kv_tiled) -> index scores ->
@@ -14,20 +14,34 @@ The key/value cache is the library's tiled bf16 layout (the cached prefix
 is packed before timing, as earlier steps would have written it; each step
 writes its own new keys); --kv-layout strided attends over the plain
 [tokens, heads, 128] cache instead (msa_prefill / msa_decode, no cache write).
-value = rows per second of the step (4,097 rows).  Inputs are resident in HBM
-before timing; the timed region enqueues K steps back to back, bracketed by a
-device synchronisation on both sides.  Inputs rotate over replicas so the
-256 MB Infinity Cache cannot hold a whole step's working set.
+value = rows per second of the headline step (4,097 rows).  Inputs are
+resident in HBM before timing; the timed region enqueues K steps back to
+back, bracketed by a device synchronisation on both sides.  Inputs rotate
+over replicas so the 256 MB Infinity Cache cannot hold a step's working set.
+The long row's calls run on a second stream, each step's starting when the
+chunk's part of the same step starts (beside the chunk's cache write,
+indexer and selection, not its attention).
 
-Every library call is bracketed by HIP events recorded on the stream the
-library launches on (torch's current stream), so per-kernel average durations
-come from the same timed region; the dominant kernel's duration gives the
-roofline entry.  The oracle (CPU) is timed on a bounded sample of the same
-workloads as a reported baseline.
+Per configuration (`configs`): each of the five named workloads (2,048-row
+prefill, batched decode, the chunk, the long row, the verify windows) alone,
+as a loop of back-to-back steps on one stream with one HIP-event pair per
+block of steps: mean, p10 / median / p90 per step, rows/s, and the fraction
+of the roofline over the whole path (MFMA for prompt chunks, HBM for decode
+shapes, algorithmic bytes counted from the distinct (sequence, key head,
+block) triples of the run's own selection).  prefill_rows_per_s and
+decode_rows_per_s come from the chunk's and the long row's loops.  A separate
+untimed pass with an event pair around every library call gives the
+per-kernel breakdown.
+
+The dominant kernel (the chunk attention) is also bracketed by HIP events in
+the headline's timed steps; its mean there gives the roofline entry.  The
+oracle (CPU) is timed on a bounded sample of the same workloads as a
+reported baseline, and its results check the run's own outputs.
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
 import gc
 import json
 import math
@@ -41,12 +55,41 @@ sys.path.insert(0, ROOT)
 METRIC = "MSA prefill rows/s + decode rows/s at 64K–256K ctx; % of MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3   # FLOP per byte
 
 
-def algorithmic_work(case, kv8=False):
+def kept_kv_bytes(case, block_idx=None, kv_bytes_per_key=None):
+    """K and V bytes of the distinct kept blocks: each (sequence, key head,
+    block) that any row keeps counts once, with the keys of it that the
+    sequence's last row can see.  block_idx: the run's own selection (int32
+    [rows, H, top_k]); without it, an upper bound (every causal block kept
+    by some row when a sequence has >= 64 rows, else top_k per row)."""
+    import numpy as np
+    B, H = case.block, case.n_kv_heads
+    per_key = kv_bytes_per_key or case.head_dim * 2 * 2       # K and V, bf16
+    total = 0
+    for s, (L, n) in enumerate(zip(case.seq_lens, case.rows)):
+        nb_last = (L - 1) // B + 1
+        if block_idx is None:
+            blocks = nb_last if n >= 64 else min(nb_last, case.top_k * n)
+            full = blocks * B - (nb_last * B - L if blocks == nb_last else 0)
+            total += full * per_key * H
+            continue
+        r0 = case.cu_rows[s]
+        sel = np.asarray(block_idx[r0:r0 + n])
+        for g in range(H):
+            kept = np.unique(sel[:, g, :])
+            kept = kept[kept >= 0]
+            keys = np.minimum(B, L - kept * B)
+            total += int(keys.sum()) * per_key
+    return total
+
+
+def algorithmic_work(case, kv8=False, block_idx=None):
     """Per-launch algorithmic FLOPs and bytes of each step for one workload
-    (kv8: the int8 cache, 128 + 4 bytes per key and key head for K and for V;
-    write_cache: the step's new keys' K and V read once and written once)."""
+    (kv8: the int8 cache, 128 + 4 bytes per key and key head for K and for
+    V; write_cache: the step's new keys' K and V read once and written
+    once; block_idx: the run's selection, for the distinct kept blocks)."""
     import numpy as np
     H, G, D, dI, B, k = case.n_kv_heads, case.group, case.head_dim, case.index_dim, case.block, case.top_k
     pairs = 0           # causal (row, key) pairs per key head
@@ -70,24 +113,35 @@ def algorithmic_work(case, kv8=False):
     w["index_select"] = dict(flops=w["index_scores"]["flops"],
                              bytes=w["index_scores"]["bytes"] + rows * H * k * 4)
     attn_bytes = rows * H * G * D * 2 * 2 + rows * H * k * 4     # q in, out
-    # kept K/V blocks, counted once per distinct (sequence, key head, block)
-    attn_bytes += kept_kv_bytes(case) * (132 if kv8 else 256) // 256
+    attn_bytes += kept_kv_bytes(case, block_idx, (D + 4) * 2 if kv8 else None)
     w["attention"] = dict(flops=4 * D * kept * H * G, bytes=attn_bytes)
     w["write_cache"] = dict(flops=0, bytes=rows * H * D * 2 * 2 * 2)
     return w
 
 
-def kept_kv_bytes(case):
-    """Distinct K/V bytes a perfect cache would read: for the chunk every
-    block below its last row is kept by some row, so K and V are read whole;
-    for a single row, its 16 blocks."""
-    total = 0
-    B, k = case.block, case.top_k
-    for L, n in zip(case.seq_lens, case.rows):
-        nb_last = (L - 1) // B + 1
-        blocks = nb_last if n >= 64 else min(nb_last, k * n)
-        total += blocks * B * case.head_dim * 2 * 2 * case.n_kv_heads
-    return total
+def path_work(work, steps):
+    """FLOPs and bytes of a whole step: the sum over the path's calls."""
+    return {"flops": sum(work[s]["flops"] for s in steps), "bytes": sum(work[s]["bytes"] for s in steps)}
+
+
+def bound_of(wk):
+    return "mfma" if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > RIDGE else "hbm"
+
+
+def fraction(wk, ms, measured=None):
+    """Achieved rate of work wk in ms against its bound's published peak (and
+    the measured one, if given)."""
+    if bound_of(wk) == "mfma":
+        ach = wk["flops"] / (ms * 1e-3) / 1e12
+        out = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS)
+        if measured:
+            out["frac_of_measured"] = ach / measured["bf16_mfma_TFLOPs"]
+    else:
+        ach = wk["bytes"] / (ms * 1e-3) / 1e9
+        out = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS)
+        if measured:
+            out["frac_of_measured"] = ach / measured["hbm_read_GBs"]
+    return out
 
 
 PROFILE_KERNELS = {"chunk/attention": "prefill_kernel", "chunk/index_scores": "index_scores_tiled",
@@ -151,143 +205,241 @@ class Timed:
 
     def quantiles_ms(self):
         """(p10, median, p90) of each call's event times."""
-        out = {}
-        for k, v in self.ev.items():
-            ts = sorted(a.elapsed_time(b) for a, b in v)
-            at = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
-            out[k] = (at(0.1), at(0.5), at(0.9))
-        return out
+        return {k: quantiles([a.elapsed_time(b) for a, b in v]) for k, v in self.ev.items()}
 
 
-# The other named workloads: (name, mode, input replicas rotated so the 256 MB
-# Infinity Cache cannot hold a call's working set across calls, timed passes).
-OTHER_CONFIGS = (("tiny", "prefill", 1, 50), ("decode", "decode", 8, 200), ("windows", "decode", 3, 200))
+def quantiles(xs):
+    ts = sorted(xs)
+    at = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+    return at(0.1), at(0.5), at(0.9)
 
 
-def other_configs(torch, msa, dev, keep=None, tiled=True):
-    """The other named workloads, for reference beside the headline line (not
-    part of `value`): the 2,048-token prefill, the batched decode of 4 x 32,768
-    keys and the four 16-row verify windows, each timed per library call with
-    HIP events (mean and p10 / median / p90 over the timed passes, after two
-    warm-up passes per replica).  keep: a dict that receives each workload's
-    case and host copies of its outputs, for the oracle leg.  tiled: attend
-    over the tiled cache (every sequence of these workloads starts on a
-    64-token boundary), each pass writing its new keys into it first."""
-    from workloads import config
-    out = {}
-    for name, mode, n_rep, steps in OTHER_CONFIGS:
-        case = config(name)
+class Workload:
+    """One named workload on the device: input replicas (rotated so the
+    Infinity Cache cannot hold a step's working set), the tiled cache of each
+    replica with its prefix packed, output buffers, and the library calls of
+    one step."""
+
+    def __init__(self, torch, msa, dev, name, case, mode, n_rep, *, fused, tiled=True, paged=False,
+                 head_major=False, kv8=False):
+        self.name, self.case, self.mode, self.fused = name, case, mode, fused
+        self.kv8, self.msa = kv8, msa
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
-        reps = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(n_rep - 1)]
-        shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
-        batch = msa.Batch(case.seq_lens, case.rows, device=dev)
-        fused = mode == "decode"
-        use_tiles = tiled and all(k0 % 64 == 0 for k0 in case.kv_start)
-        new_keys = [(k0 + L - n, k0 + L) for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows)]
-        if use_tiles:
-            for t in reps:
+        if head_major:
+            for n in ("k", "v", "ik"):
+                base[n] = base[n].permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        page_table = None
+        if paged:
+            from workloads import to_pages
+            pool, page_table = to_pages(case, seed=7)
+            base.update({n: x.to(dev) for n, x in pool.items()})
+        self.inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(n_rep - 1)]
+        self.shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
+        if kv8:
+            for t in self.inputs:
+                kc, ks = msa.msa_quantize_kv8(self.shape, t["k"])
+                vc, vs = msa.msa_quantize_kv8(self.shape, t["v"])
+                t["kv8"] = msa.KV8(kc, vc, ks, vs)
+                del t["k"], t["v"]
+        self.tiled = tiled and not kv8 and (paged or all(k0 % 64 == 0 for k0 in case.kv_start))
+        if self.tiled:
+            for t in self.inputs:   # the cached prefix, written before timing (set-up)
                 t["kvt"] = msa.KVTiled.empty(t["k"].shape[0], case.n_kv_heads, dev)
-                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"])
-        o = msa.run_path(shape, batch, base, mode, fused=fused, kvt=base.get("kvt"))
+                msa.msa_pack_kv_tiled(self.shape, t["k"], t["v"], t["kvt"])
+        self.batch = msa.Batch(case.seq_lens, case.rows, device=dev, page_table=page_table)
+        # the paged pools' new keys are not one token range per sequence:
+        # there the whole pool is packed before timing and the steps write nothing
+        self.write = self.tiled and not paged
+        self.new_keys = [(k0 + L - n, k0 + L) for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows)]
+        self.o = msa.run_path(self.shape, self.batch, self.inputs[0], mode, fused=fused,
+                              kv8=self.inputs[0].get("kv8"), kvt=self.inputs[0].get("kvt"))
+        self.steps = ((("write_cache",) if self.write else ()) +
+                      (("index_select",) if fused else ("index_scores", "select_blocks")) + ("attention",))
 
-        def write(t):   # one token range, or every sequence's new keys in one launch
-            if len(new_keys) == 1:
-                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"], *new_keys[0])
+    @property
+    def kv_cache(self):
+        if self.kv8:
+            return "int8 codes + fp32 scale per (token, key head)"
+        if self.tiled:
+            return ("bf16, tiled (64-key tiles in matrix-core operand order; each step writes its new keys "
+                    "into it)" if self.write else "bf16, tiled (pool packed before timing)")
+        return "bf16, strided"
+
+    def calls(self, i):
+        """[(step name, callable)] of step i (replica i mod the replicas)."""
+        msa, sh, b, o = self.msa, self.shape, self.batch, self.o
+        t = self.inputs[i % len(self.inputs)]
+        c = []
+        if self.write:
+            if len(self.new_keys) == 1:
+                t0, t1 = self.new_keys[0]
+                c.append(("write_cache", lambda: msa.msa_pack_kv_tiled(sh, t["k"], t["v"], t["kvt"], t0, t1)))
             else:
-                msa.msa_pack_kv_tiled_rows(shape, batch, t["k"], t["v"], t["kvt"])
+                c.append(("write_cache", lambda: msa.msa_pack_kv_tiled_rows(sh, b, t["k"], t["v"], t["kvt"])))
+        if self.fused:
+            c.append(("index_select", lambda: msa.msa_index_select(sh, b, t["iq"], t["ik"], o["block_scores"],
+                                                                   o["block_idx"], o["select_workspace"])))
+        else:
+            c.append(("index_scores", lambda: msa.msa_index_scores(sh, b, t["iq"], t["ik"], o["block_scores"])))
+            c.append(("select_blocks", lambda: msa.msa_select_blocks(sh, b, o["block_scores"], o["block_idx"])))
+        prefill = self.mode == "prefill"
+        if self.kv8:
+            c.append(("attention", (lambda: msa.msa_prefill_kv8(sh, b, t["q"], t["kv8"], o["block_idx"], o["out"],
+                                                                o["lse"])) if prefill else
+                      (lambda: msa.msa_decode_kv8(sh, b, t["q"], t["kv8"], o["block_idx"], o["out"], o["lse"],
+                                                  o["workspace"]))))
+        elif self.tiled:
+            c.append(("attention", (lambda: msa.msa_prefill_tiled(sh, b, t["q"], t["kvt"], o["block_idx"], o["out"],
+                                                                  o["lse"])) if prefill else
+                      (lambda: msa.msa_decode_tiled(sh, b, t["q"], t["kvt"], o["block_idx"], o["out"], o["lse"],
+                                                    o["workspace"]))))
+        else:
+            c.append(("attention", (lambda: msa.msa_prefill(sh, b, t["q"], t["k"], t["v"], o["block_idx"], o["out"],
+                                                            o["lse"])) if prefill else
+                      (lambda: msa.msa_decode(sh, b, t["q"], t["k"], t["v"], o["block_idx"], o["out"], o["lse"],
+                                              o["workspace"]))))
+        return c
 
-        def calls(t):
-            c = [("write_cache", lambda: write(t))] if use_tiles else []
-            if fused:
-                c += [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"],
-                                                                   o["block_idx"], o["select_workspace"]))]
-            else:
-                c += [("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
-                                                                    o["block_scores"])),
-                     ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
-                                                                     o["block_idx"]))]
-            if mode == "prefill" and use_tiles:
-                c.append(("attention", lambda: msa.msa_prefill_tiled(shape, batch, t["q"], t["kvt"], o["block_idx"],
-                                                                     o["out"], o["lse"])))
-            elif mode == "prefill":
-                c.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
-                                                               o["out"], o["lse"])))
-            elif use_tiles:
-                c.append(("attention", lambda: msa.msa_decode_tiled(shape, batch, t["q"], t["kvt"], o["block_idx"],
-                                                                    o["out"], o["lse"], o["workspace"])))
-            else:
-                c.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"], o["block_idx"],
-                                                              o["out"], o["lse"], o["workspace"])))
-            return c
+    def run_step(self, i):
+        for _, fn in self.calls(i):
+            fn()
 
-        timer = Timed(torch)
-        warm = 2 * n_rep
-        gc.disable()   # a collection between an event and its call would show up as kernel time
-        for i in range(steps + warm):
-            for kname, fn in calls(reps[i % n_rep]):
-                if i < warm:
-                    fn()
-                else:
-                    timer.run(kname, fn)
-        torch.cuda.synchronize()
-        gc.enable()
-        kms, kq = timer.mean_ms(), timer.quantiles_ms()
-        work = algorithmic_work(case)
-        total = sum(kms.values())
-        total_median = sum(q[1] for q in kq.values())
-        ent = {"mode": mode, "rows": case.total_rows, "seq_lens": case.seq_lens, "kv_heads": case.n_kv_heads,
-               "kv_cache": "bf16, tiled (new keys written in each pass)" if use_tiles else "bf16, strided",
-               "replicas": n_rep, "steps": steps, "ms": total, "rows_per_s": case.total_rows / (total * 1e-3),
-               "ms_median": total_median, "rows_per_s_median": case.total_rows / (total_median * 1e-3),
-               "kernels": {k: {"ms": v, "ms_p10": kq[k][0], "ms_median": kq[k][1], "ms_p90": kq[k][2]}
-                           for k, v in kms.items()}}
-        for k, v in kms.items():
-            wk = work[k]
-            if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
-                ent["kernels"][k].update(tflops=wk["flops"] / (v * 1e-3) / 1e12,
-                                         frac=wk["flops"] / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
-            else:
-                ent["kernels"][k].update(gbs=wk["bytes"] / (v * 1e-3) / 1e9,
-                                         frac=wk["bytes"] / (v * 1e-3) / 1e9 / PEAK_HBM_GBS)
-        out[name] = ent
-        if keep is not None:
-            keep[name] = (case, {"block_idx": o["block_idx"].cpu().numpy(), "out": o["out"].float().cpu().numpy(),
-                                 "lse": o["lse"].cpu().numpy()})
-        del base, reps, o
-    return out
+    def host_outputs(self):
+        o = self.o
+        return {"block_idx": o["block_idx"].cpu().numpy(), "out": o["out"].float().cpu().numpy(),
+                "lse": o["lse"].cpu().numpy()}
 
 
-# Oracle sample per other workload: rows timed and checked (all rows of the
+def loop_timing(torch, w, steps, block):
+    """w's steps back to back on the current stream after a warm-up of two
+    passes over the replicas: one event pair around the whole loop (the mean
+    per step) and one around each block of `block` steps (p10 / median / p90
+    of the per-step time over the blocks)."""
+    for i in range(2 * len(w.inputs)):
+        w.run_step(i)
+    torch.cuda.synchronize()
+    n_blk = max(1, steps // block)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_blk)]
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.disable()
+    first.record()
+    i = 0
+    for a, b in ev:
+        a.record()
+        for _ in range(block):
+            w.run_step(i)
+            i += 1
+        b.record()
+    last.record()
+    torch.cuda.synchronize()
+    gc.enable()
+    per = [a.elapsed_time(b) / block for a, b in ev]
+    p10, p50, p90 = quantiles(per)
+    return {"steps": i, "steps_per_event_block": block, "ms_mean": first.elapsed_time(last) / i,
+            "ms_p10": p10, "ms_median": p50, "ms_p90": p90}
+
+
+def per_call_timing(torch, w, n_steps):
+    """An untimed pass with an event pair around every call of w's steps:
+    each call's mean and (p10, median, p90); an event pair costs the stream
+    a few microseconds, so short calls read high."""
+    timer = Timed(torch)
+    gc.disable()
+    for i in range(n_steps):
+        for k, fn in w.calls(i):
+            timer.run(k, fn)
+    torch.cuda.synchronize()
+    gc.enable()
+    return timer.mean_ms(), timer.quantiles_ms()
+
+
+# Per configuration: (mode, fused selection, input replicas, back-to-back
+# steps, steps per event block).  Replicas: >= 512 MB rotated where a step's
+# working set would otherwise fit the 256 MB Infinity Cache.
+CONFIG_PLAN = {
+    "tiny": ("prefill", False, 1, 200, 10),
+    "decode": ("decode", True, 8, 400, 10),
+    "chunk": ("prefill", False, 2, 40, 2),
+    "long": ("decode", True, 4, 400, 10),
+    "windows": ("decode", True, 3, 300, 10),
+}
+CONFIG_LETTER = {"tiny": "T", "decode": "D", "chunk": "C", "long": "L", "windows": "W"}
+TARGETS = {"chunk": ("mfma", 0.60), "long": ("hbm", 0.70)}
+
+
+def config_entry(torch, w, steps, block, measured=None, kv8=False):
+    """One configuration alone: back-to-back loop, per-call breakdown, the
+    path's algorithmic work (distinct kept blocks from the run's selection)
+    and its fraction of the roofline."""
+    lt = loop_timing(torch, w, steps, block)
+    kms, kq = per_call_timing(torch, w, min(50, steps))
+    case = w.case
+    work = algorithmic_work(case, kv8=kv8, block_idx=w.o["block_idx"].cpu().numpy())
+    pw = path_work(work, w.steps)
+    rows = case.total_rows
+    ent = {"letter": CONFIG_LETTER.get(w.name), "mode": w.mode, "rows": rows, "seq_lens": case.seq_lens,
+           "kv_heads": case.n_kv_heads, "kv_cache": w.kv_cache, "replicas": len(w.inputs),
+           "path": list(w.steps), **lt,
+           "rows_per_s": rows / (lt["ms_mean"] * 1e-3), "rows_per_s_median": rows / (lt["ms_median"] * 1e-3),
+           "algorithmic_flops": pw["flops"], "algorithmic_bytes": pw["bytes"],
+           "kv_distinct_bytes": kept_kv_bytes(case, w.o["block_idx"].cpu().numpy()),
+           "path_fraction": fraction(pw, lt["ms_mean"], measured),
+           "path_fraction_median": fraction(pw, lt["ms_median"], measured)["frac"],
+           "kernels": {}}
+    for k in w.steps:
+        e = {"ms": kms[k], "ms_p10": kq[k][0], "ms_median": kq[k][1], "ms_p90": kq[k][2],
+             "algorithmic_flops": work[k]["flops"], "algorithmic_bytes": work[k]["bytes"]}
+        e.update({n: v for n, v in fraction(work[k], kms[k], measured).items() if n in ("bound", "achieved",
+                                                                                     "unit", "frac")})
+        ent["kernels"][k] = e
+    ent["kernel_timing"] = (f"event pair around every call in an untimed pass of {min(50, steps)} steps "
+                            f"(each pair costs the stream a few microseconds)")
+    if w.name in TARGETS:
+        b, tgt = TARGETS[w.name]
+        ent["target"] = {"bound": b, "frac": tgt, "met": ent["path_fraction"]["frac"] >= tgt}
+    return ent
+
+
+# Oracle sample per configuration: rows timed and checked (all rows of the
 # small decode batches, a spread of rows elsewhere).
-OTHER_SAMPLES = {"tiny": 64, "decode": None, "windows": 16}
+ORACLE_SAMPLES = {"tiny": 64, "decode": None, "windows": 16, "chunk": 96, "long": None}
 
 
-def other_cpu_baselines(kept, threads):
-    """The oracle on a sample of each other workload: its rows/s on the host
-    cores (scaled to the whole workload) and the same check of the GPU outputs
-    as the headline validation."""
+def oracle_sample(case, name):
     import numpy as np
+    n = ORACLE_SAMPLES.get(name)
+    if n is None or n >= case.total_rows:
+        return np.arange(case.total_rows)
+    if name == "chunk":
+        return np.sort(np.random.default_rng(0).choice(case.total_rows, n, replace=False))
+    return np.unique(np.linspace(0, case.total_rows - 1, n).round().astype(np.int64))
+
+
+def oracle_leg(case, name, threads, gpu=None):
+    """The oracle on the sample of one workload: its rows/s on the host cores
+    (scaled to the whole workload) and, given the GPU's outputs, the check of
+    them."""
     import oracle
-    out = {}
-    for name, (case, gpu) in kept.items():
-        n = OTHER_SAMPLES.get(name)
-        rows = (np.arange(case.total_rows) if n is None or n >= case.total_rows
-                else np.unique(np.linspace(0, case.total_rows - 1, n).round().astype(np.int64)))
-        t0 = time.perf_counter()
-        ref = oracle.run(case, rows=rows, threads=threads)
-        dt = time.perf_counter() - t0
-        per_row = dt / len(rows)
-        out[name] = {"cpu_baseline": {"value": 1.0 / per_row, "unit": "rows/s", "cores": threads, "kind": "oracle",
-                                      "sample": f"{len(rows)} of {case.total_rows} rows ({dt:.2f} s)"},
-                     "validation": validate({name: case}, {name: (rows, ref)}, {name: gpu})[name]}
-    return out
+    rows = oracle_sample(case, name)
+    t0 = time.perf_counter()
+    ref = oracle.run(case, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    out = {"cpu_baseline": {"value": len(rows) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+                            "sample": f"{len(rows)} of {case.total_rows} rows ({dt:.2f} s)"}}
+    if gpu is not None:
+        out["validation"] = validate({name: case}, {name: (rows, ref)}, {name: gpu})[name]
+    return out, (rows, ref, dt)
 
 
 def measured_peaks(torch, msa, dev):
-    """What this device sustains, beside the published peaks: the library's
-    streaming-read kernel over 2 GiB and its loop of independent bf16 MFMA
-    chains (include/msa_peaks.h), each the best of 5 timed launches."""
-    def best_ms(fn, reps=5):
+    """What this device sustains, beside the published peaks.  HBM: the
+    library's streaming-read kernel swept over loads in flight per thread (1
+    to 16), load width (4, 8, 16 bytes), plain or nontemporal loads and
+    workgroups per CU (2 to 32), over 2 GiB, best of 3 launches each (the
+    best variant is the measured floor); the same sweep's best over four
+    rotating 134 MB buffers (the long row's index-key read).  MFMA: a loop of
+    independent bf16 MFMA chains."""
+    def best_ms(fn, reps=3):
         fn()
         torch.cuda.synchronize()
         best = float("inf")
@@ -302,18 +454,47 @@ def measured_peaks(torch, msa, dev):
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
-    t_read = best_ms(lambda: msa.msa_peaks_stream_read(buf, sink))
+    sweep = []
+    for unroll in (1, 2, 4, 8, 16):
+        for width in (4, 8, 16):
+            for nt in (0, 1):
+                for wg in (2, 4, 8, 16, 32):
+                    ms = best_ms(lambda: msa.msa_peaks_stream_read_variant(buf, sink, unroll, width, nt, wg))
+                    sweep.append({"unroll": unroll, "width": width, "nontemporal": nt, "wg_per_cu": wg,
+                                  "GBs": nbytes / (ms * 1e-3) / 1e9})
+    sweep.sort(key=lambda e: -e["GBs"])
+    best = sweep[0]
+    t_default = best_ms(lambda: msa.msa_peaks_stream_read(buf, sink))
     del buf
+    # the long row's read size: 134,217,728 bytes, four rotating buffers
+    small = [torch.ones((128 << 20) // 4, dtype=torch.int32, device=dev) for _ in range(4)]
+    it = {"i": 0}
+
+    def small_read(u, wd, nt, wg):
+        msa.msa_peaks_stream_read_variant(small[it["i"] % 4], sink, u, wd, nt, wg)
+        it["i"] += 1
+    small_sweep = []
+    for e in sweep[:12]:
+        ms = best_ms(lambda: small_read(e["unroll"], e["width"], e["nontemporal"], e["wg_per_cu"]), reps=8)
+        small_sweep.append(dict(e, GBs=(128 << 20) / (ms * 1e-3) / 1e9))
+    small_sweep.sort(key=lambda e: -e["GBs"])
+    del small
     wg, iters = 256 * 8, 4000
     t_mfma = best_ms(lambda: msa.msa_peaks_mfma(sink, wg, iters))
     flops = wg * 4 * iters * 4 * 16384
-    return {"hbm_read_GBs": nbytes / (t_read * 1e-3) / 1e9,
+    return {"hbm_read_GBs": best["GBs"],
+            "hbm_read_frac_of_published": best["GBs"] / PEAK_HBM_GBS,
+            "hbm_read_best_variant": {k: best[k] for k in ("unroll", "width", "nontemporal", "wg_per_cu")},
+            "hbm_read_default_GBs": nbytes / (t_default * 1e-3) / 1e9,
+            "hbm_read_sweep_top": sweep[:8], "hbm_read_sweep_worst": sweep[-3:],
+            "hbm_read_134MB_GBs": small_sweep[0]["GBs"], "hbm_read_134MB_variant": small_sweep[0],
             "bf16_mfma_TFLOPs": flops / (t_mfma * 1e-3) / 1e12,
-            "hbm_read_frac_of_published": nbytes / (t_read * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "bf16_mfma_frac_of_published": flops / (t_mfma * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "sclk": _sclk(),
-            "method": "msa_peaks_stream_read over 2 GiB; msa_peaks_mfma with 2,048 workgroups x 4 waves x "
-                      "4,000 rounds of 4 independent v_mfma_f32_16x16x32_bf16; best of 5 launches each"}
+            "method": "msa_peaks_stream_read_variant over 2 GiB, 150 variants (loads in flight 1-16, width 4/8/16 "
+                      "B, plain/nontemporal, 2-32 workgroups per CU), best of 3 launches each; the top 12 again on "
+                      "four rotating 128 MiB buffers, best of 8; msa_peaks_mfma with 2,048 workgroups x 4 waves x "
+                      "4,000 rounds of 4 independent v_mfma_f32_16x16x32_bf16, best of 3"}
 
 
 def _sclk():
@@ -327,35 +508,6 @@ def _sclk():
         if "sclk" in line:
             return line.split(":", 2)[-1].strip()
     return None
-
-
-def cpu_baseline(cases, threads, gpu=None):
-    """Time the oracle as it stands on a bounded sample: 96 rows of the chunk
-    and the decode row; scale to rows/s of the full step.  With `gpu` (the
-    timed run's outputs on the host), the same oracle results also check them:
-    returns (baseline, validation)."""
-    import numpy as np
-    import oracle
-    chunk, long_ = cases["chunk"], cases["long"]
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(chunk.total_rows, 96, replace=False))
-    t0 = time.perf_counter()
-    ref_chunk = oracle.run(chunk, rows=sample, threads=threads)
-    t_chunk_row = (time.perf_counter() - t0) / len(sample)
-    t0 = time.perf_counter()
-    ref_long = oracle.run(long_, threads=threads)
-    t_long = time.perf_counter() - t0
-    step = t_chunk_row * chunk.total_rows + t_long
-    base = {"value": (chunk.total_rows + long_.total_rows) / step, "unit": "rows/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"96 random rows of the 4,096-row chunk ({t_chunk_row * 1e3:.1f} ms/row) and the "
-                      f"262,144-key decode row ({t_long * 1e3:.0f} ms); step time extrapolated to "
-                      f"4,096 + 1 rows = {step:.1f} s",
-            "cpu": _cpu_model()}
-    if gpu is None:
-        return base, None
-    return base, validate(cases, {"chunk": (sample, ref_chunk), "long": (np.arange(long_.total_rows), ref_long)},
-                          gpu)
 
 
 # Tolerances of the parity tests: selection exact outside the near-tie band,
@@ -387,14 +539,30 @@ def validate(cases, refs, gpu):
     return out
 
 
-def _cpu_model():
+def host_cpu():
+    """The host's CPU as the OS reports it: model, logical CPUs, and the
+    CPUs this process may run on."""
+    info = {"logical_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "cpu MHz", "vendor_id") and k not in fields:
+                    fields[k] = v
     except OSError:
         pass
-    return "unknown"
+    info.update({k.replace(" ", "_"): v for k, v in fields.items()})
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "Socket(s)", "Core(s) per socket", "Thread(s) per core", "CPU max MHz"):
+                info["lscpu_" + k.strip().lower().replace(" ", "_").replace("(s)", "s")] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
 
 
 def main():
@@ -406,7 +574,8 @@ def main():
                     help="untimed steps for at least this much wall time before the warm-up steps, so the "
                          "timed steps run at the device's steady clocks (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--cpu-threads", type=int, default=len(os.sched_getaffinity(0)),
+                    help="oracle threads (default: every CPU this process may run on)")
     ap.add_argument("--paged", action="store_true",
                     help="keys in pools of 64-token pages in a random page order, addressed through a page "
                          "table (the contiguous layout is the default)")
@@ -422,13 +591,14 @@ def main():
     ap.add_argument("--kv-layout", choices=("tiled", "strided"), default="tiled",
                     help="tiled: the library's tiled bf16 cache (msa_kv_tiled; each step packs its own new "
                          "keys into it); strided: the plain [tokens, heads, 128] cache")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="enqueue the long row's calls after the chunk's on one stream (default: on a second "
-                         "stream, concurrent with the chunk's; the two workloads share no data)")
+    ap.add_argument("--overlap", choices=("indexer", "free", "none"), default="indexer",
+                    help="the long row's calls: on a second stream starting with the chunk's part of each step "
+                         "(indexer, the default: beside the chunk's cache write, indexer and selection), on a "
+                         "free-running second stream (free), or after the chunk's on one stream (none)")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
-    ap.add_argument("--no-others", action="store_true",
-                    help="skip the reference timings of the other named workloads after the headline step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration back-to-back loops after the headline step")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the device's sustained HBM read and bf16 MFMA rates after timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -454,108 +624,32 @@ def main():
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     cases = {"chunk": config("chunk") if args.locality is None else config("chunk", locality=args.locality),
              "long": config("long")}
-    reps = {"chunk": 2, "long": 4}       # replicas: >= 512 MB rotated per workload
-    modes = {"chunk": "prefill", "long": "decode"}
-    fused = {"chunk": False, "long": not args.unfused}
-    # the paged pools' new keys are not one token range: there the whole pool
-    # is packed before timing and the steps write nothing
-    write = tiled and not args.paged
-    steps_of = {n: (("write_cache",) if write else ()) +
-                   (("index_select", "attention") if fused[n] else ("index_scores", "select_blocks", "attention"))
-                for n in modes}
-    state = {}
-    for name, case in cases.items():
-        base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
-        if args.head_major:
-            for n in ("k", "v", "ik"):
-                base[n] = base[n].permute(1, 0, 2).contiguous().permute(1, 0, 2)
-        page_table = None
-        if args.paged:
-            from workloads import to_pages
-            pool, page_table = to_pages(case, seed=7)
-            base.update({n: x.to(dev) for n, x in pool.items()})
-        inputs = [base] + [{n: x.clone() for n, x in base.items()} for _ in range(reps[name] - 1)]
-        shape = msa.make_shape(case.n_kv_heads, case.top_k, case.scale)
-        if args.kv8:
-            for t in inputs:
-                kc, ks = msa.msa_quantize_kv8(shape, t["k"])
-                vc, vs = msa.msa_quantize_kv8(shape, t["v"])
-                t["kv8"] = msa.KV8(kc, vc, ks, vs)
-                del t["k"], t["v"]
-        if tiled:
-            for t in inputs:   # the cached prefix, written before timing (set-up)
-                t["kvt"] = msa.KVTiled.empty(t["k"].shape[0], case.n_kv_heads, dev)
-                msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"])
-        batch = msa.Batch(case.seq_lens, case.rows, device=dev, page_table=page_table)
-        outs = msa.run_path(shape, batch, inputs[0], modes[name], fused=fused[name], kv8=inputs[0].get("kv8"),
-                            kvt=inputs[0].get("kvt"))
-        state[name] = (shape, batch, inputs, outs)
+    opts = dict(tiled=tiled, paged=args.paged, head_major=args.head_major, kv8=args.kv8)
+    wl = {"chunk": Workload(torch, msa, dev, "chunk", cases["chunk"], "prefill", CONFIG_PLAN["chunk"][2],
+                            fused=False, **opts),
+          "long": Workload(torch, msa, dev, "long", cases["long"], "decode", CONFIG_PLAN["long"][2],
+                           fused=not args.unfused, **opts)}
     torch.cuda.synchronize()
 
-    # Per-call HIP events cost the stream ~5 us each (measured: 0.82 against
-    # 0.77 ms per step with an event pair around each of the 5 calls), so the
-    # timed steps bracket only the dominant kernel's call; every call's
-    # duration comes from a separate untimed pass with events around each.
-    per_call = Timed(torch)
+    side = None if args.overlap == "none" else torch.cuda.Stream()
     timer = Timed(torch)
     bracket = set()
-
-    # The long row's calls go to a second stream (default priority) in the
-    # timed and warm-up steps: its kernels are latency-bound on few
-    # workgroups and share nothing with the chunk's, so they run beside them
-    # (a serving step that carries a prompt chunk and a decode row at once).
-    # The per-call timing pass keeps everything on one stream.
-    import contextlib
-    side = None if args.no_overlap else torch.cuda.Stream()
+    marks = [torch.cuda.Event() for _ in range(8)]
 
     def step(i, timed):
+        """One headline step: the long row (second stream unless --overlap
+        none) and the chunk; `timed`: bracket the calls named in `bracket`."""
+        if side is not None and args.overlap == "indexer":
+            mk = marks[i % len(marks)]
+            mk.record()                  # the chunk's part of this step starts here
+            side.wait_event(mk)
         for name in ("long", "chunk"):
-            shape, batch, inputs, o = state[name]
-            t = inputs[i % len(inputs)]
-            calls = []
-            if write:   # the step's new keys (the last total_rows tokens) into the tiles
-                n_tok = t["k"].shape[0]
-                calls.append(("write_cache", lambda: msa.msa_pack_kv_tiled(shape, t["k"], t["v"], t["kvt"],
-                                                                           n_tok - batch.total_rows, n_tok)))
-            if fused[name]:
-                calls += [("index_select", lambda: msa.msa_index_select(shape, batch, t["iq"], t["ik"],
-                                                                       o["block_scores"], o["block_idx"],
-                                                                       o["select_workspace"]))]
-            else:
-                calls += [
-                    ("index_scores", lambda: msa.msa_index_scores(shape, batch, t["iq"], t["ik"],
-                                                                  o["block_scores"])),
-                    ("select_blocks", lambda: msa.msa_select_blocks(shape, batch, o["block_scores"],
-                                                                    o["block_idx"])),
-                ]
-            if modes[name] == "prefill" and args.kv8:
-                calls.append(("attention", lambda: msa.msa_prefill_kv8(shape, batch, t["q"], t["kv8"],
-                                                                       o["block_idx"], o["out"], o["lse"])))
-            elif modes[name] == "prefill" and tiled:
-                calls.append(("attention", lambda: msa.msa_prefill_tiled(shape, batch, t["q"], t["kvt"],
-                                                                         o["block_idx"], o["out"], o["lse"])))
-            elif modes[name] == "prefill":
-                calls.append(("attention", lambda: msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"],
-                                                                   o["block_idx"], o["out"], o["lse"])))
-            elif args.kv8:
-                calls.append(("attention", lambda: msa.msa_decode_kv8(shape, batch, t["q"], t["kv8"],
-                                                                      o["block_idx"], o["out"], o["lse"],
-                                                                      o["workspace"])))
-            elif tiled:
-                calls.append(("attention", lambda: msa.msa_decode_tiled(shape, batch, t["q"], t["kvt"],
-                                                                        o["block_idx"], o["out"], o["lse"],
-                                                                        o["workspace"])))
-            else:
-                calls.append(("attention", lambda: msa.msa_decode(shape, batch, t["q"], t["k"], t["v"],
-                                                                  o["block_idx"], o["out"], o["lse"],
-                                                                  o["workspace"])))
-            on_side = side is not None and name == "long" and timed != "all"
+            w = wl[name]
+            on_side = side is not None and name == "long"
             with torch.cuda.stream(side) if on_side else contextlib.nullcontext():
-                for kname, fn in calls:
+                for kname, fn in w.calls(i):
                     key = f"{name}/{kname}"
-                    if timed == "all":
-                        per_call.run(key, fn)
-                    elif timed and key in bracket:
+                    if timed and key in bracket:
                         timer.run(key, fn)
                     else:
                         fn()
@@ -571,18 +665,19 @@ def main():
         settle_steps += 1
         if settle_steps % 8 == 0:
             torch.cuda.synchronize()
-    # untimed pass with an event pair around every call: each kernel's duration
-    n_call_steps = max(1, min(args.steps, 50))
-    gc.disable()   # a collection between an event and its call would show up as kernel time
-    for i in range(n_call_steps):
-        step(i, "all")
     torch.cuda.synchronize()
-    kms, kq = per_call.mean_ms(), per_call.quantiles_ms()
+    # which call dominates: an untimed one-stream pass with events around each
+    n_call_steps = max(1, min(args.steps, 20))
+    kms = {}
+    for name in ("chunk", "long"):
+        m, _ = per_call_timing(torch, wl[name], n_call_steps)
+        kms.update({f"{name}/{k}": v for k, v in m.items()})
     dominant = max(kms, key=kms.get)
     bracket.add(dominant)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, True)
@@ -591,38 +686,18 @@ def main():
     gc.enable()
     ms_step = elapsed / args.steps * 1e3
     rows = sum(c.total_rows for c in cases.values())
-    # the dominant kernel: its launches inside the timed steps
-    kms[dominant] = timer.mean_ms()[dominant]
-    kq[dominant] = timer.quantiles_ms()[dominant]
-
-    kernels = []
-    for name, case in cases.items():
-        work = algorithmic_work(case, kv8=args.kv8)
-        for kname in steps_of[name]:
-            ms = kms[f"{name}/{kname}"]
-            wk = work[kname]
-            bound = "mfma" if wk["flops"] and wk["flops"] / max(wk["bytes"], 1) > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm"
-            if bound == "mfma":
-                ach = wk["flops"] / (ms * 1e-3) / 1e12
-                ent = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
-            else:
-                ach = wk["bytes"] / (ms * 1e-3) / 1e9
-                ent = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s")
-            ent["frac"] = ent["achieved"] / ent["peak"]
-            p10, p50, p90 = kq[f"{name}/{kname}"]
-            ent.update(kernel=f"{name}/{kname}", ms=ms, ms_p10=p10, ms_median=p50, ms_p90=p90,
-                       algorithmic_flops=wk["flops"], algorithmic_bytes=wk["bytes"],
-                       timed_in="timed steps" if f"{name}/{kname}" == dominant else
-                       f"untimed pass of {n_call_steps} steps")
-            kernels.append(ent)
-    dom = next(e for e in kernels if e["kernel"] == dominant)
-    roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    dom_ms = timer.mean_ms()[dominant]
+    dom_q = timer.quantiles_ms()[dominant]
+    dname, dk = dominant.split("/")
+    dom_work = algorithmic_work(cases[dname], kv8=args.kv8,
+                                block_idx=wl[dname].o["block_idx"].cpu().numpy())[dk]
+    roofline = {k: v for k, v in fraction(dom_work, dom_ms).items()}
     # the committed counter summaries describe the default workload and layout only
-    variant = args.kv8 or args.paged or args.head_major or args.locality is not None
-    roofline.update(kernel=dom["kernel"], traffic=None if variant else profiled_traffic(dom["kernel"]))
+    variant = args.kv8 or args.paged or args.head_major or args.locality is not None or not tiled
+    roofline.update(kernel=dominant, ms=dom_ms, ms_p10=dom_q[0], ms_median=dom_q[1], ms_p90=dom_q[2],
+                    algorithmic_flops=dom_work["flops"], algorithmic_bytes=dom_work["bytes"],
+                    traffic=None if variant else profiled_traffic(dominant))
 
-    t_chunk = sum(kms[f"chunk/{k}"] for k in steps_of["chunk"])
-    t_long = sum(kms[f"long/{k}"] for k in steps_of["long"])
     res = {
         "metric": METRIC,
         "value": rows / (ms_step * 1e-3),
@@ -643,37 +718,57 @@ def main():
                    "rows_per_step": rows, "kv_heads": 4, "q_heads": 64,
                    "kv_layout": ("paged (64-token pages, random order)" if args.paged else
                                  "contiguous, head-major" if args.head_major else "contiguous, token-major"),
-                   "kv_cache": ("int8 codes + fp32 scale per (token, key head)" if args.kv8 else
-                                "bf16, tiled (64-key tiles in matrix-core operand order; each step writes its "
-                                "new keys into it" + (")" if write else "; pool packed before timing)")
-                                if tiled else "bf16"),
+                   "kv_cache": wl["chunk"].kv_cache,
                    "index_queries": ("i.i.d. N(0,1) per row" if args.locality is None else
                                      f"secondary workload: AR(1) across the chunk's rows, a = {args.locality}")},
         "inputs": {"generator": "torch.Generator (CPU) seeded per workload, randn in fp32 rounded to bf16",
                    "torch": torch.__version__,
                    "seeds": {n: c.seed for n, c in cases.items()},
                    "sha256": {n: c.digests() for n, c in cases.items()}},
-        "prefill_rows_per_s": cases["chunk"].total_rows / (t_chunk * 1e-3),
-        "decode_rows_per_s": cases["long"].total_rows / (t_long * 1e-3),
         "roofline": roofline,
-        "kernels": kernels,
-        "kernel_timing": (f"HIP event pairs on the launch stream: around every launch of the dominant kernel "
-                          f"({dominant}) in the timed steps; around every call in an untimed pass of "
-                          f"{n_call_steps} steps, all on one stream, for the others (events in the timed steps "
-                          f"cost ~5 us each)"),
-        "streams": ("one: the long row's calls after the chunk's" if side is None else
-                    "two (default priority): the long row's calls on a second stream, concurrent with the "
-                    "chunk's; prefill_rows_per_s and decode_rows_per_s come from the one-stream per-call pass"),
+        "roofline_timing": (f"{dominant}: HIP event pair around each of its launches in the {args.steps} timed "
+                            f"steps, on its launch stream; algorithmic work of one launch over that mean"),
+        "streams": {"none": "one: the long row's calls after the chunk's",
+                    "free": "two (default priority): the long row's calls on a free-running second stream",
+                    "indexer": "two (default priority): each step's long row on a second stream, starting when "
+                               "the chunk's part of the step starts (beside its cache write, indexer and "
+                               "selection)"}[args.overlap],
     }
-    if not args.no_others:
-        kept = {} if not args.no_cpu_baseline else None
-        res["other_configs"] = other_configs(torch, msa, dev, keep=kept, tiled=tiled)
+    print(f"[bench] headline {ms_step:.4f} ms/step ({res['value'] / 1e6:.3f} M rows/s)", file=sys.stderr,
+          flush=True)
+
+    measured = None
     if not args.no_peaks:
-        peaks = measured_peaks(torch, msa, dev)
-        res["measured_peaks"] = peaks
-        meas = peaks["hbm_read_GBs"] if roofline["unit"] == "GB/s" else peaks["bf16_mfma_TFLOPs"]
+        measured = measured_peaks(torch, msa, dev)
+        res["measured_peaks"] = measured
+        meas = measured["hbm_read_GBs"] if roofline["unit"] == "GB/s" else measured["bf16_mfma_TFLOPs"]
         roofline["measured_peak"] = meas
         roofline["frac_of_measured"] = roofline["achieved"] / meas
+
+    configs = {}
+    if not args.no_configs:
+        for name in ("tiny", "decode", "chunk", "long", "windows"):
+            mode, fused, n_rep, steps, block = CONFIG_PLAN[name]
+            if name in wl:
+                w = wl[name]
+            else:
+                w = Workload(torch, msa, dev, name, config(name), mode, n_rep, fused=fused, tiled=tiled)
+            print(f"[bench] config {name}: {steps} steps back to back", file=sys.stderr, flush=True)
+            configs[name] = config_entry(torch, w, steps, block, measured, kv8=args.kv8 and name in wl)
+            if name not in wl:
+                configs[name]["_workload"] = w
+        res["prefill_rows_per_s"] = configs["chunk"]["rows_per_s"]
+        res["decode_rows_per_s"] = configs["long"]["rows_per_s"]
+        res["config_fractions"] = {CONFIG_LETTER[n]: {"bound": e["path_fraction"]["bound"],
+                                                      "frac": e["path_fraction"]["frac"],
+                                                      "frac_median": e["path_fraction_median"],
+                                                      **({"frac_of_measured": e["path_fraction"]["frac_of_measured"]}
+                                                         if measured else {}),
+                                                      "ms_mean": e["ms_mean"], "rows_per_s": e["rows_per_s"],
+                                                      **({"target": e["target"]["frac"]} if "target" in e else {})}
+                                   for n, e in configs.items()}
+        res["rows_per_s_basis"] = ("prefill_rows_per_s: the chunk alone, back to back; decode_rows_per_s: the "
+                                   "262,144-key row alone, back to back (each step's cache write included)")
     if args.copy_calibration_mib:
         # an elementwise kernel that reads n bytes and writes n bytes once
         n = args.copy_calibration_mib << 20
@@ -683,21 +778,37 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n
+
     if not args.no_cpu_baseline:
-        # the timed run's outputs (every input replica holds the same values)
-        gpu = {}
-        for name in cases:
-            o = state[name][3]
-            gpu[name] = {"block_idx": o["block_idx"].cpu().numpy(), "out": o["out"].float().cpu().numpy(),
-                         "lse": o["lse"].cpu().numpy()}
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
-        base, val = cpu_baseline(cases, args.cpu_threads, None if args.kv8 else gpu)
-        res["cpu_baseline"] = base
-        if val is not None:
-            res["validation"] = val
-        if not args.no_others:
-            for name, ent in other_cpu_baselines(kept, args.cpu_threads).items():
-                res["other_configs"][name].update(ent)
+        res["host_cpu"] = host_cpu()
+        threads = args.cpu_threads
+        legs = {}
+        for name in ("chunk", "long"):
+            gpu = None if args.kv8 else wl[name].host_outputs()
+            legs[name] = oracle_leg(cases[name], name, threads, gpu)
+        # the headline step's oracle time: per-row time of the chunk's sample
+        # scaled to its 4,096 rows, plus the decode row
+        (_, (rc, _, dt_c)), (_, (rl, _, dt_l)) = legs["chunk"], legs["long"]
+        t_step = dt_c / len(rc) * cases["chunk"].total_rows + dt_l / len(rl) * cases["long"].total_rows
+        res["cpu_baseline"] = {
+            "value": rows / t_step, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"96 random rows of the 4,096-row chunk ({dt_c / len(rc) * 1e3:.1f} ms/row) and the "
+                      f"262,144-key decode row ({dt_l * 1e3:.0f} ms); step time extrapolated to 4,096 + 1 rows "
+                      f"= {t_step:.1f} s",
+            "cpu": res["host_cpu"].get("model_name", "unknown")}
+        if not args.kv8:
+            res["validation"] = {n: legs[n][0]["validation"] for n in legs}
+        for name, e in configs.items():
+            if name in legs:
+                e.update(legs[name][0])
+            else:
+                w = e["_workload"]
+                e.update(oracle_leg(w.case, name, threads, w.host_outputs())[0])
+    for e in configs.values():
+        e.pop("_workload", None)
+    if configs:
+        res["configs"] = configs
     print(json.dumps(res))
 
 

@@ -47,7 +47,8 @@ EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_pre
            "msa_pack_kv_tiled", "msa_pack_kv_tiled_rows", "msa_prefill_tiled", "msa_decode_tiled",
            "msa_decode_tiled_noalloc",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
-           "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_mfma")
+           "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_stream_read_variant",
+           "msa_peaks_mfma")
 
 
 class _KV8C(ctypes.Structure):
@@ -102,6 +103,8 @@ def lib():
             L.msa_version.restype = ctypes.c_char_p
             L.msa_peaks_stream_read.argtypes = [vp, i64, vp, vp]
             L.msa_peaks_mfma.argtypes = [vp, i32, i32, vp]
+            L.msa_peaks_stream_read_variant.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp]
+            L.msa_peaks_stream_read_variant.restype = ctypes.c_int
             L.msa_peaks_stream_read.restype = ctypes.c_int
             L.msa_peaks_mfma.restype = ctypes.c_int
             _lib = L
@@ -502,6 +505,15 @@ def msa_peaks_stream_read(buf, sink, stream=None):
     """Read every byte of the device tensor buf once (the device's sustained
     HBM read rate, timed by the caller).  sink: a device tensor of >= 1 uint32."""
     _check(lib().msa_peaks_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def msa_peaks_stream_read_variant(buf, sink, unroll: int, width: int, nontemporal: int, wg_per_cu: int,
+                                  stream=None):
+    """msa_peaks_stream_read with its knobs: loads in flight per thread,
+    load width in bytes, nontemporal loads, workgroups per CU."""
+    _check(lib().msa_peaks_stream_read_variant(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                               int(unroll), int(width), int(nontemporal), int(wg_per_cu),
+                                               _stream(stream)))
 
 
 def msa_peaks_mfma(sink, workgroups: int, iters: int, stream=None):

@@ -29,6 +29,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *p, int64_
     if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// The same read with the knobs a streaming kernel has: U loads in flight per
+// thread per iteration, loads of W = sizeof(T) bytes, plain or nontemporal
+// loads (the grid is the caller's).  Swept by the benchmark to find the best
+// read rate the device sustains.
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fold_word(uint32_t x) { return x; }
+__device__ __forceinline__ uint32_t fold_word(u32x2v x) { return x.x ^ x.y; }
+__device__ __forceinline__ uint32_t fold_word(u32x4 x) { return x.x ^ x.y ^ x.z ^ x.w; }
+
+template <int U, typename T, bool NT>
+__device__ __forceinline__ T read_word(const T *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int U, typename T, bool NT>
+__global__ __launch_bounds__(256) void stream_read_variant_kernel(const T *p, int64_t n, uint32_t *sink) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0u;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        T v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = read_word<U, T, NT>(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += fold_word(v[u]);
+    }
+    for (; i < n; i += stride) acc ^= fold_word(read_word<U, T, NT>(p + i));
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 // Four independent accumulation chains per wave, so the MFMA pipeline never
 // waits on a result; operands depend on the lane so nothing folds away.
 __global__ __launch_bounds__(256) void mfma_loop_kernel(float *sink, int iters) {
@@ -75,6 +106,50 @@ extern "C" int msa_peaks_stream_read(const void *buf, int64_t bytes, uint32_t *s
     hipLaunchKernelGGL(msa::stream_read_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(buf), n16, sink);
     return launched(hipGetLastError(), "stream_read");
+}
+
+namespace {
+template <int U, typename T>
+void launch_variant(const void *buf, int64_t n, uint32_t *sink, bool nt, unsigned grid, hipStream_t st) {
+    if (nt) hipLaunchKernelGGL((msa::stream_read_variant_kernel<U, T, true>), dim3(grid), dim3(256), 0, st,
+                               static_cast<const T *>(buf), n, sink);
+    else hipLaunchKernelGGL((msa::stream_read_variant_kernel<U, T, false>), dim3(grid), dim3(256), 0, st,
+                            static_cast<const T *>(buf), n, sink);
+}
+template <typename T>
+void launch_unroll(int unroll, const void *buf, int64_t n, uint32_t *sink, bool nt, unsigned grid, hipStream_t st) {
+    switch (unroll) {
+        case 1: launch_variant<1, T>(buf, n, sink, nt, grid, st); break;
+        case 2: launch_variant<2, T>(buf, n, sink, nt, grid, st); break;
+        case 4: launch_variant<4, T>(buf, n, sink, nt, grid, st); break;
+        case 8: launch_variant<8, T>(buf, n, sink, nt, grid, st); break;
+        default: launch_variant<16, T>(buf, n, sink, nt, grid, st); break;
+    }
+}
+}  // namespace
+
+extern "C" int msa_peaks_stream_read_variant(const void *buf, int64_t bytes, uint32_t *sink, int32_t unroll,
+                                             int32_t width, int32_t nontemporal, int32_t wg_per_cu, void *stream) {
+    if (!buf || !sink) return peaks_fail(MSA_ERR_INVALID, "stream_read_variant: NULL buffer");
+    if (bytes <= 0 || (bytes & 15) != 0 || ((uintptr_t)buf & 15u) != 0)
+        return peaks_fail(MSA_ERR_INVALID, "stream_read_variant: bytes=%lld must be > 0, a multiple of 16, "
+                          "16-byte aligned", (long long)bytes);
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+        return peaks_fail(MSA_ERR_INVALID, "stream_read_variant: unroll=%d not 1, 2, 4, 8 or 16", unroll);
+    if (width != 4 && width != 8 && width != 16)
+        return peaks_fail(MSA_ERR_INVALID, "stream_read_variant: width=%d not 4, 8 or 16", width);
+    if (wg_per_cu < 1 || wg_per_cu > 64)
+        return peaks_fail(MSA_ERR_INVALID, "stream_read_variant: wg_per_cu=%d outside [1, 64]", wg_per_cu);
+    const int64_t n = bytes / width;
+    const int64_t blocks = (n + 255) / 256;
+    const int64_t cap = 256LL * wg_per_cu;
+    const unsigned grid = (unsigned)(blocks < cap ? blocks : cap);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool nt = nontemporal != 0;
+    if (width == 4) launch_unroll<uint32_t>(unroll, buf, n, sink, nt, grid, st);
+    else if (width == 8) launch_unroll<msa::u32x2v>(unroll, buf, n, sink, nt, grid, st);
+    else launch_unroll<u32x4>(unroll, buf, n, sink, nt, grid, st);
+    return launched(hipGetLastError(), "stream_read_variant");
 }
 
 extern "C" int msa_peaks_mfma(float *sink, int32_t workgroups, int32_t iters, void *stream) {

@@ -28,6 +28,15 @@ extern "C" {
  * MSA_ERR_INVALID on a NULL, misaligned or badly sized buffer. */
 int msa_peaks_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
+/* The same read with its knobs exposed, for a sweep of the read rate:
+ * `unroll` loads in flight per thread per iteration (1, 2, 4, 8 or 16), loads
+ * of `width` bytes (4, 8 or 16), plain (nontemporal == 0) or nontemporal
+ * loads, and at most wg_per_cu (1..64) workgroups of 256 threads per CU
+ * (256 CUs), grid-striding over the buffer.  Arguments otherwise as
+ * msa_peaks_stream_read; MSA_ERR_INVALID for a knob outside its set. */
+int msa_peaks_stream_read_variant(const void *buf, int64_t bytes, uint32_t *sink, int32_t unroll, int32_t width,
+                                  int32_t nontemporal, int32_t wg_per_cu, void *stream);
+
 /* workgroups x 4 waves each run `iters` rounds of 4 independent 16x16x32 bf16
  * MFMAs: workgroups * 4 * iters * 4 * 16384 FLOP in total.  sink: device
  * float[256] the kernel may write to; contents unspecified.  workgroups in

@@ -78,3 +78,22 @@ def test_validation_fails_on_wrong_outputs(small):
     wrong["block_idx"][77, 0, 0] = wrong["block_idx"][77, 0, 1]   # a wrong selection
     v = bench.validate({"chunk": c, "long": l}, refs, {"chunk": wrong, "long": _gpu_like(full_l)})
     assert not v["chunk"]["selection_exact"] and not v["chunk"]["pass"]
+
+
+def test_kept_bytes_count_distinct_blocks():
+    """The attention's K/V bytes count each (sequence, key head, block) kept
+    by any row once, with the keys of it that the sequence's last row sees."""
+    case = make_case("d", [1000, 300], [3, 2], 2, seed=9, top_k=4)
+    idx = np.full((5, 2, 4), -1, dtype=np.int32)
+    idx[0, 0, :3] = [0, 1, 15]          # sequence 0 (1,000 keys: block 15 holds 40 of them)
+    idx[1, 0, :3] = [1, 2, 15]
+    idx[2, 0, :4] = [0, 7, 9, 15]
+    idx[:3, 1, :2] = [3, 15]            # head 1: the same two blocks on every row
+    idx[3, 0, :2] = [0, 4]              # sequence 1 (300 keys: block 4 holds 44 of them)
+    idx[4, 0, :1] = [4]
+    idx[3:, 1, :1] = [4]
+    per_key = 128 * 2 * 2               # K and V, bf16
+    want = (5 * 64 + 40) + (64 + 40) + (64 + 44) + 44
+    assert bench.kept_kv_bytes(case, idx) == want * per_key
+    w = bench.algorithmic_work(case, block_idx=idx)
+    assert w["attention"]["bytes"] == 5 * 2 * 16 * 128 * 2 * 2 + 5 * 2 * 4 * 4 + want * per_key

@@ -15,6 +15,13 @@ def test_peaks_kernels_run():
     msa.msa_peaks_stream_read(buf, sink)
     msa.msa_peaks_stream_read(buf[:16], sink)        # 64 bytes: fewer words than threads
     msa.msa_peaks_mfma(sink, 4, 10)
+    for unroll in (1, 2, 4, 8, 16):
+        for width in (4, 8, 16):
+            for nt in (0, 1):
+                msa.msa_peaks_stream_read_variant(buf, sink, unroll, width, nt, 2)
+    msa.msa_peaks_stream_read_variant(buf[:16], sink, 16, 16, 1, 64)   # fewer words than threads
     torch.cuda.synchronize()
     with pytest.raises(msa.MsaError):
         msa.msa_peaks_stream_read(buf[:3], sink)     # 12 bytes: not a multiple of 16
+    with pytest.raises(msa.MsaError):
+        msa.msa_peaks_stream_read_variant(buf, sink, 3, 16, 0, 2)      # unroll not in the set
