@@ -419,7 +419,7 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 }
 
 // Prefill.  One wave per group of RW consecutive rows of one key head.  For each row it holds the 16 query heads (so every
-// kept block is read once for all of them) and an online-softmax state.  The
+// kept block is fetched once for the whole group) and an online-softmax state.  The
 // rows' kept blocks are merged into one list sorted by block index and walked
 // 32 keys at a time, the next chunk's K/V loads in flight while the current
 // one is folded.  A block kept by several of the rows (their shared local
@@ -772,11 +772,16 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
     combine_group<8>(wm, wl, vt_all, 0, h, d0, M, Ls, accv);
 
     if (wg_per_unit > 1) {
-        // Publish the workgroup's partial with device-scoped stores (written
-        // through to the device level), wait for them, then count the
-        // workgroup in: no release fence, which would write back the whole L2
-        // in each of the many workgroups.  The last one to arrive merges, in
-        // split order, reading the others' partials with device-scoped loads.
+        // Publish the workgroup's partial with agent-scope stores, wait for
+        // them, then count the workgroup in; the last one to arrive merges, in
+        // split order, reading the others' partials with agent-scope loads.
+        // Relaxed atomics order nothing in the language's model: this relies
+        // on gfx950 compiling agent-scope stores and loads with the sc1 bit
+        // (stores written through the XCD's L2 to the device-coherent level,
+        // loads not served from a copy in it), on s_waitcnt returning only
+        // once the stores are acknowledged, and on the counter's atomic add
+        // being performed at that level.  A release fence would make it
+        // formal but writes back the whole L2 in each of the many workgroups.
         float *pw = part_unit + split * (int64_t)kPartialFloats;
         if (d0 == 0) {
             __hip_atomic_store(pw + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

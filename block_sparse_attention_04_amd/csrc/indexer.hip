@@ -371,11 +371,14 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         }
     }
     if constexpr (kSelect) {
-        // Every score store above is device-scoped, so publishing them needs only
-        // their completion (no write-back of the whole L2, which an agent-scope
-        // release fence would issue in each of the many workgroups): wait for
-        // this wave's stores, meet at the barrier, then count the workgroup in.
-        // The last workgroup reads the scores with device-scoped loads.
+        // Every score store above is agent-scoped (compiled with sc1: written
+        // through the XCD's L2 to the device-coherent level), so publishing
+        // them needs only their completion: wait for this wave's stores, meet
+        // at the barrier, then count the workgroup in (the atomic add is
+        // performed at that level).  The last workgroup reads the scores with
+        // agent-scope loads (sc1: not served from a copy in its own L2).  The
+        // language's model orders none of this; an agent-scope release fence
+        // would, but writes back the whole L2 in each of the many workgroups.
         extern __shared__ uint32_t dyn[];
         __shared__ SelScratch sc;
         __shared__ int is_last;

@@ -2,8 +2,8 @@
 //
 // The cache keeps keys and values as int8 codes with one fp32 scale per
 // (token, key head) (TensorFold pull request 1388, commit adding the
-// minimax_m3 family: keys and values cached as int8 with a scale a position
-// and head).  The rule that makes a row's codes is this library's reading (the
+// minimax_m3 family, which describes an int8 key/value cache scaled per
+// position and key head).  The rule that makes a row's codes is this library's reading (the
 // pages name the scale, not its rule), taken in fp32:
 //   scale  = max_d |x_d| / 127
 //   code_d = round_half_even(x_d / scale), clamped to [-127, 127]

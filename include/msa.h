@@ -11,8 +11,8 @@
  *     per row and key head; decode attends over the kept blocks in 32-key
  *     partials; prompt chunks attend over each tile's kept blocks.
  *   - same pull request, commit on 4,096-row prompt chunks: the 16 query heads
- *     of one key head share that key head's selection, so each kept key/value
- *     block is read once for all of them.
+ *     of one key head share that key head's selection, so one fetch of a kept
+ *     key/value block serves all sixteen.
  *
  * Notation.  A ragged batch holds n_seqs sequences.  Sequence s has
  * seq_lens[s] keys (every key visible to its last row, the rows' own keys
@@ -181,8 +181,8 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch,
 /*
  * Step 4 for prompt chunks: out[r, h, :] = softmax over the kept, visible keys
  * of scale * q[r,h,:].k[j,g,:], applied to v[j,g,:], g = h / group.  One pass
- * per row; the group's query heads share the row's selection, so each kept
- * block is read once for all of them.  Keys are walked in ascending block
+ * per row; the group's query heads share the row's selection, so one fetch of
+ * a kept block serves every head of the group.  Keys are walked in ascending block
  * order, so a row's bits do not depend on the other rows in the batch.
  *   q, out    bf16 [total_rows, n_kv_heads*group, head_dim], contiguous
  *   k, v      bf16, element (token t, key head g, dim d) at
@@ -205,10 +205,11 @@ int msa_prefill(const msa_shape *shape, const msa_batch *batch,
  * code * scale.  Attention over it scales each key's score by the key's scale
  * and each weight by the value's scale before the weighted sum (the softmax
  * sum uses the unscaled weights), so the codes feed the matrix cores as exact
- * bf16.  (TensorFold pull request 1388, commit adding the minimax_m3 family:
- * keys and values cached as int8 with a scale a position and head, 57% of
- * bf16's bytes; prompt chunks scale scores by the keys' scales and
- * probabilities by the values'.  A later commit of the same pull request
+ * bf16.  (TensorFold pull request 1388, commit adding the minimax_m3 family,
+ * describes such a cache: int8 keys and values with one scale per position
+ * and key head, a little over half the bytes of bf16, with the key scales
+ * applied to the scores and the value scales to the weights in prompt
+ * chunks.  A later commit of the same pull request
  * removed the int8 cache because it changes the model's arithmetic; here it
  * is an alternative entry point and the bf16 path is unchanged.)
  * Index keys stay bf16.  The paged layout applies to the codes and scales as

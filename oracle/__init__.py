@@ -30,6 +30,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# An AddressSanitizer + UndefinedBehaviorSanitizer build of the same source,
+# loaded instead when MSA_ORACLE_SANITIZED=1 (the process must preload the
+# sanitizer runtimes; tests/test_oracle_sanitized.py runs the pins that way).
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 _lock = threading.Lock()
 _lib = None
 
@@ -40,25 +45,34 @@ F32P = ctypes.POINTER(ctypes.c_float)
 F64P = ctypes.POINTER(ctypes.c_double)
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, sanitized: bool = False) -> str:
     """Compile liboracle.so with the host compiler (no fast-math: sums keep
-    their order)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+    their order); sanitized: liboracle_san.so, the same source built with
+    AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts)."""
+    lib = _LIB_SAN if sanitized else _LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(_SRC):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = SAN_FLAGS if sanitized else ["-O2"]
+    cmd = ["gcc", *opt, "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
            "-shared", "-fPIC", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def loaded_path() -> str:
+    """Path of the oracle library this process uses."""
+    return _LIB_SAN if os.environ.get("MSA_ORACLE_SANITIZED") == "1" else _LIB
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            sanitized = os.environ.get("MSA_ORACLE_SANITIZED") == "1"
+            build(force=False, sanitized=sanitized)
+            lib = ctypes.CDLL(_LIB_SAN if sanitized else _LIB)
             lib.oracle_block_scores.restype = ctypes.c_int
             lib.oracle_block_scores.argtypes = [
                 ctypes.c_int, I32P, I32P, I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
