@@ -92,8 +92,9 @@ def lib():
                       "msa_pack_kv_tiled_rows",
                       "msa_prefill_tiled", "msa_decode_tiled", "msa_decode_tiled_noalloc"):
                 getattr(L, n).restype = ctypes.c_int
+            L.msa_decode_workspace_bytes.argtypes = [SP, i32]
+            L.msa_index_select_workspace_bytes.argtypes = [SP, BP]
             for n in ("msa_decode_workspace_bytes", "msa_index_select_workspace_bytes"):
-                getattr(L, n).argtypes = [SP, i32]
                 getattr(L, n).restype = ctypes.c_size_t
             L.msa_status_string.argtypes = [ctypes.c_int]
             L.msa_status_string.restype = ctypes.c_char_p
@@ -211,29 +212,40 @@ def msa_select_blocks(shape: Shape, batch: Batch, block_scores, block_idx, strea
                                    block_scores.shape[-1], _ptr(block_idx), _stream(stream)))
 
 
-def msa_index_select_workspace_bytes(shape: Shape, n_seqs: int) -> int:
-    return int(lib().msa_index_select_workspace_bytes(ctypes.byref(shape), int(n_seqs)))
+def msa_index_select_workspace_bytes(shape: Shape, batch: Batch) -> int:
+    return int(lib().msa_index_select_workspace_bytes(ctypes.byref(shape), ctypes.byref(batch.c)))
 
 
-def index_select_workspace(shape: Shape, n_seqs: int, device="cuda"):
-    """A zero-filled workspace for msa_index_select (its arrival counters must
-    start at 0; the library leaves them at 0 after every completed call)."""
-    n = max(msa_index_select_workspace_bytes(shape, n_seqs), 256)
+def index_select_workspace(shape: Shape, batch: Batch, device="cuda"):
+    """A zero-filled workspace for msa_index_select on this batch (its arrival
+    counters must start at 0; the library leaves them at 0 after every
+    completed call, so it serves any batch it is large enough for)."""
+    n = max(msa_index_select_workspace_bytes(shape, batch), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def chunk_select_eligible(shape: Shape, batch: Batch) -> bool:
+    """Whether msa_index_select can take this batch with block_scores=None
+    (more than 16 rows in a sequence, top_k <= 16): the scores then never
+    reach memory."""
+    return batch.max_rows > 16 and shape.top_k <= 16
 
 
 def msa_index_select(shape: Shape, batch: Batch, iq, ik, block_scores, block_idx, workspace=None,
                      stream=None):
+    """block_scores=None: the fused prompt-chunk path (no scores written)."""
     _need(iq, torch.bfloat16, "iq")
     _need(ik, torch.bfloat16, "ik", contiguous=False)
-    _need(block_scores, torch.float32, "block_scores")
+    if block_scores is not None:
+        _need(block_scores, torch.float32, "block_scores")
     _need(block_idx, torch.int32, "block_idx")
     tok, head = _strides_tok_head(ik, "ik")
     if workspace is None:
-        workspace = index_select_workspace(shape, batch.n_seqs, iq.device)
+        workspace = index_select_workspace(shape, batch, iq.device)
     _check(lib().msa_index_select(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(iq), _ptr(ik), tok, head,
-                                  _ptr(block_scores), block_scores.shape[-1], _ptr(block_idx), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+                                  _ptr(block_scores), 0 if block_scores is None else block_scores.shape[-1],
+                                  _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
 
 
 def msa_prefill(shape: Shape, batch: Batch, q, k, v, block_idx, out, lse=None, stream=None):
@@ -453,7 +465,9 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
              stream=None, fused: bool = False, kv8: KV8 | None = None, kvt: KVTiled | None = None) -> dict:
     """Enqueue the whole path -- index scores, selection, attention -- on
     device tensors t = {q, k, v, iq, ik}.  mode: "prefill" or "decode".
-    fused: steps 1-3 through msa_index_select.
+    fused: steps 1-3 through msa_index_select (for batches of more than 16
+    rows in a sequence with top_k <= 16, the fused prompt-chunk kernel: no
+    block scores are written then).
     kv8: attend over this int8 cache instead of t["k"], t["v"].
     kvt: attend over this tiled cache instead of t["k"], t["v"].
     Output buffers are allocated unless given in `out`."""
@@ -470,8 +484,10 @@ def run_path(shape: Shape, batch: Batch, t: dict, mode: str = "prefill", out: di
         out["lse"] = torch.empty(rows, H * GROUP, dtype=torch.float32, device=dev)
     if fused:
         if "select_workspace" not in out:
-            out["select_workspace"] = index_select_workspace(shape, batch.n_seqs, dev)
-        msa_index_select(shape, batch, t["iq"], t["ik"], out["block_scores"], out["block_idx"],
+            out["select_workspace"] = index_select_workspace(shape, batch, dev)
+        # prompt chunks: no scores written (block_scores is left as allocated)
+        scores = None if chunk_select_eligible(shape, batch) else out["block_scores"]
+        msa_index_select(shape, batch, t["iq"], t["ik"], scores, out["block_idx"],
                          out["select_workspace"], stream)
     else:
         msa_index_scores(shape, batch, t["iq"], t["ik"], out["block_scores"], stream)

@@ -198,9 +198,12 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch, const floa
     return launched(msa::launch_select_blocks(a, static_cast<hipStream_t>(stream)), "select_blocks");
 }
 
-size_t msa_index_select_workspace_bytes(const msa_shape *shape, int32_t n_seqs) {
-    if (!shape || check_shape(shape) || n_seqs < 0) return 0;
-    return msa::index_select_workspace_bytes(n_seqs, shape->n_kv_heads);
+size_t msa_index_select_workspace_bytes(const msa_shape *shape, const msa_batch *batch) {
+    bool empty = false;
+    if (!shape || check_shape(shape) || check_batch(batch, shape, &empty)) return 0;
+    if (empty) return msa::kIndexSelectCountBytes;
+    return msa::index_select_workspace_bytes(batch->n_seqs, shape->n_kv_heads, batch->total_rows, batch->max_rows,
+                                             batch->max_seq_len, shape->top_k);
 }
 
 int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
@@ -210,28 +213,35 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     bool empty;
     if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
     if (empty) return ok();
-    if (!iq || !ik || !block_scores || !block_idx)
-        return fail(MSA_ERR_INVALID, "iq/ik/block_scores/block_idx must not be NULL");
+    if (!iq || !ik || !block_idx) return fail(MSA_ERR_INVALID, "iq/ik/block_idx must not be NULL");
     if (ik_tok_stride < msa::kIndexDim || ik_head_stride < 0 ||
         (ik_head_stride > 0 && ik_head_stride < msa::kIndexDim))
         return fail(MSA_ERR_INVALID, "ik strides (%lld, %lld) overlap a %d-element row",
                     (long long)ik_tok_stride, (long long)ik_head_stride, msa::kIndexDim);
     if (!aligned16(iq) || !aligned16(ik) || (ik_tok_stride * 2) % 16 || (ik_head_stride * 2) % 16)
         return fail(MSA_ERR_INVALID, "iq/ik rows must be 16-byte aligned");
+    const int H = shape->n_kv_heads;
+    // NULL block_scores: the prompt-chunk kernel, whose scores never reach memory
+    const bool chunk = !block_scores;
+    if (chunk && !msa::chunk_select_eligible(batch->n_seqs, H, batch->max_rows, shape->top_k))
+        return fail(MSA_ERR_INVALID, "block_scores may be NULL only for batches with more than 16 rows in a "
+                    "sequence, top_k <= %d and at most %lld (sequence, key head, 256-row tile) units",
+                    msa::kChunkMaxTopK, (long long)msa::kIndexSelectCounters);
     const int64_t need = ((int64_t)batch->max_seq_len + msa::kBlock - 1) / msa::kBlock;
-    if (bs_stride < need)
+    if (!chunk && bs_stride < need)
         return fail(MSA_ERR_INVALID, "bs_stride=%d < ceil(max_seq_len/64)=%lld", bs_stride, (long long)need);
-    if (need > msa::kMaxSelectBlocks)
+    if (!chunk && need > msa::kMaxSelectBlocks)
         return fail(MSA_ERR_UNSUPPORTED, "max_seq_len=%d: selection supports at most %d blocks (%d keys)",
                     batch->max_seq_len, msa::kMaxSelectBlocks, msa::kMaxSelectBlocks * msa::kBlock);
-    const size_t ws_need = msa::index_select_workspace_bytes(batch->n_seqs, shape->n_kv_heads);
+    const size_t ws_need = msa::index_select_workspace_bytes(batch->n_seqs, H, batch->total_rows,
+                                                             batch->max_rows, batch->max_seq_len, shape->top_k);
     if (!workspace || workspace_bytes < ws_need)
         return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws_need);
     if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID, "workspace must be 256-byte aligned");
     if ((rc = check_device())) return rc;
     msa::IndexArgs a;
     a.b = to_dev(batch);
-    a.H = shape->n_kv_heads;
+    a.H = H;
     a.iq = static_cast<const uint16_t *>(iq);
     a.ik = static_cast<const uint16_t *>(ik);
     a.ik_tok = ik_tok_stride;
@@ -239,6 +249,16 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     a.scores = block_scores;
     a.bs_stride = bs_stride;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (chunk) {
+        msa::ChunkSelect c{};
+        c.top_k = shape->top_k;
+        c.idx = block_idx;
+        c.count = static_cast<unsigned *>(workspace);
+        c.cand = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(workspace) + msa::kIndexSelectCountBytes);
+        c.tiles = msa::chunk_tiles(batch->max_rows);
+        msa::chunk_splits(batch->n_seqs, H, batch->max_rows, batch->max_seq_len, &c.splits, &c.per_split);
+        return launched(msa::launch_index_select_chunk(a, c, st), "index_select_chunk");
+    }
     if (batch->max_rows > 1) {
         // Several rows per sequence: the last workgroup would select them one
         // after another, which costs more than a second launch that selects

@@ -258,6 +258,295 @@ __global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int block
     }
 }
 
+// ---- Selection fused into the prompt-chunk indexer ----
+//
+// The candidate blocks of a (sequence, key head, 256-row tile) -- every block
+// below the tile's last row's local block -- are split over c.splits
+// workgroups.  Each computes its blocks' maxima as index_scores_tiled does
+// (the same operands, products and order, so the same bits) and, instead of
+// storing them, folds each 16 of them into a sorted list of the 16 best
+// (score, block) pairs of every row, in registers.  The lists are published
+// with agent-scope stores; the last workgroup of the tile to count in merges
+// each row's lists and writes its selection.  Each row's kept set is the top
+// top_k-1 of the union of the lists: every block of the row's top top_k-1 is
+// in the top of its own split with the same tie order, so the result equals
+// one pass over all blocks (and msa_select_blocks on the stored scores).
+//
+// A candidate is one 64-bit value: the score's order key in the high word and
+// 0x7fffffff minus the block in the low word, so a larger value is a better
+// candidate (higher score, then lower block: the selection's tie rule), and 0
+// (an empty slot) is below every real one.
+__device__ __forceinline__ uint64_t cand_pack(uint32_t key, int blk) {
+    return ((uint64_t)key << 32) | (uint32_t)(0x7fffffff - blk);
+}
+__device__ __forceinline__ int cand_block(uint64_t c) { return 0x7fffffff - (int)(uint32_t)c; }
+
+// Compare-exchange leaving a >= b (kDesc) or a <= b.
+template <bool kDesc, typename T>
+__device__ __forceinline__ void cex(T &a, T &b) {
+    const bool sw = kDesc ? a < b : b < a;
+    const T x = sw ? b : a, y = sw ? a : b;
+    a = x;
+    b = y;
+}
+
+// Bitonic sort of 16 values, descending (kDesc) or ascending.
+template <bool kDesc, typename T>
+__device__ __forceinline__ void sort16(T (&v)[16]) {
+#pragma unroll
+    for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    if (((i & k) == 0) != kDesc) cex<false>(v[i], v[l]);
+                    else cex<true>(v[i], v[l]);
+                }
+            }
+}
+
+// r (descending) becomes the 16 largest of r and q, descending; q is given
+// ascending.  The elementwise maxima of a descending and an ascending
+// sequence hold the 16 largest of both as a bitonic sequence, which the
+// four-stage half-cleaner cascade sorts.
+__device__ __forceinline__ void merge_top16(uint64_t (&r)[16], const uint64_t (&q_asc)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = r[i] < q_asc[i] ? q_asc[i] : r[i];
+#pragma unroll
+    for (int j = 8; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int l = i ^ j;
+            if (l > i) cex<true>(r[i], r[l]);
+        }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void index_select_tiled(IndexArgs a, ChunkSelect c) {
+    constexpr int kRowsWave = 16 * NT;
+    constexpr int kRowsWg = kRowsWave * kTiledWaves;
+    static_assert(kRowsWg == kChunkRowsWg && kChunkList == 16, "tile and list sizes");
+    static_assert(NT * 16 == kWave, "one wave row per lane");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][kBlock * kLdsRow];
+    __shared__ float otile[kTiledWaves][kRowsWave * 16];
+    __shared__ int is_last;
+
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int lg = lane >> 4, lr = lane & 15;
+    const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
+    if (s >= a.b.n_seqs) return;
+    const int row0 = a.b.cu_rows[s];
+    const int rows_s = a.b.cu_rows[s + 1] - row0;
+    const int L = a.b.seq_lens[s];
+    // a malformed sequence, or a tile past its rows: every split of the tile
+    // returns alike, so no counter is touched
+    if (rows_s <= 0 || rows_s > L || L > a.b.max_seq_len) return;
+    const int tile = blockIdx.y, tile0 = tile * kRowsWg;
+    if (tile0 >= rows_s) return;
+    const int tile_rows = min(kRowsWg, rows_s - tile0);
+    const int p_base = L - rows_s;                       // position of row 0 of the sequence
+    const int l_last = (p_base + tile0 + tile_rows - 1) / kBlock;   // candidates lie below it
+    const int split = blockIdx.x;
+    const int b_begin = split * c.per_split;
+    const int b_end = min(b_begin + c.per_split, l_last);
+    const int nblk = max(b_end - b_begin, 0);
+    const int64_t kv0 = seq_token0(a.b, s);
+
+    // This wave's rows (B operand in VGPRs); after the reduce-and-scatter,
+    // lane l holds row wrow0 + l.
+    const int wrow0 = tile0 + wave * kRowsWave;
+    u32x4 bq[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rl = wrow0 + nt * 16 + lr;
+        if (rl < rows_s) {
+            const uint16_t *src = a.iq + ((int64_t)(row0 + rl) * a.H + g) * kIndexDim + 16 * lg;
+            bq[nt][0] = load16(src);
+            bq[nt][1] = load16(src + 8);
+        } else {
+            bq[nt][0] = zero16();
+            bq[nt][1] = zero16();
+        }
+    }
+    const int my_row = wrow0 + lane;
+    const bool my_valid = my_row < rows_s;
+    const int my_p = p_base + my_row;
+    const int my_l = my_p / kBlock;                      // the row's local block (not a candidate)
+
+    // First token of the workgroup's blocks, three windows of 64 (lane q of
+    // window w: block b_begin + 64w + q, clamped to the sequence's blocks),
+    // looked up once so the loop's loads never wait on a page-table read.
+    const int last_blk = (L - 1) / kBlock;
+    const int64_t tw0 = block_token0(a.b, s, kv0, min(b_begin + lane, last_blk));
+    const int64_t tw1 = block_token0(a.b, s, kv0, min(b_begin + 64 + lane, last_blk));
+    const int64_t tw2 = block_token0(a.b, s, kv0, min(b_begin + 128 + lane, last_blk));
+    const int st_key = threadIdx.x >> 2, st_piece = threadIdx.x & 3;
+    const uint16_t *ik_g = a.ik + (int64_t)g * a.ik_head + 16 * st_piece;
+    struct Stage {
+        u32x4 x0, x1;
+    };
+    auto gload = [&](int b, Stage &r) {
+        const int q = b - b_begin;                       // 0 <= q < per_split <= 192
+        const int w = q >> 6, qq = q & 63;
+        auto at = [&](int64_t t) {                       // lane qq's value of t (wave-uniform)
+            return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uint64_t)t >> 32), qq) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)t, qq));
+        };
+        const int64_t tok0 = w == 0 ? at(tw0) : (w == 1 ? at(tw1) : at(tw2));
+        const int j = min(b * kBlock + st_key, L - 1);
+        const uint16_t *src = ik_g + (tok0 + (j - b * kBlock)) * a.ik_tok;
+        r.x0 = load16(src);
+        r.x1 = load16(src + 8);
+    };
+    auto sstore = [&](int buf, const Stage &r) {
+        uint8_t *dst = &lds[buf][st_key * kLdsRow + 32 * st_piece];
+        *reinterpret_cast<u32x4 *>(dst) = r.x0;
+        *reinterpret_cast<u32x4 *>(dst + 16) = r.x1;
+    };
+
+    float *out_tile = otile[wave];
+    // Every candidate block lies wholly below the row's position, so its
+    // maximum needs no causal mask; blocks at or past a row's local block are
+    // computed like the others and dropped by the row's filter.
+    auto step = [&](int i, Stage &r, bool sync) {
+        const int b = b_begin + i;
+        const uint8_t *buf = lds[i & 3];
+        u32x4 av[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint8_t *src = buf + (16 * mt + lr) * kLdsRow + 32 * lg;
+            av[mt][0] = *reinterpret_cast<const u32x4 *>(src);
+            av[mt][1] = *reinterpret_cast<const u32x4 *>(src + 16);
+        }
+        float m[NT];
+        floatx4 prev[4];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            floatx4 cur[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma_16x16x32(av[mt][0], bq[nt][0], acc);
+                cur[mt] = mfma_16x16x32(av[mt][1], bq[nt][1], acc);
+            }
+            if (nt == 1) {
+                sstore((i + 2) & 3, r);
+                gload(min(b + 4, b_end - 1), r);
+            }
+            if (nt > 0) m[nt - 1] = lane_max_64<false>(prev, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) prev[mt] = cur[mt];
+        }
+        m[NT - 1] = lane_max_64<false>(prev, 0, 0);
+        const float v = max_scatter_lane_groups(m[0], m[1], m[2], m[3]);
+        if (sync) __syncthreads();
+        out_tile[(i & 15) * kRowsWave + lane] = v;
+    };
+
+    // The row's running list: the 16 best candidates so far, descending.
+    uint64_t best[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) best[q] = 0ull;
+    // Fold the batch of n (<= 16) maxima in the tile slots (blocks base ..
+    // base+n-1) into the list.
+    auto fold_batch = [&](int base, int n) {
+        wave_lds_sync();
+        uint64_t x[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int blk = base + q;
+            const float v = out_tile[q * kRowsWave + lane];
+            x[q] = (q < n && blk < my_l) ? cand_pack(order_key(v), blk) : 0ull;
+        }
+        wave_lds_sync();   // the slots are read before the next batch overwrites them
+        sort16<false>(x);
+        merge_top16(best, x);
+    };
+
+    Stage r0, r1;
+    if (nblk > 0) {
+        gload(b_begin, r0);
+        gload(min(b_begin + 1, b_end - 1), r1);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        force_ready(bq[nt][0]);
+        force_ready(bq[nt][1]);
+    }
+    if (nblk > 0) {
+        sstore(0, r0);
+        sstore(1, r1);
+        gload(min(b_begin + 2, b_end - 1), r0);
+        gload(min(b_begin + 3, b_end - 1), r1);
+    }
+    __syncthreads();
+    int i = 0;
+    for (; i + 1 < nblk; i += 2) {
+        step(i, r0, false);
+        step(i + 1, r1, true);
+        if (((i + 1) & 15) == 15 || i + 1 == nblk - 1) fold_batch(b_begin + ((i + 1) & ~15), ((i + 1) & 15) + 1);
+    }
+    if (i < nblk) {
+        step(i, r0, false);
+        fold_batch(b_begin + (i & ~15), (i & 15) + 1);
+    }
+
+    // Publish the list (agent-scope stores: written through this XCD's L2),
+    // wait for the stores, then count the workgroup in.  The language's model
+    // orders none of this; gfx950's sc1 stores and loads and its
+    // device-level atomic add do (see decode_kernel).
+    uint64_t *mine = c.cand + (((int64_t)(row0 + my_row) * a.H + g) * c.splits + split) * kChunkList;
+    if (my_valid) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) __hip_atomic_store(mine + q, best[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unsigned *counter = c.count + ((int64_t)s * a.H + g) * c.tiles + tile;
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    if (threadIdx.x == 0)   // leave the counter at zero for the next call
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!my_valid) return;
+
+    // The last workgroup: each lane merges its row's lists from every split.
+    const uint64_t *lists = c.cand + ((int64_t)(row0 + my_row) * a.H + g) * c.splits * kChunkList;
+    for (int sp = 0; sp < c.splits; ++sp) {
+        if (sp == split) continue;
+        uint64_t q_asc[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            q_asc[15 - q] = __hip_atomic_load(lists + sp * kChunkList + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        merge_top16(best, q_asc);
+    }
+    const int top_k = c.top_k, nb = my_l + 1;
+    int32_t *out = c.idx + ((int64_t)(row0 + my_row) * a.H + g) * top_k;
+    int f[16];
+    if (nb <= top_k) {          // every causal block
+#pragma unroll
+        for (int q = 0; q < 16; ++q) f[q] = q < nb ? q : -1;
+    } else {                    // the best top_k-1, then the local block, ascending
+#pragma unroll
+        for (int q = 0; q < 15; ++q) f[q] = q < top_k - 1 ? cand_block(best[q]) : 0x7fffffff;
+        f[15] = my_l;
+        sort16<false>(f);
+    }
+    if (top_k == 16 && ((uintptr_t)c.idx & 15u) == 0) {
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) *reinterpret_cast<int4 *>(out + q) = make_int4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (q < top_k) out[q] = f[q];
+    }
+}
+
 // tok0: token of the block's first key; keys past the sequence end read its
 // last key (in the same block) and are masked.
 __device__ __forceinline__ void window_load_block(u32x4 (&av)[4][2], const uint16_t *ik_g, int64_t tok0,
@@ -424,6 +713,12 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
         dim3 grid((a.bs_stride + kTiledBlocks - 1) / kTiledBlocks, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
         hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, kTiledBlocks);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, hipStream_t st) {
+    const dim3 grid((unsigned)c.splits, (unsigned)c.tiles, (unsigned)(a.b.n_seqs * a.H));
+    hipLaunchKernelGGL(index_select_tiled<4>, grid, dim3(256), 0, st, a, c);
     return hipGetLastError();
 }
 

@@ -73,8 +73,62 @@ struct SelectTail {
     unsigned *count;             // one arrival counter per (sequence, key head); zero between calls
     int cap;                     // staged keys per row (set by the launcher)
 };
-inline size_t index_select_workspace_bytes(int64_t n_seqs, int H) {
-    return (size_t)((n_seqs * H * 4 + 255) / 256 * 256);
+
+// Selection fused into the prompt-chunk indexer: the candidate blocks of each
+// (sequence, key head, 256-row tile) are split over `splits` workgroups of
+// `per_split` blocks; each keeps a sorted list of its kChunkList best
+// (score, block) pairs per row and publishes it, and the last workgroup of
+// the tile merges the lists and writes the selection.
+constexpr int kChunkRowsWg = 256;
+constexpr int kChunkList = 16;          // list length: top_k - 1 <= 15 candidates plus one spare
+constexpr int kChunkMaxTopK = 16;
+constexpr int kChunkMaxPerSplit = 192;  // blocks a workgroup's page lookups cover
+struct ChunkSelect {
+    int top_k;
+    int32_t *idx;                // [total_rows, H, top_k]
+    unsigned *count;             // one counter per (sequence, key head, row tile); zero between calls
+    uint64_t *cand;              // [total_rows, H, splits, kChunkList] packed (key, block) pairs
+    int splits, per_split, tiles;
+};
+// Workspace of msa_index_select: a fixed region of arrival counters (one per
+// (sequence, key head) for one-row batches, per (sequence, key head, row
+// tile) for prompt chunks), then the prompt chunks' candidate lists.  The
+// counters' place does not depend on the batch, so one zeroed workspace
+// serves batches of any size it covers.
+constexpr size_t kIndexSelectCountBytes = 256 * 1024;
+constexpr int64_t kIndexSelectCounters = kIndexSelectCountBytes / 4;
+inline int chunk_tiles(int max_rows) { return (max_rows + kChunkRowsWg - 1) / kChunkRowsWg; }
+// Splits of the key range: about 512 workgroups in all (two per CU), at most
+// one per 16 blocks, at most kChunkMaxPerSplit blocks each.
+inline void chunk_splits(int n_seqs, int H, int max_rows, int max_seq_len, int *splits, int *per_split) {
+    const int64_t tiles = chunk_tiles(max_rows);
+    const int nbk = (max_seq_len + 63) / 64;
+    const int64_t units = (int64_t)n_seqs * H * tiles;
+    int S = (int)((512 + units - 1) / units);
+    S = S < 1 ? 1 : S;
+    const int s_max = (nbk + 15) / 16 > 0 ? (nbk + 15) / 16 : 1;
+    S = S > s_max ? s_max : S;
+    int per = (nbk + S - 1) / S;
+    while (per > kChunkMaxPerSplit) {
+        ++S;
+        per = (nbk + S - 1) / S;
+    }
+    *splits = S;
+    *per_split = per > 0 ? per : 1;
+}
+// Whether msa_index_select can run a batch through the fused prompt-chunk kernel.
+inline bool chunk_select_eligible(int n_seqs, int H, int max_rows, int top_k) {
+    return max_rows > 16 && top_k <= kChunkMaxTopK && (int64_t)n_seqs * H * chunk_tiles(max_rows) <= kIndexSelectCounters;
+}
+inline size_t index_select_workspace_bytes(int n_seqs, int H, int total_rows, int max_rows, int max_seq_len,
+                                           int top_k) {
+    size_t b = kIndexSelectCountBytes;
+    if (chunk_select_eligible(n_seqs, H, max_rows, top_k)) {
+        int S, per;
+        chunk_splits(n_seqs, H, max_rows, max_seq_len, &S, &per);
+        b += (size_t)total_rows * H * S * kChunkList * sizeof(uint64_t);
+    }
+    return b;
 }
 
 // Decode partial: m[16], l[16], acc[16][128] (fp32) for one workgroup's kept blocks.
@@ -139,6 +193,7 @@ hipError_t launch_pack_kv_rows(const PackRowsArgs &a, hipStream_t st);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);
+hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, hipStream_t st);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st);
 

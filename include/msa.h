@@ -146,33 +146,47 @@ int msa_select_blocks(const msa_shape *shape, const msa_batch *batch,
                       int32_t *block_idx, void *stream);
 
 /*
- * Steps 1-3 in one call, for decode steps and verify windows: the index
- * scores and max-pool of msa_index_scores, then the selection of
- * msa_select_blocks.  When every sequence has one row, both run in one
- * launch: the key axis of every (sequence, key head) is spread over many
- * workgroups and the last of them to finish (an arrival counter in
- * `workspace`) selects the row, so there is no second launch and the scores
- * are read back while still in the caches.  A batch with several rows in a
- * sequence takes the two launches of msa_index_scores and msa_select_blocks
- * (selecting the rows in parallel is faster than the last workgroup selecting
- * them one by one).  Either way block_idx is bit-identical to
- * msa_index_scores followed by msa_select_blocks, and block_scores is written
- * as by msa_index_scores (it is the exchange buffer).  The computation is the
- * one of steps 1-3 (TensorFold pull request 1388, commit adding the
- * minimax_m3 family: index scores and a top-16 block selection per row and
- * key head); the pages keep the block scores as a buffer of their own between
- * the two steps (a later commit of the same pull request shares its memory
- * with other buffers).  Running both in one launch is this library's
- * addition, for decode latency.
+ * Steps 1-3 in one call: the index scores and max-pool of msa_index_scores,
+ * then the selection of msa_select_blocks, with block_idx bit-identical to
+ * those two calls.  The computation is the one of steps 1-3 (TensorFold pull
+ * request 1388, commit adding the minimax_m3 family: index scores and a
+ * top-16 block selection per row and key head); the pages keep the block
+ * scores as a buffer of their own between the two steps (a later commit of
+ * the same pull request shares its memory with other buffers, so that
+ * 4,096-row chunks fit).  Doing both in one launch is this library's
+ * addition.  Three cases:
+ *   - block_scores == NULL (batches with more than 16 rows in a sequence and
+ *     top_k <= 16: prompt chunks): one launch in which the scores never reach
+ *     memory.  The candidate blocks of every (sequence, key head, 256-row
+ *     tile) are split over a few workgroups; each keeps, per row, a sorted
+ *     list of its 16 best (score, block) pairs, publishes it in `workspace`,
+ *     and the last workgroup of the tile merges the lists (every kept block
+ *     is in its own split's list with the same tie order) and writes the
+ *     selection.
+ *   - block_scores != NULL, one row per sequence (decode steps): one launch;
+ *     the key axis of every (sequence, key head) is spread over many
+ *     workgroups, the last of which (an arrival counter in `workspace`)
+ *     selects the row from the scores, which it reads back while they are
+ *     still in the caches.  block_scores is written as by msa_index_scores
+ *     (it is the exchange buffer).
+ *   - block_scores != NULL, several rows in a sequence: the two launches of
+ *     msa_index_scores and msa_select_blocks (selecting the rows in parallel
+ *     is faster than a last workgroup selecting them one by one).
  *   workspace   device, 256-byte aligned, msa_index_select_workspace_bytes()
- *               bytes: one arrival counter per (sequence, key head).  Must be
- *               zero before the first call; every call leaves it zero.  Calls
- *               that share a workspace must not overlap in time.  Required
- *               (and checked) for every batch, used by one-row batches only.
- * Errors: as msa_index_scores and msa_select_blocks; a missing or short
- * workspace -> MSA_ERR_WORKSPACE.
+ *               bytes for the batch: a fixed 256 KiB region of arrival
+ *               counters, then (for batches the NULL-score case can take) the
+ *               candidate lists, 128 bytes per (row, key head, split).  The
+ *               counters must be zero before the first call (allocate it
+ *               zeroed); every completed call leaves them zero, whatever the
+ *               batch, so one workspace serves every batch it is large
+ *               enough for.  Calls that share a workspace must not overlap in
+ *               time.  Required (and checked) for every batch.
+ * Errors: as msa_index_scores and msa_select_blocks; NULL block_scores for a
+ * batch outside the first case -> MSA_ERR_INVALID; a missing or short
+ * workspace -> MSA_ERR_WORKSPACE.  msa_index_select_workspace_bytes returns 0
+ * for an invalid shape or batch (host fields only are read).
  */
-size_t msa_index_select_workspace_bytes(const msa_shape *shape, int32_t n_seqs);
+size_t msa_index_select_workspace_bytes(const msa_shape *shape, const msa_batch *batch);
 int msa_index_select(const msa_shape *shape, const msa_batch *batch,
                      const void *iq, const void *ik, int64_t ik_tok_stride, int64_t ik_head_stride,
                      float *block_scores, int32_t bs_stride, int32_t *block_idx,

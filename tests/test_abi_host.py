@@ -180,16 +180,29 @@ def test_select_rejects_contexts_beyond_the_staging_limit():
 def test_index_select_checks():
     L = msa.lib()
     sh = msa.make_shape(2)
-    assert msa.msa_index_select_workspace_bytes(sh, 3) == 256
-    assert msa.msa_index_select_workspace_bytes(sh, 100) == 1024     # 100 * 2 * 4 -> 800 -> 1024
-    call = lambda b, ws, nbytes, bs=2: L.msa_index_select(
+    counters = 256 * 1024
+    # decode-shaped batches (<= 16 rows): the counter region only
+    assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=3, total_rows=3, max_rows=1)) == counters
+    assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=2, total_rows=32, max_rows=16)) == counters
+    # prompt chunks: + 128 bytes of candidate lists per (row, key head, split);
+    # 1 sequence x 2 heads x 1 tile -> 256 splits wanted, at most one per 16 blocks
+    b = FakeBatch(n_seqs=1, total_rows=300, max_rows=300, max_seq_len=5000)   # 79 blocks -> 5 splits
+    assert msa.msa_index_select_workspace_bytes(sh, b) == counters + 300 * 2 * 5 * 128
+    assert msa.msa_index_select_workspace_bytes(msa.make_shape(2, top_k=17), b) == counters
+    assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=-1)) == 0
+    ws_one = counters
+    call = lambda b, ws, nbytes, bs=2, scores=12288: L.msa_index_select(
         ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), ctypes.c_void_p(8192), 64, 0,
-        ctypes.c_void_p(12288), bs, ctypes.c_void_p(16384), ctypes.c_void_p(ws) if ws else None, nbytes, None)
-    assert call(FakeBatch(), 65536, 255) == -3
-    assert call(FakeBatch(), 0, 256) == -3
-    assert call(FakeBatch(), 65536 + 4, 256) == -1 and "aligned" in _err()
+        ctypes.c_void_p(scores) if scores else None, bs, ctypes.c_void_p(16384),
+        ctypes.c_void_p(ws) if ws else None, nbytes, None)
+    assert call(FakeBatch(), 65536, ws_one - 1) == -3
+    assert call(FakeBatch(), 0, ws_one) == -3
+    assert call(FakeBatch(), 65536 + 4, ws_one) == -1 and "aligned" in _err()
     big = FakeBatch(max_seq_len=(1 << 20) + 64)
-    assert call(big, 65536, 256, bs=16385) == -2 and "16384" in _err()
+    assert call(big, 65536, ws_one, bs=16385) == -2 and "16384" in _err()
+    # NULL scores: only for batches of > 16 rows in a sequence (FakeBatch has 4)
+    assert call(FakeBatch(), 65536, ws_one, scores=0) == -1 and "NULL" in _err()
+    assert call(b, 65536, counters, scores=0) == -3     # the candidate lists do not fit
 
 
 def test_paged_batch_checks():

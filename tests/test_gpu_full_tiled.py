@@ -40,7 +40,7 @@ def bench_calls(case, t, batch, o, kvt):
         msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"])
         msa.msa_prefill_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"])
     else:
-        ws = msa.index_select_workspace(shape, batch.n_seqs)
+        ws = msa.index_select_workspace(shape, batch)
         msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"], o["block_idx"], ws)
         msa.msa_decode_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"],
                              msa.decode_workspace(shape, batch.total_rows))

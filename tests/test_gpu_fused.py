@@ -68,7 +68,7 @@ def test_fused_workspace_reuse_and_counters():
     shape = shape_of(case)
     batch = msa.Batch(case.seq_lens, case.rows)
     t = device_tensors(case)
-    ws = msa.index_select_workspace(shape, batch.n_seqs)
+    ws = msa.index_select_workspace(shape, batch)
     res = []
     for _ in range(3):
         s = torch.empty(batch.total_rows, 2, batch.n_blocks, dtype=torch.float32, device="cuda")
@@ -80,13 +80,20 @@ def test_fused_workspace_reuse_and_counters():
     assert int(ws.view(torch.int32).abs().sum().item()) == 0
 
 
-def test_prompt_chunks_take_two_launches():
-    """More than 16 rows in a sequence (a prompt chunk): the same results as
-    the two separate steps."""
+def test_prompt_chunk_with_scores_takes_two_launches():
+    """More than 16 rows in a sequence with block_scores given: the two
+    separate steps' launches, scores written as msa_index_scores writes them."""
     case = make_case("chunk", [3000, 900], [300, 1], 2, seed=208)
-    a, b = _both(case)
-    assert torch.equal(a["block_scores"], b["block_scores"])
-    assert torch.equal(a["block_idx"], b["block_idx"])
+    shape = shape_of(case)
+    batch = msa.Batch(case.seq_lens, case.rows)
+    t = device_tensors(case)
+    a = gpu_run(case, "decode", t=t)
+    s = torch.empty(batch.total_rows, 2, batch.n_blocks, dtype=torch.float32, device="cuda")
+    i = torch.empty(batch.total_rows, 2, case.top_k, dtype=torch.int32, device="cuda")
+    msa.msa_index_select(shape, batch, t["iq"], t["ik"], s, i)
+    torch.cuda.synchronize()
+    assert torch.equal(a["block_scores"], s.cpu())
+    assert torch.equal(a["block_idx"], i.cpu())
 
 
 def test_max_context_one_row():
@@ -113,7 +120,7 @@ def test_fused_reused_buffers_see_new_scores():
     assert not torch.equal(want[0], want[1])
     s = torch.empty(batch.total_rows, 2, batch.n_blocks, dtype=torch.float32, device="cuda")
     i = torch.empty(batch.total_rows, 2, cases[0].top_k, dtype=torch.int32, device="cuda")
-    ws = msa.index_select_workspace(shape, batch.n_seqs)
+    ws = msa.index_select_workspace(shape, batch)
     for it in range(6):
         k = it % 2
         msa.msa_index_select(shape, batch, ts[k]["iq"], ts[k]["ik"], s, i, ws)
