@@ -221,13 +221,16 @@ class Workload:
     one step."""
 
     def __init__(self, torch, msa, dev, name, case, mode, n_rep, *, fused, tiled=True, paged=False,
-                 head_major=False, kv8=False):
+                 head_major=False, kv8=False, ik_head_major=False):
         self.name, self.case, self.mode, self.fused = name, case, mode, fused
         self.kv8, self.msa = kv8, msa
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
         if head_major:
             for n in ("k", "v", "ik"):
                 base[n] = base[n].permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        elif ik_head_major and not paged:
+            base["ik"] = base["ik"].permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        self.ik_layout = "head-major" if (head_major or (ik_head_major and not paged)) else "token-major"
         page_table = None
         if paged:
             from workloads import to_pages
@@ -591,6 +594,9 @@ def main():
     ap.add_argument("--kv-layout", choices=("tiled", "strided"), default="tiled",
                     help="tiled: the library's tiled bf16 cache (msa_kv_tiled; each step packs its own new "
                          "keys into it); strided: the plain [tokens, heads, 128] cache")
+    ap.add_argument("--ik-layout", choices=("token-major", "head-major"), default="token-major",
+                    help="the index-key cache: [tokens, heads, 64] (token-major) or [heads, tokens, 64] "
+                         "(head-major, passed as a strided [tokens, heads, 64] view)")
     ap.add_argument("--overlap", choices=("indexer", "free", "none"), default="indexer",
                     help="the long row's calls: on a second stream starting with the chunk's part of each step "
                          "(indexer, the default: beside the chunk's cache write, indexer and selection), on a "
@@ -624,7 +630,8 @@ def main():
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     cases = {"chunk": config("chunk") if args.locality is None else config("chunk", locality=args.locality),
              "long": config("long")}
-    opts = dict(tiled=tiled, paged=args.paged, head_major=args.head_major, kv8=args.kv8)
+    ik_hm = args.ik_layout == "head-major"
+    opts = dict(tiled=tiled, paged=args.paged, head_major=args.head_major, kv8=args.kv8, ik_head_major=ik_hm)
     wl = {"chunk": Workload(torch, msa, dev, "chunk", cases["chunk"], "prefill", CONFIG_PLAN["chunk"][2],
                             fused=False, **opts),
           "long": Workload(torch, msa, dev, "long", cases["long"], "decode", CONFIG_PLAN["long"][2],
@@ -719,6 +726,7 @@ def main():
                    "kv_layout": ("paged (64-token pages, random order)" if args.paged else
                                  "contiguous, head-major" if args.head_major else "contiguous, token-major"),
                    "kv_cache": wl["chunk"].kv_cache,
+                   "index_key_cache": wl["chunk"].ik_layout,
                    "index_queries": ("i.i.d. N(0,1) per row" if args.locality is None else
                                      f"secondary workload: AR(1) across the chunk's rows, a = {args.locality}")},
         "inputs": {"generator": "torch.Generator (CPU) seeded per workload, randn in fp32 rounded to bf16",
@@ -752,7 +760,8 @@ def main():
             if name in wl:
                 w = wl[name]
             else:
-                w = Workload(torch, msa, dev, name, config(name), mode, n_rep, fused=fused, tiled=tiled)
+                w = Workload(torch, msa, dev, name, config(name), mode, n_rep, fused=fused, tiled=tiled,
+                             ik_head_major=ik_hm)
             print(f"[bench] config {name}: {steps} steps back to back", file=sys.stderr, flush=True)
             configs[name] = config_entry(torch, w, steps, block, measured, kv8=args.kv8 and name in wl)
             if name not in wl:

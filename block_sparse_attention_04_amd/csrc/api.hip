@@ -277,6 +277,8 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     t.top_k = shape->top_k;
     t.idx = block_idx;
     t.count = static_cast<unsigned *>(workspace);
+    t.wmax = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::kIndexSelectCountBytes);
+    t.ranges = msa::window_ranges(batch->max_seq_len);
     return launched(msa::launch_index_select(a, t, st), "index_select");
 }
 

@@ -576,31 +576,155 @@ __device__ __forceinline__ float window_lane_max(const u32x4 (&av)[4][2], u32x4 
                                                            : lane_max_64<false>(acc, key0, prow);
 }
 
-// Each wave owns 4 consecutive blocks: all their loads go out before the
-// first MFMA (a block past the sequence re-reads its last computed block and
-// is discarded), and lane group lg ends up holding block b_begin + lg.
-constexpr int kWindowBlocks = 4;
+// Each wave owns kWindowBlocks = 4 consecutive blocks: all their loads go
+// out before the first MFMA (a block past the sequence re-reads its last
+// computed block and is discarded), and lane group lg ends up holding block
+// b_begin + lg.
+
+// The selection of one one-row unit by the wave that finished last, from the
+// range maxima and scores every wave published (agent-scope loads).  The
+// range maxima give T0, a lower bound on the (top_k-1)-th best candidate
+// score T: the top_k-1 largest range maxima belong to distinct ranges, each
+// holding a candidate at least that large.  Every candidate >= T then lies in
+// a range whose maximum is >= T0, so only those ranges' scores are read
+// (usually top_k-1 of them, at most 64 here), in ascending block order, and
+// the top top_k-1 among them -- ties to the lower block -- are the selection.
+// More than 64 such ranges (mass ties) take an exact search over every
+// candidate score instead, streamed from memory.
+__device__ __forceinline__ void window_select_tail(const float *scores, const float *wmax, int n, int top_k,
+                                                   int32_t *out, int32_t *cr) {
+    const int lane = threadIdx.x & 63;
+    const int nb = n + 1, need = top_k - 1;
+    if (nb <= top_k || need == 0) {
+        if (lane < top_k) out[lane] = nb <= top_k ? (lane < nb ? lane : -1) : n;
+        return;
+    }
+    auto ld = [](const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    const int nw = (n + kWindowBlocks - 1) / kWindowBlocks;       // ranges holding candidates
+    // pass 1: T0 from the per-lane maxima of the range maxima (16 per lane per
+    // round; the first round's values stay in registers for pass 2)
+    float x0[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x0[j] = ld(wmax + min(lane + kWave * j, nw - 1));
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (lane + kWave * j < nw) lmax = max(lmax, order_key(x0[j]));
+    for (int w0 = 16 * kWave; w0 < nw; w0 += 16 * kWave) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = ld(wmax + min(w0 + lane + kWave * j, nw - 1));
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (w0 + lane + kWave * j < nw) lmax = max(lmax, order_key(x[j]));
+    }
+    const uint32_t t0 = kth_largest_wave<16>(lmax, need);
+    // pass 2: the ranges with a maximum >= T0, in ascending order
+    int c = 0;
+    for (int w0 = 0; w0 < nw; w0 += 16 * kWave) {
+        float x[16];
+        if (w0 == 0) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = x0[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = ld(wmax + min(w0 + lane + kWave * j, nw - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int w = w0 + lane + kWave * j;
+            const bool f = w < nw && order_key(x[j]) >= t0;
+            const uint64_t mk = __ballot(f);
+            const int pos = c + lanes_below(mk);
+            if (f && pos < kWave) cr[pos] = w;
+            c += __popcll(mk);
+        }
+    }
+    if (c <= kWave) {
+        wave_lds_sync();
+        // lane l: the 4 blocks of candidate range l (keys 0 past the candidates)
+        const int w = lane < c ? cr[lane] : 0;
+        float sv[kWindowBlocks];
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) sv[j] = ld(scores + min(kWindowBlocks * w + j, n - 1));
+        uint32_t v[kWindowBlocks];
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) v[j] = lane < c && kWindowBlocks * w + j < n ? order_key(sv[j]) : 0u;
+        // T: the need-th largest key (the candidates hold >= need real keys)
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cb = t | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < kWindowBlocks; ++j) cnt += __popcll(__ballot(v[j] >= cb));
+            t = cnt >= need ? cb : t;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) gt += __popcll(__ballot(v[j] > t));
+        const int need_eq = need - gt;
+        // index order is lane-major here (range l's blocks come before range l+1's)
+        int eq_before = 0;
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) eq_before += lanes_below(__ballot(v[j] == t));
+        bool take[kWindowBlocks];
+        int within = 0;
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) {
+            const bool eq = v[j] == t;
+            take[j] = v[j] > t || (eq && eq_before + within < need_eq);
+            within += eq ? 1 : 0;
+        }
+        int pos = 0;
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) pos += lanes_below(__ballot(take[j]));
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j)
+            if (take[j]) out[pos++] = kWindowBlocks * w + j;
+    } else {
+        // exact fallback: bitwise search for T over every candidate score
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cb = t | (1u << bit);
+            int cnt = 0;
+            for (int j = lane; j < n; j += kWave) cnt += order_key(ld(scores + j)) >= cb;
+            if (wave_sum_int(cnt) >= need) t = cb;
+        }
+        int cnt = 0;
+        for (int j = lane; j < n; j += kWave) cnt += order_key(ld(scores + j)) > t;
+        const int need_eq = need - wave_sum_int(cnt);
+        int taken = 0, eq_seen = 0;
+        for (int j0 = 0; j0 < n; j0 += kWave) {
+            const int j = j0 + lane;
+            const uint32_t v = j < n ? order_key(ld(scores + j)) : 0u;
+            const bool eq = j < n && v == t;
+            const uint64_t em = __ballot(eq);
+            const bool tk = (j < n && v > t) || (eq && eq_seen + lanes_below(em) < need_eq);
+            const uint64_t tm = __ballot(tk);
+            if (tk) out[taken + lanes_below(tm)] = j;
+            taken += __popcll(tm);
+            eq_seen += __popcll(em);
+        }
+    }
+    if (lane == 0) out[need] = n;
+}
 
 // kSelect: the fused index-and-select variant (launched for one-row
-// sequences).  Every workgroup of a (sequence, key head) stores its scores
-// with device-scoped stores and, once they have completed, counts itself in on
-// a device-scoped counter; the last one reads the scores back with
-// device-scoped loads, selects the sequence's rows, resets the counter and
-// leaves.
+// sequences).  Every wave stores its scores and its range's best candidate
+// score with agent-scope stores; once a workgroup's stores have completed it
+// counts itself in on the counter of its (sequence, key-head group); the last
+// workgroup's waves select the group's heads, one head per wave.
 template <bool kSelect>
 __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t) {
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int lg = lane >> 4, lr = lane & 15;
-    // Scores only, with a multiple of 4 key heads: a workgroup's 4 waves are 4
-    // heads of one 4-block key range (blockIdx.x = key range * H/4 + head
-    // group), so index keys of neighbouring heads, side by side in token-major
-    // caches, are read by one CU at the same time (4-7% faster).  Otherwise a
-    // workgroup is one head's 16 blocks (blockIdx.x = key range * H + head),
-    // the heads of a key range dispatched together; the fused selection keeps
-    // this mapping, so that the last workgroups of different heads are
-    // different workgroups and the heads' selections run side by side.
-    constexpr bool kHeadsOk = !kSelect;
-    const bool heads_wg = kHeadsOk && a.H % 4 == 0;
+    // With a multiple of 4 key heads, a workgroup's 4 waves are 4 heads of one
+    // 4-block key range (blockIdx.x = key range * H/4 + head group), so index
+    // keys of neighbouring heads, side by side in token-major caches, are
+    // read by one CU at the same time.  Otherwise a workgroup is one head's
+    // 16 blocks (blockIdx.x = key range * H + head), the heads of a key range
+    // dispatched together.
+    const bool heads_wg = a.H % 4 == 0;
     const int s = blockIdx.z;
     const int n_groups = heads_wg ? a.H / 4 : a.H;          // workgroups per key range
     const int g0 = heads_wg ? (blockIdx.x % n_groups) * 4 : blockIdx.x % a.H;   // the workgroup's first head
@@ -611,7 +735,9 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
     const int rows_s = a.b.cu_rows[s + 1] - row0;
     const int L = a.b.seq_lens[s];
     if (rows_s <= 0 || rows_s > 16 || rows_s > L || L > a.b.max_seq_len) return;   // whole (s, g) alike
-    const int b_begin = (heads_wg ? xr : xr * 4 + wave) * kWindowBlocks;
+    if (kSelect && rows_s != 1) return;                                            // launched for one-row batches
+    const int range = heads_wg ? xr : xr * 4 + wave;        // this wave's 4-block range
+    const int b_begin = range * kWindowBlocks;
     const int b_end = min(b_begin + kWindowBlocks, a.bs_stride);
     const int p_first = L - rows_s;
     if (b_begin < b_end) {
@@ -653,51 +779,55 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         const int blk = b_begin + lg;
         if (rvalid && blk < b_end) {
             float *dst = a.scores + ((int64_t)(row0 + lr) * a.H + g) * a.bs_stride + blk;
-            if constexpr (kSelect)   // device-coherent store (written through to the device level)
+            if constexpr (kSelect)   // agent-scope store (written through the XCD's L2)
                 __hip_atomic_store(dst, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             else
                 *dst = mine;
         }
+        if constexpr (kSelect) {
+            // the range's best candidate (blocks below the row's local block)
+            const int n_cand = p_first / kBlock;
+            const float cm = max_over_lane_groups(lr == 0 && lg < nblk && blk < n_cand ? mine : -INFINITY);
+            if (lane == 0 && b_begin < n_cand)
+                __hip_atomic_store(t.wmax + ((int64_t)s * a.H + g) * t.ranges + range, cm, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if constexpr (kSelect) {
-        // Every score store above is agent-scoped (compiled with sc1: written
+        // Every store above is agent-scoped (compiled with sc1: written
         // through the XCD's L2 to the device-coherent level), so publishing
         // them needs only their completion: wait for this wave's stores, meet
         // at the barrier, then count the workgroup in (the atomic add is
-        // performed at that level).  The last workgroup reads the scores with
+        // performed at that level).  The last workgroup reads them with
         // agent-scope loads (sc1: not served from a copy in its own L2).  The
         // language's model orders none of this; an agent-scope release fence
         // would, but writes back the whole L2 in each of the many workgroups.
-        extern __shared__ uint32_t dyn[];
-        __shared__ SelScratch sc;
+        __shared__ int32_t cr_all[4][kWave];
         __shared__ int is_last;
-        const int unit = s * a.H + g;                        // (sequence, key head)
+        const int unit = s * n_groups + (heads_wg ? g0 / 4 : g0);   // (sequence, head group)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
             const unsigned prev = __hip_atomic_fetch_add(t.count + unit, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == gridDim.x / a.H - 1;
+            is_last = prev == gridDim.x / n_groups - 1;
         }
         __syncthreads();
         if (!is_last) return;
         if (threadIdx.x == 0)   // leave the counter at zero for the next call
             __hip_atomic_store(t.count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the workgroup per row (the launcher sends one-row sequences here)
-        for (int r = 0; r < rows_s; ++r) {
-            const int row = row0 + r;
-            const int nb = (p_first + r) / kBlock + 1;
-            __syncthreads();   // the previous row's reads are done before restaging
-            stage_keys_coherent(dyn, a.scores + ((int64_t)row * a.H + g) * a.bs_stride, nb - 1, threadIdx.x, 256);
-            select_unit_wg(dyn, nb, t.top_k, t.idx + ((int64_t)row * a.H + g) * t.top_k, sc);
-        }
+        if (!heads_wg && wave != 0) return;          // one head: its first wave selects
+        const int gs = heads_wg ? g0 + wave : g0;
+        const int64_t u = (int64_t)row0 * a.H + gs;
+        window_select_tail(a.scores + u * a.bs_stride, t.wmax + ((int64_t)s * a.H + gs) * t.ranges, p_first / kBlock,
+                           t.top_k, t.idx + u * t.top_k, cr_all[wave]);
     }
 }
 
-// index_scores_window's grid: scores only, with heads in fours, a workgroup
-// per (4-block key range, group of 4 heads); else per (16-block range, head).
-static dim3 window_grid(const IndexArgs &a, bool select) {
-    if (!select && a.H % 4 == 0)
+// index_scores_window's grid: with heads in fours, a workgroup per (4-block
+// key range, group of 4 heads); else per (16-block range, head).
+static dim3 window_grid(const IndexArgs &a) {
+    if (a.H % 4 == 0)
         return dim3((a.bs_stride + kWindowBlocks - 1) / kWindowBlocks * (a.H / 4), 1, a.b.n_seqs);
     const int per_wg = kWindowBlocks * 4;
     return dim3((a.bs_stride + per_wg - 1) / per_wg * a.H, 1, a.b.n_seqs);
@@ -706,7 +836,7 @@ static dim3 window_grid(const IndexArgs &a, bool select) {
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
     const int gz = a.b.n_seqs * a.H;
     if (a.b.max_rows <= 16) {
-        hipLaunchKernelGGL(index_scores_window<false>, window_grid(a, false), dim3(256), 0, st, a, SelectTail{});
+        hipLaunchKernelGGL(index_scores_window<false>, window_grid(a), dim3(256), 0, st, a, SelectTail{});
     } else {
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
@@ -723,11 +853,7 @@ hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, h
 }
 
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st) {
-    const dim3 grid = window_grid(a, true);
-    const int nb_max = (a.b.max_seq_len + kBlock - 1) / kBlock;
-    t.cap = ((nb_max + 63) / 64) * 64;                      // staged keys per row
-    const size_t lds = (size_t)t.cap * sizeof(uint32_t);
-    hipLaunchKernelGGL(index_scores_window<true>, grid, dim3(256), lds, st, a, t);
+    hipLaunchKernelGGL(index_scores_window<true>, window_grid(a), dim3(256), 0, st, a, t);
     return hipGetLastError();
 }
 

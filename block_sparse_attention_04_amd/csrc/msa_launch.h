@@ -66,13 +66,16 @@ struct AttnArgs {
     int64_t s_tok, s_head;
 };
 
-// Selection fused after the decode-shaped indexer.
+// Selection fused after the decode-shaped indexer (one-row batches).
 struct SelectTail {
     int top_k;
     int32_t *idx;                // [total_rows, H, top_k]
-    unsigned *count;             // one arrival counter per (sequence, key head); zero between calls
-    int cap;                     // staged keys per row (set by the launcher)
+    unsigned *count;             // one arrival counter per (sequence, key-head group); zero between calls
+    float *wmax;                 // [n_seqs, H, ranges]: the best candidate score of each 4-block range
+    int ranges;                  // row stride of wmax: ceil(ceil(max_seq_len / 64) / 4)
 };
+constexpr int kWindowBlocks = 4;   // blocks per wave of the decode-shaped indexer
+inline int window_ranges(int max_seq_len) { return ((max_seq_len + 63) / 64 + kWindowBlocks - 1) / kWindowBlocks; }
 
 // Selection fused into the prompt-chunk indexer: the candidate blocks of each
 // (sequence, key head, 256-row tile) are split over `splits` workgroups of
@@ -127,6 +130,8 @@ inline size_t index_select_workspace_bytes(int n_seqs, int H, int total_rows, in
         int S, per;
         chunk_splits(n_seqs, H, max_rows, max_seq_len, &S, &per);
         b += (size_t)total_rows * H * S * kChunkList * sizeof(uint64_t);
+    } else if (max_rows == 1) {   // the range maxima of the one-row path
+        b += ((size_t)n_seqs * H * window_ranges(max_seq_len) * sizeof(float) + 255) / 256 * 256;
     }
     return b;
 }

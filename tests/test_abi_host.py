@@ -181,8 +181,12 @@ def test_index_select_checks():
     L = msa.lib()
     sh = msa.make_shape(2)
     counters = 256 * 1024
-    # decode-shaped batches (<= 16 rows): the counter region only
-    assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=3, total_rows=3, max_rows=1)) == counters
+    # one-row batches: + the 4-block range maxima, 4 bytes per (sequence, key
+    # head, range), rounded to 256 bytes (100 keys: 2 blocks, 1 range)
+    assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=3, total_rows=3, max_rows=1)) == counters + 256
+    b1 = FakeBatch(n_seqs=3, total_rows=3, max_rows=1, max_seq_len=262144)     # 4,096 blocks: 1,024 ranges
+    assert msa.msa_index_select_workspace_bytes(sh, b1) == counters + 3 * 2 * 1024 * 4
+    # windows (2..16 rows): the counter region only
     assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=2, total_rows=32, max_rows=16)) == counters
     # prompt chunks: + 128 bytes of candidate lists per (row, key head, split);
     # 1 sequence x 2 heads x 1 tile -> 256 splits wanted, at most one per 16 blocks
@@ -190,7 +194,7 @@ def test_index_select_checks():
     assert msa.msa_index_select_workspace_bytes(sh, b) == counters + 300 * 2 * 5 * 128
     assert msa.msa_index_select_workspace_bytes(msa.make_shape(2, top_k=17), b) == counters
     assert msa.msa_index_select_workspace_bytes(sh, FakeBatch(n_seqs=-1)) == 0
-    ws_one = counters
+    ws_one = counters                   # FakeBatch(): 4 rows, no range maxima
     call = lambda b, ws, nbytes, bs=2, scores=12288: L.msa_index_select(
         ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), ctypes.c_void_p(8192), 64, 0,
         ctypes.c_void_p(scores) if scores else None, bs, ctypes.c_void_p(16384),
