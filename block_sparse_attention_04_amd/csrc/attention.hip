@@ -782,6 +782,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         // once the stores are acknowledged, and on the counter's atomic add
         // being performed at that level.  A release fence would make it
         // formal but writes back the whole L2 in each of the many workgroups.
+        // A partial: 16 maxima, 16 sums, then value i of thread t at 32 + 256 i + t
+        // (each store and load instruction covers 1 KiB of consecutive words).
         float *pw = part_unit + split * (int64_t)kPartialFloats;
         if (d0 == 0) {
             __hip_atomic_store(pw + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -789,7 +791,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            __hip_atomic_store(pw + 32 + h * kHeadDim + d0 + i, accv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pw + 32 + 256 * i + threadIdx.x, accv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -802,41 +804,33 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
         if (threadIdx.x == 0)   // leave the counter at zero for the next call
             __hip_atomic_store(a.ws_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (!u.ok) return;
-        // every split's max first (one batch of loads), then its values
-        float ms[kMaxTopK / 4];
-        M = -INFINITY;
+        // every split's max, sum and values in one batch of loads (one round
+        // trip; splits past the last are not read), then the merge in split
+        // order
+        float ms[kMaxTopK / 4], lv[kMaxTopK / 4], xv[kMaxTopK / 4][8];
 #pragma unroll
         for (int w = 0; w < kMaxTopK / 4; ++w) {
-            ms[w] = w < wg_per_unit ? __hip_atomic_load(part_unit + w * kPartialFloats + h, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT)
-                                    : -INFINITY;
-            M = fmaxf(M, ms[w]);
+            if (w >= wg_per_unit) break;
+            const float *ps = part_unit + w * kPartialFloats;
+            ms[w] = __hip_atomic_load(ps + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lv[w] = __hip_atomic_load(ps + 16 + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                xv[w][i] = __hip_atomic_load(ps + 32 + 256 * i + threadIdx.x, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
         }
+        M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kMaxTopK / 4; ++w)
+            if (w < wg_per_unit) M = fmaxf(M, ms[w]);
         Ls = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) accv[i] = 0.f;
         if (M != -INFINITY) {
+            // an empty partial (max -inf) has weight 0
 #pragma unroll
-            for (int w0 = 0; w0 < kMaxTopK / 4; w0 += 4) {
-                if (w0 >= wg_per_unit) break;
-                float lv[4], xv[4][8];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // an empty partial or a split past the last has weight 0: read
-                    // split 0 instead so every load stays in bounds
-                    const bool use = w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY;
-                    const float *ps = part_unit + (use ? w0 + q : 0) * kPartialFloats;
-                    lv[q] = __hip_atomic_load(ps + 16 + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        xv[q][i] = __hip_atomic_load(ps + 32 + h * kHeadDim + d0 + i, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (w0 + q < wg_per_unit && ms[w0 + q] != -INFINITY)
-                        merge_partial<8>(M, ms[w0 + q], lv[q], xv[q], Ls, accv);
-            }
+            for (int w = 0; w < kMaxTopK / 4; ++w)
+                if (w < wg_per_unit && ms[w] != -INFINITY) merge_partial<8>(M, ms[w], lv[w], xv[w], Ls, accv);
         }
     } else if (!u.ok) {
         return;
