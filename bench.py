@@ -116,6 +116,8 @@ def algorithmic_work(case, kv8=False, block_idx=None):
     attn_bytes += kept_kv_bytes(case, block_idx, (D + 4) * 2 if kv8 else None)
     w["attention"] = dict(flops=4 * D * kept * H * G, bytes=attn_bytes)
     w["write_cache"] = dict(flops=0, bytes=rows * H * D * 2 * 2 * 2)
+    # the write carried by the selection's launch (msa_index_select_pack_rows)
+    w["write_index_select"] = {q: w["write_cache"][q] + w["index_select"][q] for q in ("flops", "bytes")}
     return w
 
 
@@ -145,7 +147,8 @@ def fraction(wk, ms, measured=None):
 
 
 PROFILE_KERNELS = {"chunk/attention": "prefill_kernel", "chunk/index_scores": "index_scores_tiled",
-                   "long/index_scores": "index_scores_window", "long/index_select": "index_scores_window"}
+                   "long/index_scores": "index_scores_window", "long/index_select": "index_scores_window",
+                   "long/write_index_select": "index_scores_window"}
 
 
 def source_digest() -> str:
@@ -221,7 +224,7 @@ class Workload:
     one step."""
 
     def __init__(self, torch, msa, dev, name, case, mode, n_rep, *, fused, tiled=True, paged=False,
-                 head_major=False, kv8=False, ik_head_major=False):
+                 head_major=False, kv8=False, ik_head_major=False, fold_write=True):
         self.name, self.case, self.mode, self.fused = name, case, mode, fused
         self.kv8, self.msa = kv8, msa
         base = {n: getattr(case, n).to(dev) for n in ("q", "k", "v", "iq", "ik")}
@@ -256,8 +259,14 @@ class Workload:
         self.new_keys = [(k0 + L - n, k0 + L) for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows)]
         self.o = msa.run_path(self.shape, self.batch, self.inputs[0], mode, fused=fused,
                               kv8=self.inputs[0].get("kv8"), kvt=self.inputs[0].get("kvt"))
-        self.steps = ((("write_cache",) if self.write else ()) +
-                      (("index_select",) if fused else ("index_scores", "select_blocks")) + ("attention",))
+        # decode steps: the new keys' write rides in the selection's launch
+        # (msa_index_select_pack_rows) unless fold_write is off
+        self.fold = self.write and fused and mode == "decode" and fold_write
+        if self.fold:
+            self.steps = ("write_index_select", "attention")
+        else:
+            self.steps = ((("write_cache",) if self.write else ()) +
+                          (("index_select",) if fused else ("index_scores", "select_blocks")) + ("attention",))
 
     @property
     def kv_cache(self):
@@ -273,13 +282,19 @@ class Workload:
         msa, sh, b, o = self.msa, self.shape, self.batch, self.o
         t = self.inputs[i % len(self.inputs)]
         c = []
-        if self.write:
+        if self.fold:
+            c.append(("write_index_select", lambda: msa.msa_index_select_pack_rows(
+                sh, b, t["iq"], t["ik"], o["block_scores"], o["block_idx"], t["k"], t["v"], t["kvt"],
+                o["select_workspace"])))
+        elif self.write:
             if len(self.new_keys) == 1:
                 t0, t1 = self.new_keys[0]
                 c.append(("write_cache", lambda: msa.msa_pack_kv_tiled(sh, t["k"], t["v"], t["kvt"], t0, t1)))
             else:
                 c.append(("write_cache", lambda: msa.msa_pack_kv_tiled_rows(sh, b, t["k"], t["v"], t["kvt"])))
-        if self.fused:
+        if self.fold:
+            pass
+        elif self.fused:
             c.append(("index_select", lambda: msa.msa_index_select(sh, b, t["iq"], t["ik"], o["block_scores"],
                                                                    o["block_idx"], o["select_workspace"])))
         else:
@@ -601,6 +616,10 @@ def main():
                     help="the long row's calls: on a second stream starting with the chunk's part of each step "
                          "(indexer, the default: beside the chunk's cache write, indexer and selection), on a "
                          "free-running second stream (free), or after the chunk's on one stream (none)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="decode workloads: write the new keys with their own launch "
+                         "(msa_pack_kv_tiled_rows / msa_pack_kv_tiled) instead of inside the selection's "
+                         "launch (msa_index_select_pack_rows)")
     ap.add_argument("--unfused", action="store_true",
                     help="long row: msa_index_scores + msa_select_blocks instead of msa_index_select")
     ap.add_argument("--no-configs", action="store_true",
@@ -631,7 +650,8 @@ def main():
     cases = {"chunk": config("chunk") if args.locality is None else config("chunk", locality=args.locality),
              "long": config("long")}
     ik_hm = args.ik_layout == "head-major"
-    opts = dict(tiled=tiled, paged=args.paged, head_major=args.head_major, kv8=args.kv8, ik_head_major=ik_hm)
+    opts = dict(tiled=tiled, paged=args.paged, head_major=args.head_major, kv8=args.kv8, ik_head_major=ik_hm,
+                fold_write=not args.separate_write)
     wl = {"chunk": Workload(torch, msa, dev, "chunk", cases["chunk"], "prefill", CONFIG_PLAN["chunk"][2],
                             fused=False, **opts),
           "long": Workload(torch, msa, dev, "long", cases["long"], "decode", CONFIG_PLAN["long"][2],
@@ -761,7 +781,7 @@ def main():
                 w = wl[name]
             else:
                 w = Workload(torch, msa, dev, name, config(name), mode, n_rep, fused=fused, tiled=tiled,
-                             ik_head_major=ik_hm)
+                             ik_head_major=ik_hm, fold_write=not args.separate_write)
             print(f"[bench] config {name}: {steps} steps back to back", file=sys.stderr, flush=True)
             configs[name] = config_entry(torch, w, steps, block, measured, kv8=args.kv8 and name in wl)
             if name not in wl:

@@ -45,7 +45,7 @@ class _BatchC(ctypes.Structure):
 EXPORTS = ("msa_index_scores", "msa_select_blocks", "msa_index_select", "msa_prefill", "msa_decode",
            "msa_quantize_kv8", "msa_prefill_kv8", "msa_decode_kv8",
            "msa_pack_kv_tiled", "msa_pack_kv_tiled_rows", "msa_prefill_tiled", "msa_decode_tiled",
-           "msa_decode_tiled_noalloc",
+           "msa_decode_tiled_noalloc", "msa_index_select_pack_rows",
            "msa_decode_workspace_bytes", "msa_index_select_workspace_bytes", "msa_status_string",
            "msa_last_error", "msa_version", "msa_peaks_stream_read", "msa_peaks_stream_read_variant",
            "msa_peaks_mfma")
@@ -84,6 +84,8 @@ def lib():
             TP = ctypes.POINTER(_KVTiledC)
             L.msa_pack_kv_tiled.argtypes = [SP, i64, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp]
             L.msa_pack_kv_tiled_rows.argtypes = [SP, BP, vp, vp, i64, i64, vp, vp, i64, i64, vp]
+            L.msa_index_select_pack_rows.argtypes = [SP, BP, vp, vp, i64, i64, vp, i32, vp, vp, ctypes.c_size_t,
+                                                     vp, vp, i64, i64, vp, vp, i64, i64, vp]
             L.msa_prefill_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
             L.msa_decode_tiled.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.msa_decode_tiled_noalloc.argtypes = [SP, BP, vp, TP, vp, vp, vp, vp]
@@ -420,6 +422,33 @@ def msa_pack_kv_tiled_rows(shape: Shape, batch: Batch, k, v, tiles: KVTiled, str
     _check(lib().msa_pack_kv_tiled_rows(ctypes.byref(shape), ctypes.byref(batch.c), _ptr(k), _ptr(v), tok, head,
                                         ctypes.c_void_p(c.k), ctypes.c_void_p(c.v), c.block_stride, c.head_stride,
                                         _stream(stream)))
+
+
+def msa_index_select_pack_rows(shape: Shape, batch: Batch, iq, ik, block_scores, block_idx, k, v, tiles: KVTiled,
+                               workspace=None, stream=None):
+    """msa_pack_kv_tiled_rows(k, v -> tiles) and msa_index_select in one call
+    (the writes ride in the selection's launch for decode-shaped batches)."""
+    _need(iq, torch.bfloat16, "iq")
+    _need(ik, torch.bfloat16, "ik", contiguous=False)
+    if block_scores is not None:
+        _need(block_scores, torch.float32, "block_scores")
+    _need(block_idx, torch.int32, "block_idx")
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(v, torch.bfloat16, "v", contiguous=False)
+    itok, ihead = _strides_tok_head(ik, "ik")
+    tok, head = _strides_tok_head(k, "k")
+    if _strides_tok_head(v, "v") != (tok, head):
+        raise ValueError("k and v must share strides")
+    if k.shape[1] != tiles.k.shape[1] or (k.shape[0] + 63) // 64 > tiles.k.shape[0]:
+        raise ValueError("the tiles do not cover k's tokens or key heads")
+    if workspace is None:
+        workspace = index_select_workspace(shape, batch, iq.device)
+    c = tiles.c
+    _check(lib().msa_index_select_pack_rows(
+        ctypes.byref(shape), ctypes.byref(batch.c), _ptr(iq), _ptr(ik), itok, ihead, _ptr(block_scores),
+        0 if block_scores is None else block_scores.shape[-1], _ptr(block_idx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(k), _ptr(v), tok, head, ctypes.c_void_p(c.k),
+        ctypes.c_void_p(c.v), c.block_stride, c.head_stride, _stream(stream)))
 
 
 def msa_prefill_tiled(shape: Shape, batch: Batch, q, kv: KVTiled, block_idx, out, lse=None, stream=None):

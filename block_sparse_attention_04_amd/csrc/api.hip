@@ -206,9 +206,15 @@ size_t msa_index_select_workspace_bytes(const msa_shape *shape, const msa_batch 
                                              batch->max_seq_len, shape->top_k);
 }
 
-int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
-                     int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores, int32_t bs_stride,
-                     int32_t *block_idx, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+// msa_index_select, and msa_index_select_pack_rows with pk = its batch writer
+// (checked by the caller): decode-shaped launches carry the writer's
+// workgroups, the others launch it first.
+static int index_select_impl(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
+                             int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores, int32_t bs_stride,
+                             int32_t *block_idx, void *workspace, size_t workspace_bytes,
+                             const msa::PackRowsArgs *pk, void *stream) {
     int rc;
     bool empty;
     if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
@@ -257,13 +263,14 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
         c.cand = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(workspace) + msa::kIndexSelectCountBytes);
         c.tiles = msa::chunk_tiles(batch->max_rows);
         msa::chunk_splits(batch->n_seqs, H, batch->max_rows, batch->max_seq_len, &c.splits, &c.per_split);
+        if (pk && (rc = launched(msa::launch_pack_kv_rows(*pk, st), "pack_kv_tiled_rows"))) return rc;
         return launched(msa::launch_index_select_chunk(a, c, st), "index_select_chunk");
     }
     if (batch->max_rows > 1) {
         // Several rows per sequence: the last workgroup would select them one
         // after another, which costs more than a second launch that selects
         // every (row, key head) in parallel.
-        if ((rc = launched(msa::launch_index_scores(a, st), "index_scores"))) return rc;
+        if ((rc = launched(msa::launch_index_scores(a, st, pk), "index_scores"))) return rc;
         msa::SelectArgs s;
         s.b = a.b;
         s.H = a.H;
@@ -279,7 +286,16 @@ int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void 
     t.count = static_cast<unsigned *>(workspace);
     t.wmax = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + msa::kIndexSelectCountBytes);
     t.ranges = msa::window_ranges(batch->max_seq_len);
-    return launched(msa::launch_index_select(a, t, st), "index_select");
+    return launched(msa::launch_index_select(a, t, st, pk), "index_select");
+}
+
+extern "C" {
+
+int msa_index_select(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
+                     int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores, int32_t bs_stride,
+                     int32_t *block_idx, void *workspace, size_t workspace_bytes, void *stream) {
+    return index_select_impl(shape, batch, iq, ik, ik_tok_stride, ik_head_stride, block_scores, bs_stride,
+                             block_idx, workspace, workspace_bytes, nullptr, stream);
 }
 
 static int check_kv8(const msa_kv8 *kv, int n_kv_heads) {
@@ -604,6 +620,36 @@ int msa_pack_kv_tiled_rows(const msa_shape *shape, const msa_batch *batch, const
     a.t_head = head_stride;
     a.H = H;
     return launched(msa::launch_pack_kv_rows(a, static_cast<hipStream_t>(stream)), "pack_kv_tiled_rows");
+}
+
+int msa_index_select_pack_rows(const msa_shape *shape, const msa_batch *batch, const void *iq, const void *ik,
+                               int64_t ik_tok_stride, int64_t ik_head_stride, float *block_scores,
+                               int32_t bs_stride, int32_t *block_idx, void *workspace, size_t workspace_bytes,
+                               const void *k, const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
+                               void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
+                               void *stream) {
+    int rc;
+    bool empty = false;
+    if ((rc = check_shape(shape)) || (rc = check_batch(batch, shape, &empty))) return rc;
+    if (empty) return ok();
+    const int H = shape->n_kv_heads;
+    if ((rc = check_kv(k, v, kv_tok_stride, kv_head_stride, H))) return rc;
+    if ((rc = check_tiles(k_tiles, v_tiles, block_stride, head_stride, H))) return rc;
+    if ((int64_t)batch->total_rows * H * 64 / 256 > (int64_t)0x7fffffff)
+        return fail(MSA_ERR_UNSUPPORTED, "batch too large for one call");
+    msa::PackRowsArgs p;
+    p.b = to_dev(batch);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.tok = kv_tok_stride;
+    p.head = kv_head_stride;
+    p.kt = static_cast<uint16_t *>(k_tiles);
+    p.vt = static_cast<uint16_t *>(v_tiles);
+    p.t_blk = block_stride;
+    p.t_head = head_stride;
+    p.H = H;
+    return index_select_impl(shape, batch, iq, ik, ik_tok_stride, ik_head_stride, block_scores, bs_stride,
+                             block_idx, workspace, workspace_bytes, &p, stream);
 }
 
 int msa_quantize_kv8(const msa_shape *shape, int64_t n_tokens, const void *x, int64_t tok_stride,

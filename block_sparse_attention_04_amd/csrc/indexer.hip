@@ -27,6 +27,7 @@
 
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "msa_pack.h"
 #include "msa_select.h"
 
 namespace msa {
@@ -714,9 +715,18 @@ __device__ __forceinline__ void window_select_tail(const float *scores, const fl
 // score with agent-scope stores; once a workgroup's stores have completed it
 // counts itself in on the counter of its (sequence, key-head group); the last
 // workgroup's waves select the group's heads, one head per wave.
+// Workgroup columns from x_index on (sequence slice z = 0 only) carry the
+// batch's own keys into the tiled cache, one (row, key head) per wave
+// (msa_index_select_pack_rows): nothing in this launch reads the tiles, and
+// the attention that does comes after it on the stream.
 template <bool kSelect>
-__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t) {
+__global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t, PackRowsArgs pk,
+                                                           int x_index) {
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    if ((int)blockIdx.x >= x_index) {
+        if (blockIdx.z == 0) pack_row_key(pk, (int64_t)(blockIdx.x - x_index) * 4 + wave, lane);
+        return;
+    }
     const int lg = lane >> 4, lr = lane & 15;
     // With a multiple of 4 key heads, a workgroup's 4 waves are 4 heads of one
     // 4-block key range (blockIdx.x = key range * H/4 + head group), so index
@@ -810,7 +820,7 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         if (threadIdx.x == 0) {
             const unsigned prev = __hip_atomic_fetch_add(t.count + unit, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == gridDim.x / n_groups - 1;
+            is_last = prev == x_index / n_groups - 1;
         }
         __syncthreads();
         if (!is_last) return;
@@ -825,19 +835,33 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
 }
 
 // index_scores_window's grid: with heads in fours, a workgroup per (4-block
-// key range, group of 4 heads); else per (16-block range, head).
-static dim3 window_grid(const IndexArgs &a) {
-    if (a.H % 4 == 0)
-        return dim3((a.bs_stride + kWindowBlocks - 1) / kWindowBlocks * (a.H / 4), 1, a.b.n_seqs);
-    const int per_wg = kWindowBlocks * 4;
-    return dim3((a.bs_stride + per_wg - 1) / per_wg * a.H, 1, a.b.n_seqs);
+// key range, group of 4 heads); else per (16-block range, head).  With a
+// batch writer `pk`, one more column per 4 (row, key head) units.
+static dim3 window_grid(const IndexArgs &a, const PackRowsArgs *pk, int *x_index) {
+    int x = 0;
+    if (a.H % 4 == 0) {
+        x = (a.bs_stride + kWindowBlocks - 1) / kWindowBlocks * (a.H / 4);
+    } else {
+        const int per_wg = kWindowBlocks * 4;
+        x = (a.bs_stride + per_wg - 1) / per_wg * a.H;
+    }
+    *x_index = x;
+    const int64_t pack_wgs = pk ? ((int64_t)pk->b.total_rows * pk->H + 3) / 4 : 0;
+    return dim3((unsigned)(x + pack_wgs), 1, a.b.n_seqs);
 }
 
-hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st) {
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRowsArgs *pk) {
     const int gz = a.b.n_seqs * a.H;
     if (a.b.max_rows <= 16) {
-        hipLaunchKernelGGL(index_scores_window<false>, window_grid(a), dim3(256), 0, st, a, SelectTail{});
+        int x_index = 0;
+        const dim3 grid = window_grid(a, pk, &x_index);
+        hipLaunchKernelGGL(index_scores_window<false>, grid, dim3(256), 0, st, a, SelectTail{},
+                           pk ? *pk : PackRowsArgs{}, x_index);
     } else {
+        if (pk) {   // the prompt-chunk indexer carries no writer: its own launch first
+            const hipError_t e = launch_pack_kv_rows(*pk, st);
+            if (e != hipSuccess) return e;
+        }
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
         dim3 grid((a.bs_stride + kTiledBlocks - 1) / kTiledBlocks, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
@@ -852,8 +876,10 @@ hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, h
     return hipGetLastError();
 }
 
-hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st) {
-    hipLaunchKernelGGL(index_scores_window<true>, window_grid(a), dim3(256), 0, st, a, t);
+hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st, const PackRowsArgs *pk) {
+    int x_index = 0;
+    const dim3 grid = window_grid(a, pk, &x_index);
+    hipLaunchKernelGGL(index_scores_window<true>, grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{}, x_index);
     return hipGetLastError();
 }
 

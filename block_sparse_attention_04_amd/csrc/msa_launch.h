@@ -195,9 +195,11 @@ int report(int status, const char *msg);
 hipError_t launch_quantize_kv8(const QuantArgs &a, hipStream_t st);
 hipError_t launch_pack_kv_tiled(const PackTiledArgs &a, hipStream_t st);
 hipError_t launch_pack_kv_rows(const PackRowsArgs &a, hipStream_t st);
-hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st);
+// pk (optional): the batch's own keys into the tiled cache in the same launch
+// (extra workgroups for decode-shaped batches, else a launch of its own first).
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRowsArgs *pk = nullptr);
 hipError_t launch_select_blocks(const SelectArgs &a, hipStream_t st);
-hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st);
+hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st, const PackRowsArgs *pk = nullptr);
 hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, hipStream_t st);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const AttnArgs &a, hipStream_t st);

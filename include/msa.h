@@ -310,6 +310,28 @@ int msa_pack_kv_tiled_rows(const msa_shape *shape, const msa_batch *batch,
                            void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
                            void *stream);
 
+/*
+ * A decode step's first two calls in one: msa_pack_kv_tiled_rows (the batch's
+ * own keys into their tiles; arguments k .. head_stride as there) and
+ * msa_index_select (arguments iq .. workspace_bytes as there), with results
+ * bit-identical to those two calls.  Each computes what its own declaration
+ * cites; the pages' step kernels write a step's keys and values into the
+ * cache that its attention then reads (TensorFold pull request 1388, the
+ * commit that drops the int8 cache: the prep and decode kernels and the cache
+ * layout).  The tiles are read by the attention only, never by the index
+ * scores or the selection, so for batches with at most 16 rows per sequence
+ * the writes ride in the selection's first launch as extra workgroups instead
+ * of a launch of their own; larger batches take the writer's launch first.
+ * Errors: the union of the two calls'; on any error nothing is launched.
+ */
+int msa_index_select_pack_rows(const msa_shape *shape, const msa_batch *batch,
+                               const void *iq, const void *ik, int64_t ik_tok_stride, int64_t ik_head_stride,
+                               float *block_scores, int32_t bs_stride, int32_t *block_idx,
+                               void *workspace, size_t workspace_bytes,
+                               const void *k, const void *v, int64_t kv_tok_stride, int64_t kv_head_stride,
+                               void *k_tiles, void *v_tiles, int64_t block_stride, int64_t head_stride,
+                               void *stream);
+
 /* msa_prefill over a tiled cache (other arguments and errors as msa_prefill). */
 int msa_prefill_tiled(const msa_shape *shape, const msa_batch *batch, const void *q, const msa_kv_tiled *kv,
                       const int32_t *block_idx, void *out, float *lse, void *stream);

@@ -16,6 +16,10 @@ HEADER = os.path.join(ROOT, "include", "msa.h")
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH), reason="libmsa.so not built")
+# Calls with valid arguments and the fake pointers below reach the device
+# check; they are made only where there is no device, so that nothing is ever
+# launched on those pointers.
+NO_DEVICE = not torch.cuda.is_available()
 
 
 def declared_functions(headers=None):
@@ -155,7 +159,7 @@ def test_kv_token_stride_limit():
     assert call((1 << 24) + 8) == -2 and "stride" in _err()
 
 
-@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
+@pytest.mark.skipif(not NO_DEVICE, reason="checks the no-device path only")
 def test_no_device_returns_hip_error():
     # every argument is valid, so only the device check can fail here
     rc = _call_index(msa.make_shape(1), FakeBatch())
@@ -250,10 +254,6 @@ def test_tiled_cache_checks():
     assert call(kv(bs=4096)) == -1 and "tile" in _err()
     assert call(kv(hs=4096)) == -1 and "tile" in _err()           # two heads' tiles overlap
     assert call(kv(), out=0) == -1
-    one = msa.make_shape(1)
-    assert L.msa_prefill_tiled(ctypes.byref(one), ctypes.byref(b.c), ctypes.c_void_p(1 << 20),
-                               ctypes.byref(kv(hs=0)), ctypes.c_void_p(32768), ctypes.c_void_p(65536),
-                               None, None) in (0, -4)               # valid: only the device check may fail
     need = msa.msa_decode_workspace_bytes(sh, 4)
     assert L.msa_decode_tiled(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(1 << 20), ctypes.byref(kv()),
                               ctypes.c_void_p(32768), ctypes.c_void_p(65536), None, ctypes.c_void_p(131072),
@@ -270,7 +270,19 @@ def test_tiled_cache_checks():
         ctypes.c_void_p(kt) if kt else None, ctypes.c_void_p(1 << 21), 2 * 8192, 8192, None)
     assert rows(k=0) == -1 and "NULL" in _err()
     assert rows(kt=0) == -1 and "tiles" in _err()
-    assert rows() in (0, -4)                                        # valid: only the device check may fail
+
+
+@pytest.mark.skipif(not NO_DEVICE, reason="valid arguments would launch on the fake pointers")
+def test_valid_tiled_calls_reach_the_device_check():
+    L = msa.lib()
+    sh, one = msa.make_shape(2), msa.make_shape(1)
+    b = FakeBatch()
+    kv = msa._KVTiledC(4096, 8192, 2 * 8192, 0)
+    assert L.msa_prefill_tiled(ctypes.byref(one), ctypes.byref(b.c), ctypes.c_void_p(1 << 20), ctypes.byref(kv),
+                               ctypes.c_void_p(32768), ctypes.c_void_p(65536), None, None) == -4
+    assert L.msa_pack_kv_tiled_rows(ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096),
+                                    ctypes.c_void_p(8192), 256, 128, ctypes.c_void_p(1 << 20),
+                                    ctypes.c_void_p(1 << 21), 2 * 8192, 8192, None) == -4
 
 
 def test_decode_noalloc_argument_checks():
@@ -292,3 +304,28 @@ def test_decode_noalloc_argument_checks():
     assert L.msa_decode_tiled_noalloc(ctypes.byref(msa.make_shape(4, top_k=33)), ctypes.byref(b.c),
                                       ctypes.c_void_p(4096), ctypes.byref(kv), ctypes.c_void_p(32768),
                                       ctypes.c_void_p(65536), None, None) == -2
+
+
+def test_index_select_pack_rows_checks():
+    """msa_index_select_pack_rows validates the writer's and the selection's
+    arguments before anything is launched."""
+    L = msa.lib()
+    sh = msa.make_shape(2)
+    b = FakeBatch(n_seqs=1, total_rows=1, max_rows=1)
+    ws = msa.msa_index_select_workspace_bytes(sh, b)
+    call = lambda k=4096, kt=1 << 20, tok=256, bs_t=2 * 8192, wsb=ws, idx=16384: L.msa_index_select_pack_rows(
+        ctypes.byref(sh), ctypes.byref(b.c), ctypes.c_void_p(4096), ctypes.c_void_p(8192), 64, 0,
+        ctypes.c_void_p(12288), 2, ctypes.c_void_p(idx) if idx else None, ctypes.c_void_p(65536), wsb,
+        ctypes.c_void_p(k) if k else None, ctypes.c_void_p(8192), tok, 128,
+        ctypes.c_void_p(kt) if kt else None, ctypes.c_void_p(1 << 21), bs_t, 8192, None)
+    assert call(k=0) == -1 and "NULL" in _err()
+    assert call(kt=0) == -1 and "tiles" in _err()
+    assert call(tok=64) == -1 and "kv strides" in _err()
+    assert call(bs_t=8) == -1 and "tile" in _err()
+    assert call(idx=0) == -1 and "NULL" in _err()
+    assert call(wsb=ws - 1) == -3
+    empty = FakeBatch(n_seqs=0, total_rows=0, max_rows=0)
+    assert L.msa_index_select_pack_rows(ctypes.byref(sh), ctypes.byref(empty.c), None, None, 64, 0, None, 0, None,
+                                        None, 0, None, None, 256, 128, None, None, 2 * 8192, 8192, None) == 0
+    if NO_DEVICE:
+        assert call() == -4                                    # valid: only the device check fails

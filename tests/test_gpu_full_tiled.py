@@ -1,11 +1,11 @@
 """The benchmarked path at full size: the five named workloads through exactly
 the calls the benchmark times over the tiled bf16 cache -- the step's new
-keys written into the tiles (one token range for the prompt chunk, the
-2,048-token prefill and the 262,144-key row; msa_pack_kv_tiled_rows for the
-batched decode and the verify windows, whose other keys are packed first and
-whose row keys are left NaN until the batch writer fills them), the selection
-(msa_index_scores + msa_select_blocks for prompt chunks, msa_index_select for
-decode batches) and msa_prefill_tiled / msa_decode_tiled.
+keys written into the tiles (msa_pack_kv_tiled over one token range for the
+prompt chunk and the 2,048-token prefill; for decode batches the write rides
+in the selection's launch, msa_index_select_pack_rows; every other key is
+packed first and the row keys are left NaN until the step writes them), the
+selection (msa_index_scores + msa_select_blocks for prompt chunks) and
+msa_prefill_tiled / msa_decode_tiled.
 
 Each is checked two ways: bit for bit against the strided cache's path on
 every row (block scores, selection, outputs, lse), and element by element
@@ -30,18 +30,17 @@ def bench_calls(case, t, batch, o, kvt):
     new keys into kvt and the results into o."""
     shape = shape_of(case)
     mode = MODE[case.name]
-    if mode == "prefill" or case.n_seqs == 1:      # one token range: each sequence's last rows
-        for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows):
-            msa.msa_pack_kv_tiled(shape, t["k"], t["v"], kvt, k0 + L - n, k0 + L)
-    else:
-        msa.msa_pack_kv_tiled_rows(shape, batch, t["k"], t["v"], kvt)
     if mode == "prefill":
+        for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows):   # one token range per sequence
+            msa.msa_pack_kv_tiled(shape, t["k"], t["v"], kvt, k0 + L - n, k0 + L)
         msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])
         msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"])
         msa.msa_prefill_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"])
     else:
+        # the new keys' write rides in the selection's launch
         ws = msa.index_select_workspace(shape, batch)
-        msa.msa_index_select(shape, batch, t["iq"], t["ik"], o["block_scores"], o["block_idx"], ws)
+        msa.msa_index_select_pack_rows(shape, batch, t["iq"], t["ik"], o["block_scores"], o["block_idx"],
+                                       t["k"], t["v"], kvt, ws)
         msa.msa_decode_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"],
                              msa.decode_workspace(shape, batch.total_rows))
 
