@@ -286,17 +286,25 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
     // FMA and one exp2.
     float z[2][4];
     float mx = -INFINITY;
-    const bool edge = kbase + 31 > p;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float v = sacc[mt][i];
             if constexpr (KV8) v *= ksc[mt][i];
-            if (edge && kbase + 16 * mt + 4 * lg + i > p) v = -INFINITY;
             z[mt][i] = v;
-            mx = fmaxf(mx, v);
         }
+    if (__builtin_expect(kbase + 31 > p, 0)) {   // uniform: the chunk reaching past p
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kbase + 16 * mt + 4 * lg + i > p) z[mt][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[mt][i]);
     mx = max_over_lane_groups(mx) * scale_log2;   // finite: key kbase <= p is visible
     float m_cur = st[0].m, l_cur = st[0].l;
 #pragma unroll
@@ -327,7 +335,8 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -m_cur));
-            psum += pr[mt][i];
+            // the first weight starts the sum (0 + w == w for every w >= +0)
+            psum = mt == 0 && i == 0 ? pr[0][0] : psum + pr[mt][i];
             if constexpr (KV8) pr[mt][i] *= vsc[mt][i];
         }
     l_cur += psum;
