@@ -64,7 +64,8 @@ __device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, 
 }
 
 constexpr int kTiledWaves = 4;
-constexpr int kTiledBlocks = 16;   // blocks per workgroup key range
+constexpr int kTiledBlocks = 16;   // blocks per workgroup key range (at most)
+constexpr int64_t kTiledFillWgs = 512;   // workgroups below which ranges shrink
 constexpr int kLdsRow = 144;   // bytes per staged key (128 + 16 pad: conflict-free b128 reads)
 
 template <int NT>
@@ -864,8 +865,14 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRow
         }
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
-        dim3 grid((a.bs_stride + kTiledBlocks - 1) / kTiledBlocks, (a.b.max_rows + rows_wg - 1) / rows_wg, gz);
-        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, kTiledBlocks);
+        const int tiles = (a.b.max_rows + rows_wg - 1) / rows_wg;
+        // 16 blocks per workgroup; fewer (8, 4, 2, 1) while the grid would
+        // leave most of the chip idle (a 2,048-row prefill has 8 row tiles x
+        // 2 ranges of 16 blocks).  Scores do not depend on it.
+        int per = kTiledBlocks;
+        while (per > 1 && (int64_t)gz * tiles * ((a.bs_stride + per - 1) / per) < kTiledFillWgs) per /= 2;
+        dim3 grid((a.bs_stride + per - 1) / per, tiles, gz);
+        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, per);
     }
     return hipGetLastError();
 }
