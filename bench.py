@@ -118,6 +118,9 @@ def algorithmic_work(case, kv8=False, block_idx=None):
     w["write_cache"] = dict(flops=0, bytes=rows * H * D * 2 * 2 * 2)
     # the write carried by the selection's launch (msa_index_select_pack_rows)
     w["write_index_select"] = {q: w["write_cache"][q] + w["index_select"][q] for q in ("flops", "bytes")}
+    # the same call on a prompt chunk: the indexer (with the writer) and the selection, scores through memory
+    w["write_index_scores_select"] = {q: w["write_cache"][q] + w["index_scores"][q] + w["select_blocks"][q]
+                                      for q in ("flops", "bytes")}
     return w
 
 
@@ -260,10 +263,15 @@ class Workload:
         self.o = msa.run_path(self.shape, self.batch, self.inputs[0], mode, fused=fused,
                               kv8=self.inputs[0].get("kv8"), kvt=self.inputs[0].get("kvt"))
         # decode steps: the new keys' write rides in the selection's launch
-        # (msa_index_select_pack_rows) unless fold_write is off
-        self.fold = self.write and fused and mode == "decode" and fold_write
+        # (msa_index_select_pack_rows) unless fold_write is off.  Prompt
+        # chunks write their token range with msa_pack_kv_tiled: beside a
+        # chip-filling indexer the carried writer measured slower (headline
+        # step 679-680 against 675-676 us)
+        self.fold = self.write and fold_write and mode == "decode"
         if self.fold:
-            self.steps = ("write_index_select", "attention")
+            self.steps = ("write_index_select" if fused else "write_index_scores_select", "attention")
+            if "select_workspace" not in self.o:
+                self.o["select_workspace"] = msa.index_select_workspace(self.shape, self.batch, dev)
         else:
             self.steps = ((("write_cache",) if self.write else ()) +
                           (("index_select",) if fused else ("index_scores", "select_blocks")) + ("attention",))
@@ -283,7 +291,7 @@ class Workload:
         t = self.inputs[i % len(self.inputs)]
         c = []
         if self.fold:
-            c.append(("write_index_select", lambda: msa.msa_index_select_pack_rows(
+            c.append((self.steps[0], lambda: msa.msa_index_select_pack_rows(
                 sh, b, t["iq"], t["ik"], o["block_scores"], o["block_idx"], t["k"], t["v"], t["kvt"],
                 o["select_workspace"])))
         elif self.write:

@@ -68,14 +68,23 @@ constexpr int kTiledBlocks = 16;   // blocks per workgroup key range (at most)
 constexpr int64_t kTiledFillWgs = 512;   // workgroups below which ranges shrink
 constexpr int kLdsRow = 144;   // bytes per staged key (128 + 16 pad: conflict-free b128 reads)
 
+// Slices z >= z_index (msa_index_select_pack_rows) carry the batch's own keys
+// into the tiled cache, one (row, key head) per wave: nothing in this launch
+// reads the tiles, and the attention that does comes after it on the stream.
 template <int NT>
-__global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int blocks_per_wg) {
+__global__ __launch_bounds__(256) void index_scores_tiled(IndexArgs a, int blocks_per_wg, PackRowsArgs pk,
+                                                          int z_index) {
     constexpr int kRowsWave = 16 * NT;
     constexpr int kRowsWg = kRowsWave * kTiledWaves;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4][kBlock * kLdsRow];
     __shared__ float otile[kTiledWaves][kRowsWave * kTiledBlocks];
 
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    if ((int)blockIdx.z >= z_index) {
+        const int64_t wg = ((int64_t)(blockIdx.z - z_index) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        pack_row_key(pk, wg * 4 + wave, lane);
+        return;
+    }
     const int lg = lane >> 4, lr = lane & 15;
     const int s = blockIdx.z / a.H, g = blockIdx.z % a.H;
     if (s >= a.b.n_seqs) return;
@@ -859,10 +868,6 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRow
         hipLaunchKernelGGL(index_scores_window<false>, grid, dim3(256), 0, st, a, SelectTail{},
                            pk ? *pk : PackRowsArgs{}, x_index);
     } else {
-        if (pk) {   // the prompt-chunk indexer carries no writer: its own launch first
-            const hipError_t e = launch_pack_kv_rows(*pk, st);
-            if (e != hipSuccess) return e;
-        }
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
         const int tiles = (a.b.max_rows + rows_wg - 1) / rows_wg;
@@ -872,7 +877,12 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRow
         int per = kTiledBlocks;
         while (per > 1 && (int64_t)gz * tiles * ((a.bs_stride + per - 1) / per) < kTiledFillWgs) per /= 2;
         dim3 grid((a.bs_stride + per - 1) / per, tiles, gz);
-        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, per);
+        if (pk) {   // the writer's workgroups: whole slices after the indexer's
+            const int64_t pack_wgs = ((int64_t)pk->b.total_rows * pk->H + 3) / 4;
+            const int64_t per_slice = (int64_t)grid.x * grid.y;
+            grid.z += (unsigned)((pack_wgs + per_slice - 1) / per_slice);
+        }
+        hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, per, pk ? *pk : PackRowsArgs{}, gz);
     }
     return hipGetLastError();
 }

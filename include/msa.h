@@ -319,9 +319,12 @@ int msa_pack_kv_tiled_rows(const msa_shape *shape, const msa_batch *batch,
  * cache that its attention then reads (TensorFold pull request 1388, the
  * commit that drops the int8 cache: the prep and decode kernels and the cache
  * layout).  The tiles are read by the attention only, never by the index
- * scores or the selection, so for batches with at most 16 rows per sequence
- * the writes ride in the selection's first launch as extra workgroups instead
- * of a launch of their own; larger batches take the writer's launch first.
+ * scores or the selection, so the writes ride in the selection's first launch
+ * as extra workgroups (the index-score launch, or the one launch of one-row
+ * batches) instead of a launch of their own; only the NULL-block_scores
+ * prompt-chunk path takes the writer's launch first.  Each wave writes one
+ * (row, key head) key; a prompt chunk whose new keys are one token range per
+ * sequence writes them faster with msa_pack_kv_tiled.
  * Errors: the union of the two calls'; on any error nothing is launched.
  */
 int msa_index_select_pack_rows(const msa_shape *shape, const msa_batch *batch,
