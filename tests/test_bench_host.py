@@ -44,6 +44,21 @@ def test_cache_write_bytes():
         assert w["write_cache"] == {"flops": 0, "bytes": rows * 4 * (256 + 256) * 2}
 
 
+def test_folded_write_work_is_the_sum_of_its_calls():
+    """msa_index_select_pack_rows does the cache write and the selection in one
+    call: its algorithmic work is theirs added, so a decode step's whole-path
+    fraction does not depend on whether the write is folded."""
+    for name in ("long", "decode", "windows"):
+        w = bench.algorithmic_work(config(name))
+        for q in ("flops", "bytes"):
+            assert w["write_index_select"][q] == w["write_cache"][q] + w["index_select"][q]
+        assert (bench.path_work(w, ("write_index_select", "attention")) ==
+                bench.path_work(w, ("write_cache", "index_select", "attention")))
+    w = bench.algorithmic_work(config("chunk"))
+    assert (bench.path_work(w, ("write_index_scores_select", "attention")) ==
+            bench.path_work(w, ("write_cache", "index_scores", "select_blocks", "attention")))
+
+
 @pytest.fixture(scope="module")
 def small():
     c = make_case("v", [3000], [200], 2, seed=5)
