@@ -66,6 +66,7 @@ __device__ __forceinline__ float lane_max_64(const floatx4 (&acc)[4], int key0, 
 constexpr int kTiledWaves = 4;
 constexpr int kTiledBlocks = 16;   // blocks per workgroup key range (at most)
 constexpr int64_t kTiledFillWgs = 512;   // workgroups below which ranges shrink
+constexpr int64_t kMaxGridZ = 65535;     // the launch grid's z extent, at most
 constexpr int kLdsRow = 144;   // bytes per staged key (128 + 16 pad: conflict-free b128 reads)
 
 // Slices z >= z_index (msa_index_select_pack_rows) carry the batch's own keys
@@ -880,7 +881,14 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRow
         if (pk) {   // the writer's workgroups: whole slices after the indexer's
             const int64_t pack_wgs = ((int64_t)pk->b.total_rows * pk->H + 3) / 4;
             const int64_t per_slice = (int64_t)grid.x * grid.y;
-            grid.z += (unsigned)((pack_wgs + per_slice - 1) / per_slice);
+            const int64_t slices = (pack_wgs + per_slice - 1) / per_slice;
+            if (gz + slices <= kMaxGridZ) {
+                grid.z += (unsigned)slices;
+            } else {   // past the grid's z limit: the writer's own launch first
+                const hipError_t e = launch_pack_kv_rows(*pk, st);
+                if (e != hipSuccess) return e;
+                pk = nullptr;
+            }
         }
         hipLaunchKernelGGL(index_scores_tiled<NT>, grid, dim3(256), 0, st, a, per, pk ? *pk : PackRowsArgs{}, gz);
     }
