@@ -128,10 +128,12 @@ __device__ __forceinline__ void wave_top(const uint32_t *keys, int n, int need, 
     }
 }
 
-// Stage order keys of scores S[0..n) into LDS (a burst of independent loads).
+// Stage order keys of scores S[0..n) into LDS (a burst of independent loads;
+// nontemporal: every score is read once, and the caches are better left to
+// the attention that follows).
 __device__ __forceinline__ void stage_keys(uint32_t *dst, const float *S, int n, int from, int step) {
 #pragma unroll 16
-    for (int j = from; j < n; j += step) dst[j] = order_key(S[j]);
+    for (int j = from; j < n; j += step) dst[j] = order_key(__builtin_nontemporal_load(S + j));
 }
 
 // As stage_keys, reading the scores with device-scoped loads (scores stored
