@@ -621,9 +621,9 @@ def main():
                     help="the index-key cache: [tokens, heads, 64] (token-major) or [heads, tokens, 64] "
                          "(head-major, passed as a strided [tokens, heads, 64] view)")
     ap.add_argument("--overlap", choices=("indexer", "free", "none"), default="indexer",
-                    help="the long row's calls: on a second stream starting with the chunk's part of each step "
-                         "(indexer, the default: beside the chunk's cache write, indexer and selection), on a "
-                         "free-running second stream (free), or after the chunk's on one stream (none)")
+                    help="the long row's calls: on a second stream starting when the chunk's cache write of "
+                         "each step is done (indexer, the default: beside the chunk's indexer and selection), on "
+                         "a free-running second stream (free), or after the chunk's on one stream (none)")
     ap.add_argument("--separate-write", action="store_true",
                     help="decode workloads: write the new keys with their own launch "
                          "(msa_pack_kv_tiled_rows / msa_pack_kv_tiled) instead of inside the selection's "
@@ -671,23 +671,30 @@ def main():
     bracket = set()
     marks = [torch.cuda.Event() for _ in range(8)]
 
+    def run_calls(name, calls, timed):
+        for kname, fn in calls:
+            key = f"{name}/{kname}"
+            if timed and key in bracket:
+                timer.run(key, fn)
+            else:
+                fn()
+
     def step(i, timed):
         """One headline step: the long row (second stream unless --overlap
-        none) and the chunk; `timed`: bracket the calls named in `bracket`."""
+        none) and the chunk; `timed`: bracket the calls named in `bracket`.
+        --overlap indexer: the long row's calls start once the chunk's cache
+        write is done, beside the chunk's indexer and selection."""
+        chunk_calls = wl["chunk"].calls(i)
         if side is not None and args.overlap == "indexer":
+            head = [c for c in chunk_calls if c[0] == "write_cache"]
+            run_calls("chunk", head, timed)
+            chunk_calls = [c for c in chunk_calls if c[0] != "write_cache"]
             mk = marks[i % len(marks)]
-            mk.record()                  # the chunk's part of this step starts here
+            mk.record()                  # after the chunk's cache write
             side.wait_event(mk)
-        for name in ("long", "chunk"):
-            w = wl[name]
-            on_side = side is not None and name == "long"
-            with torch.cuda.stream(side) if on_side else contextlib.nullcontext():
-                for kname, fn in w.calls(i):
-                    key = f"{name}/{kname}"
-                    if timed and key in bracket:
-                        timer.run(key, fn)
-                    else:
-                        fn()
+        with torch.cuda.stream(side) if side is not None else contextlib.nullcontext():
+            run_calls("long", wl["long"].calls(i), timed)
+        run_calls("chunk", chunk_calls, timed)
 
     # Settle: the device raises its clocks over the first tens of milliseconds
     # of sustained work (measured: ~7% slower steps after 3 warm-up steps than
@@ -767,7 +774,7 @@ def main():
         "streams": {"none": "one: the long row's calls after the chunk's",
                     "free": "two (default priority): the long row's calls on a free-running second stream",
                     "indexer": "two (default priority): each step's long row on a second stream, starting when "
-                               "the chunk's part of the step starts (beside its cache write, indexer and "
+                               "the chunk's cache write of the same step is done (beside its indexer and "
                                "selection)"}[args.overlap],
     }
     print(f"[bench] headline {ms_step:.4f} ms/step ({res['value'] / 1e6:.3f} M rows/s)", file=sys.stderr,
