@@ -427,7 +427,8 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
     return row_unit(a, (int)(unit % a.b.total_rows), (int)(unit / a.b.total_rows));
 }
 
-// Prefill.  One wave per group of RW consecutive rows of one key head.  For each row it holds the 16 query heads (so every
+// Prefill.  One wave per group of RW rows of one key head (which rows: see
+// group_rows below).  For each row it holds the 16 query heads (so every
 // kept block is fetched once for the whole group) and an online-softmax state.  The
 // rows' kept blocks are merged into one list sorted by block index and walked
 // 32 keys at a time, the next chunk's K/V loads in flight while the current
@@ -441,6 +442,99 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 // different ranks of their own lists, long after L2 has turned over.
 constexpr int kInvalidKey = 1 << 25;   // above every block index of an int32 position
 
+// Which rows share a wave.  A resident wave's key position at a given time is
+// set by its merged list: if the lists of some waves crowd into a part of the
+// key range and others spread out, the waves drift apart, the band of blocks
+// in use at once outgrows L2, and rows that keep the same block no longer read
+// it while it is cached.  With rows that keep unrelated blocks, the rows of
+// each key head are therefore grouped per window of 64 consecutive rows: the
+// window's rows are ranked by the mean of their kept blocks, ranks are paired
+// from both ends (k with 63-k), and a wave of 4 rows takes two such pairs from
+// the two halves (ranks w, 63-w, 16+w, 47-w), so every wave's list covers the
+// key range about evenly and all of them advance through it together (chunk
+// attention with i.i.d. selections: L2 hits 0.61 -> 0.79).  Where neighbouring
+// rows keep mostly the same blocks, the consecutive grouping is worth more (the
+// wave loads a shared block once for all its rows), so a window whose
+// neighbouring rows match in more than 35% of their blocks keeps it.  The
+// grouping decides only which wave computes a row: a row's result depends on
+// its own blocks alone.
+constexpr int kGroupWindow = 64;
+
+// Position of rank rho among the W rows of a window under the pairing above:
+// pair k = (rank k, rank W-1-k), pairs of the lower half (k < h) at even pair
+// positions and of the upper half at odd ones; with odd W the highest rank
+// takes the last position.  A bijection of [0, W).
+__device__ __forceinline__ int paired_position(int rho, int W) {
+    if (W & 1) {
+        if (rho == W - 1) return W - 1;
+        --W;
+    }
+    const int P = W >> 1, h = (P + 1) >> 1;
+    const int k = min(rho, W - 1 - rho), s = rho > W - 1 - rho ? 1 : 0;
+    const int sp = k < h ? 2 * k : 2 * (k - h) + 1;
+    return 2 * sp + s;
+}
+
+// The rows of group r0 / RW of key head g (wave-uniform).  Groups past the
+// batch's end get row total_rows - 1 (the caller marks them not ok).
+template <int RW>
+__device__ __forceinline__ void group_rows(const AttnArgs &a, int g, int r0, int (&rows)[RW]) {
+    const int n = a.b.total_rows;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) rows[i] = min(r0 + i, n - 1);
+    if constexpr (RW > 1) {
+        const int lane = threadIdx.x & 63;
+        const int w0 = r0 & ~(kGroupWindow - 1), wn = min(kGroupWindow, n - w0);
+        // lane l: row w0 + l, its sort key (mean kept block, lane as the tie
+        // break) and a 128-bit hashed set of its kept blocks
+        uint32_t ukey = 0x80000000u | (uint32_t)lane;   // lanes past the batch rank last
+        uint32_t hs[4] = {0u, 0u, 0u, 0u};
+        if (lane < wn) {
+            constexpr int kT = RW == 4 ? 16 : kMaxTopK;   // top_k's bound at RW rows per wave
+            const int32_t *ix = a.idx + ((int64_t)(w0 + lane) * a.H + g) * a.top_k;
+            int v[kT];
+#pragma unroll
+            for (int t = 0; t < kT; ++t) v[t] = ix[min(t, a.top_k - 1)];   // all in flight together
+            uint32_t sum = 0, cnt = 0;
+#pragma unroll
+            for (int t = 0; t < kT; ++t) {
+                const int b = v[t];
+                if (t < a.top_k && b >= 0 && b < kInvalidKey) {
+                    sum += (uint32_t)b;
+                    ++cnt;
+                    const uint32_t hb = ((uint32_t)b * 2654435761u) >> 25;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) hs[w] |= (hb >> 5) == (uint32_t)w ? 1u << (hb & 31) : 0u;
+                }
+            }
+            const float mean = cnt ? (float)sum / (float)cnt : 0.f;
+            ukey = ((uint32_t)fminf(mean * 64.f, 33554431.f) << 6) | (uint32_t)lane;
+        }
+        int common = 0, total = 0;   // vs. the neighbouring row (lane ^ 1)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)hs[w], 1);
+            common += __popc(hs[w] & o);
+            total += __popc(hs[w]);
+        }
+        int rank = 0, csum = 0, tsum = 0;
+#pragma unroll 8
+        for (int m = 0; m < kWave; ++m) {
+            rank += (uint32_t)__builtin_amdgcn_readlane((int)ukey, m) < ukey;
+            csum += __builtin_amdgcn_readlane(common, m);
+            tsum += __builtin_amdgcn_readlane(total, m);
+        }
+        if (100 * csum <= 35 * tsum) {
+            const int pos = lane < wn ? paired_position(rank, wn) : kWave;
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                const uint64_t hit = __ballot(pos == r0 - w0 + i);
+                if (hit) rows[i] = w0 + __builtin_ctzll(hit);
+            }
+        }
+    }
+}
+
 // kTiled: K/V from a tiled cache (kv_tok / kv_head are the tiles' block and
 // head strides); the chunk's V^T operands stay in registers.
 template <int RW, bool KV8, bool kTiled>
@@ -450,20 +544,24 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     const int hq = a.H * kGroup;
     const int top_k = a.top_k;
 
+    int rows[RW];
+    group_rows<RW>(a, g, r0, rows);
     Unit u[RW];
     Softmax st[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-        const int r = min(r0 + i, a.b.total_rows - 1);   // rows past the end: not ok
+        const int r = rows[i];
         u[i] = row_unit(a, r, g);
-        u[i].ok = u[i].ok && r0 + i < a.b.total_rows;
+        u[i].ok = u[i].ok && r0 + i < a.b.total_rows;   // rows past the end: not ok
         stage_q(qt + i * kQTileBytes, a.q + ((int64_t)r * hq + g * kGroup) * kHeadDim);
         softmax_init(st[i]);
     }
     // Entry (row li, slot lt) on lane li*top_k + lt: its block if kept and
     // visible, with its row's position and K/V offset.
     const int li = lane / top_k, lt = lane - li * top_k;
-    const int rl = min(r0 + li, a.b.total_rows - 1);
+    int rl = rows[0];
+#pragma unroll
+    for (int i = 1; i < RW; ++i) rl = li == i ? rows[i] : rl;
     const Unit ul = row_unit(a, rl, g);
     int key = kInvalidKey;
     if (li < RW && r0 + li < a.b.total_rows && ul.ok) {
@@ -611,8 +709,8 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     }
 }
 
-// Groups are enumerated head-major (consecutive groups: consecutive rows of one
-// key head), one per wave.
+// Groups are enumerated head-major (consecutive groups: groups of one key head,
+// in the order of their 64-row windows), one per wave.
 template <int RW, bool KV8, bool kTiled>
 __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled ? 16 : 8192];

@@ -7,7 +7,7 @@ import torch
 
 import block_sparse_attention_04_amd as msa
 import oracle
-from gpu_helpers import device_tensors, full_check, gpu_run, sample_rows, say, shape_of
+from gpu_helpers import check_lse, check_out, device_tensors, full_check, gpu_run, sample_rows, say, shape_of
 from workloads import Case, config, make_case
 
 pytestmark = pytest.mark.gpu
@@ -298,3 +298,47 @@ def test_decode_kernels_agree(top_k):
         assert torch.equal(big["block_idx"][r0:r1], one["block_idx"]), s
         assert torch.equal(big["out"][r0:r1], one["out"]), s
         assert torch.equal(big["lse"][r0:r1], one["lse"]), s
+
+
+# Batches whose rows the prefill groups into waves per 64-row window of each
+# key head: i.i.d. rows (ranked by their mean kept block and paired from both
+# ends), correlated rows (kept consecutive), ragged batches whose last window
+# holds an odd number of rows, and 4 or 2 rows per wave.
+GROUPING = {
+    "iid_w4_ragged": dict(seq_lens=[3000, 700, 65, 1900], rows=[1601, 37, 1, 464], n_kv_heads=4, seed=171),
+    "iid_w2_ragged": dict(seq_lens=[3000, 900], rows=[1999, 102], n_kv_heads=2, seed=172),
+    "correlated_w4": dict(seq_lens=[5000], rows=[2100], n_kv_heads=4, seed=173, locality=0.95),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(GROUPING))
+def test_prefill_row_grouping(name):
+    """Every row of the batch is computed exactly once, by whichever wave its
+    window's grouping gives it: outputs start as NaN and must all be written,
+    equal the oracle on the GPU's own selection on every row, and be
+    bit-identical between the strided and the tiled cache."""
+    from test_gpu_tiled import aligned_copy
+    case = make_case(name, **GROUPING[name])
+    R, H = case.total_rows, case.n_kv_heads
+    say(f"[gpu] row grouping {name}: seqs={case.seq_lens} rows={case.rows} heads={H}")
+    t = device_tensors(case)
+    shape = shape_of(case)
+    batch = msa.Batch(case.seq_lens, case.rows)
+    sel = msa.run_path(shape, batch, t, "prefill")["block_idx"]
+    nan_out = lambda: (torch.full_like(t["q"], float("nan")),
+                       torch.full((R, H * 16), float("nan"), device="cuda"))
+    o_s, l_s = nan_out()
+    msa.msa_prefill(shape, batch, t["q"], t["k"], t["v"], sel, o_s, l_s)
+    t2, starts = aligned_copy(case, t)
+    kvt = msa.KVTiled.empty(t2["k"].shape[0], H, "cuda", fill=float("nan"))
+    msa.msa_pack_kv_tiled(shape, t2["k"], t2["v"], kvt)
+    o_t, l_t = nan_out()
+    msa.msa_prefill_tiled(shape, msa.Batch(case.seq_lens, case.rows, kv_start=starts), t["q"], kvt, sel, o_t, l_t)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o_s.float()).any() and not torch.isnan(l_s).any(), "a row was never written"
+    assert torch.equal(o_t.view(torch.int16), o_s.view(torch.int16))
+    assert torch.equal(l_t.view(torch.int32), l_s.view(torch.int32))
+    o_ref, l_ref = oracle.attention(case, sel.cpu().numpy())
+    check_out(o_s.cpu(), o_ref, f"{name}/all rows")
+    check_lse(l_s.cpu(), l_ref, f"{name}/all rows")
