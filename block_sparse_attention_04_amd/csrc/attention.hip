@@ -82,16 +82,26 @@ constexpr int kQRowBytes = 272;
 constexpr float kLazyLog2 = 8.f;   // weights stay <= 256 between rescales
 constexpr int kQTileBytes = kGroup * kQRowBytes;
 
-// Copy the row's q (16 heads) from global memory into its LDS tile.
-__device__ __forceinline__ void stage_q(uint8_t *qt, const uint16_t *qrow_head0) {
+// The row's q (16 heads) from global memory into registers (16-byte piece
+// s * 64 + lane of 256 in qv[s]), then into its LDS tile.
+__device__ __forceinline__ void load_q_tile(u32x4 (&qv)[4], const uint16_t *qrow_head0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const int e = s * kWave + lane;            // 16-byte piece e of 256
-        const int h = e >> 4, c = e & 15;
-        *reinterpret_cast<u32x4 *>(qt + h * kQRowBytes + c * 16) = load16(qrow_head0 + h * kHeadDim + 8 * c);
+        const int e = s * kWave + lane;
+        qv[s] = load16(qrow_head0 + (e >> 4) * kHeadDim + 8 * (e & 15));
     }
 }
+
+__device__ __forceinline__ void store_q_tile(uint8_t *qt, const u32x4 (&qv)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int e = s * kWave + lane;
+        *reinterpret_cast<u32x4 *>(qt + (e >> 4) * kQRowBytes + (e & 15) * 16) = qv[s];
+    }
+}
+
 
 // The query B operand (as load_q) from an LDS tile.
 template <bool kBlocked>
@@ -502,7 +512,7 @@ __device__ __forceinline__ void group_rows(const AttnArgs &a, int g, int r0, int
                 if (t < a.top_k && b >= 0 && b < kInvalidKey) {
                     sum += (uint32_t)b;
                     ++cnt;
-                    const uint32_t hb = ((uint32_t)b * 2654435761u) >> 25;
+                    const uint32_t hb = (uint32_t)b & 127u;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) hs[w] |= (hb >> 5) == (uint32_t)w ? 1u << (hb & 31) : 0u;
                 }
@@ -510,20 +520,22 @@ __device__ __forceinline__ void group_rows(const AttnArgs &a, int g, int r0, int
             const float mean = cnt ? (float)sum / (float)cnt : 0.f;
             ukey = ((uint32_t)fminf(mean * 64.f, 33554431.f) << 6) | (uint32_t)lane;
         }
-        int common = 0, total = 0;   // vs. the neighbouring row (lane ^ 1)
+        int common = 0, total = 0;   // vs. the neighbouring row (lane ^ 1), each <= 32
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const uint32_t o = (uint32_t)__shfl_xor((int)hs[w], 1);
             common += __popc(hs[w] & o);
             total += __popc(hs[w]);
         }
-        int rank = 0, csum = 0, tsum = 0;
-#pragma unroll 8
-        for (int m = 0; m < kWave; ++m) {
-            rank += (uint32_t)__builtin_amdgcn_readlane((int)ukey, m) < ukey;
-            csum += __builtin_amdgcn_readlane(common, m);
-            tsum += __builtin_amdgcn_readlane(total, m);
+        int csum = 0, tsum = 0;      // their sums over the wave, bit by bit
+#pragma unroll
+        for (int bit = 0; bit < 6; ++bit) {
+            csum += (int)__popcll(__ballot((common >> bit) & 1)) << bit;
+            tsum += (int)__popcll(__ballot((total >> bit) & 1)) << bit;
         }
+        int rank = 0;
+#pragma unroll 8
+        for (int m = 0; m < kWave; ++m) rank += (uint32_t)__builtin_amdgcn_readlane((int)ukey, m) < ukey;
         if (100 * csum <= 35 * tsum) {
             const int pos = lane < wn ? paired_position(rank, wn) : kWave;
 #pragma unroll
@@ -546,6 +558,11 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
 
     int rows[RW];
     group_rows<RW>(a, g, r0, rows);
+    // The rows' q: loaded now, written to the LDS tiles once the entries are
+    // sorted and the first chunk's loads are out, so all these loads overlap.
+    u32x4 qv[RW][4];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) load_q_tile(qv[i], a.q + ((int64_t)rows[i] * hq + g * kGroup) * kHeadDim);
     Unit u[RW];
     Softmax st[RW];
 #pragma unroll
@@ -553,16 +570,20 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         const int r = rows[i];
         u[i] = row_unit(a, r, g);
         u[i].ok = u[i].ok && r0 + i < a.b.total_rows;   // rows past the end: not ok
-        stage_q(qt + i * kQTileBytes, a.q + ((int64_t)r * hq + g * kGroup) * kHeadDim);
         softmax_init(st[i]);
     }
     // Entry (row li, slot lt) on lane li*top_k + lt: its block if kept and
     // visible, with its row's position and K/V offset.
     const int li = lane / top_k, lt = lane - li * top_k;
     int rl = rows[0];
+    Unit ul = u[0];   // the entry's row's unit, from the group's (wave-uniform) units
 #pragma unroll
-    for (int i = 1; i < RW; ++i) rl = li == i ? rows[i] : rl;
-    const Unit ul = row_unit(a, rl, g);
+    for (int i = 1; i < RW; ++i) {
+        rl = li == i ? rows[i] : rl;
+        ul.s = li == i ? u[i].s : ul.s;
+        ul.p = li == i ? u[i].p : ul.p;
+        ul.ok = li == i ? u[i].ok : ul.ok;
+    }
     int key = kInvalidKey;
     if (li < RW && r0 + li < a.b.total_rows && ul.ok) {
         const int b = a.idx[((int64_t)rl * a.H + g) * top_k + lt];
@@ -672,11 +693,13 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     // The prefetch is unconditional (past the last chunk it re-reads the chunk
     // being folded), so every path through the loop has the same loads in
     // flight and a fold waits only for its own chunk, never for the prefetch.
+    Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
+    Regs ca, cb;
+    if (n_ent > 0) load(ca, c0);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) store_q_tile(qt + i * kQTileBytes, qv[i]);
     wave_lds_sync();   // q tiles written before the first fold reads them
     if (n_ent > 0) {
-        Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
-        Regs ca, cb;
-        load(ca, c0);
         for (;;) {
             const bool have1 = next_chunk(c1);
             if (!have1) c1 = c0;
