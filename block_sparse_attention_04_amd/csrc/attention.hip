@@ -162,19 +162,26 @@ __device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
 // elements of its block's K and V tiles).  The K tile holds the 8 operands
 // ka[mt][s] in order and the V tile the 8 V^T operands of fold_rows' PV
 // product (d-tile dt in vr[dt / 2][dt % 2]), each as 64 lane-ordered 16-byte
-// pieces, so every load reads 1 KiB of contiguous memory.  Keys past `last`
-// (the chunk's largest visible key offset) may never have been written: their
-// scores are masked in fold_rows, and their V elements are cleared here (their
-// weight is 0, but 0 times an unwritten NaN would not be).
-__device__ __forceinline__ void load_chunk_tiled(ChunkRegs &c, const uint16_t *kt, const uint16_t *vt,
-                                                 int last) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4;
+// pieces, so every load reads 1 KiB of contiguous memory.  Keys past the
+// chunk's largest visible key offset may never have been written: their scores
+// are masked in fold_rows, and their V elements are cleared by
+// clear_tail_v_tiled before the fold (their weight is 0, but 0 times an
+// unwritten NaN would not be) -- at fold time, so that the prefetch of a chunk
+// never waits for its own loads.
+__device__ __forceinline__ void load_chunk_tiled(ChunkRegs &c, const uint16_t *kt, const uint16_t *vt) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int s = 0; s < 4; ++s) c.ka[mt][s] = load16(kt + 8 * ((4 * mt + s) * kWave + lane));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) c.vr[dt >> 1][dt & 1] = load16(vt + 8 * (dt * kWave + lane));
+}
+
+// Clear the V elements of keys past `last` (the chunk's largest visible key
+// offset) in a tiled chunk's registers.
+__device__ __forceinline__ void clear_tail_v_tiled(ChunkRegs &c, int last) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
     if (last < 31) {
         // dword w of a V^T operand: keys k0 (low half) and k0 + 1 (high half)
         uint32_t m[4];
@@ -650,7 +657,7 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     auto load = [&](Regs &r, const Chunk &c) {
         if constexpr (kTiled) {   // block c.tok / 64, half (c.tok / 32) % 2
             const int64_t off = (c.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head + ((c.tok >> 5) & 1) * 4096;
-            load_chunk_tiled(r, a.k + off, a.v + off, c.p_max - c.kb);
+            load_chunk_tiled(r, a.k + off, a.v + off);
             return;
         }
         const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
@@ -663,8 +670,9 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
     };
     // Fold one loaded chunk into every row of its group that sees it (keys
     // past a row's own position are masked in its fold).
-    auto fold = [&](const Regs &r, const Chunk &c) {
+    auto fold = [&](Regs &r, const Chunk &c) {
         u32x4 ka8[2][4];
+        if constexpr (kTiled) clear_tail_v_tiled(r, c.p_max - c.kb);
         if constexpr (KV8) {
             stage_v8(r, vt, sct);
             k_operands8(r, ka8);
@@ -767,10 +775,14 @@ __device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit 
     if constexpr (kTiled) {   // the tile of block t0 / 64
         const int64_t off = (t0 >> 6) * a.kv_tok + (int64_t)u.g * a.kv_head;
         ChunkRegs ca, cb;
-        load_chunk_tiled(ca, a.k + off, a.v + off, u.p - kb0);
-        if (kb1 <= u.p) load_chunk_tiled(cb, a.k + off + 4096, a.v + off + 4096, u.p - kb1);
+        load_chunk_tiled(ca, a.k + off, a.v + off);
+        if (kb1 <= u.p) load_chunk_tiled(cb, a.k + off + 4096, a.v + off + 4096);
+        clear_tail_v_tiled(ca, u.p - kb0);
         fold_chunk_tiled(st, qb, ca, kb0, u.p, a.scale_log2);
-        if (kb1 <= u.p) fold_chunk_tiled(st, qb, cb, kb1, u.p, a.scale_log2);
+        if (kb1 <= u.p) {
+            clear_tail_v_tiled(cb, u.p - kb1);
+            fold_chunk_tiled(st, qb, cb, kb1, u.p, a.scale_log2);
+        }
         return;
     }
     const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
