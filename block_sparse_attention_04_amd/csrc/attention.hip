@@ -145,8 +145,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, c
     }
 }
 
-// Write one loaded chunk's V rows into this wave's 8 KiB LDS tile.
-__device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
+// Write 32 keys' V rows (load_chunk's vr, here flattened: v[2*kk + hf]) into
+// an 8 KiB LDS tile.
+__device__ __forceinline__ void stage_v_rows(const u32x4 (&v)[8], uint8_t *vt) {
     const int lane = threadIdx.x & 63;
     const int kg = lane >> 3, dc = lane & 7;
 #pragma unroll
@@ -154,8 +155,13 @@ __device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
         const int key = 4 * kg + kk;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-            *reinterpret_cast<u32x4 *>(vt + key * 256 + 16 * v_unit(key, dc + 8 * hf)) = c.vr[kk][hf];
+            *reinterpret_cast<u32x4 *>(vt + key * 256 + 16 * v_unit(key, dc + 8 * hf)) = v[2 * kk + hf];
     }
+}
+
+// Write one loaded chunk's V rows into this wave's 8 KiB LDS tile.
+__device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
+    stage_v_rows(*reinterpret_cast<const u32x4(*)[8]>(&c.vr[0][0]), vt);
 }
 
 // Registers of one 32-key chunk from a tiled cache (kt, vt: the chunk's 4,096
@@ -392,6 +398,183 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
         }
 }
 
+// ---- 64-key block folds (bf16 caches) ----
+//
+// A block's fold for one row: S^T = K Q^T over its 4 key tiles, one
+// online-softmax step over its 64 keys, then O^T += V^T P^T over its two
+// 32-key halves.  Per key it costs the same MFMAs as two 32-key folds, but
+// the fold's fixed chain (q read, max and its cross-lane step, the reference
+// test, the row's state selects) runs once per 64 keys, and the QK^T products
+// form 4 independent chains instead of 2.
+
+// S^T of one block for one row's 16 heads: sacc[mt] holds keys 16*mt + 4*lg
+// + i (i < 4) of head lr.
+__device__ __forceinline__ void qk_block(floatx4 (&sacc)[4], const u32x4 (&qb)[4], const u32x4 (&ka)[4][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(ka[mt][s], qb[s], acc);
+        sacc[mt] = acc;
+    }
+}
+
+// The rest of a block's fold into row `row` of a group of RW rows' states
+// (keys past p masked; kbase: the block's first key).  kVR: the V^T operands
+// of half h are vr[h][0..7] (tiled cache); else they are gathered from the
+// wave's LDS V tile (half h at vt + 8192 * h, stage_v_rows' layout) as
+// fold_rows does for a chunk.
+template <int RW, bool kVR>
+__device__ __forceinline__ void softmax_pv_block(Softmax (&st)[RW], int row, const floatx4 (&sacc)[4],
+                                                 const u32x4 (&vr)[2][8], const uint8_t *vt, int kbase, int p,
+                                                 float scale_log2) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    float z[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[mt][i] = sacc[mt][i];
+    if (__builtin_expect(kbase + 63 > p, 0)) {   // uniform: the block reaching past p
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kbase + 16 * mt + 4 * lg + i > p) z[mt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[mt][i]);
+    mx = max_over_lane_groups(mx) * scale_log2;   // finite: key kbase <= p is visible
+    float m_cur = st[0].m, l_cur = st[0].l;
+#pragma unroll
+    for (int i = 1; i < RW; ++i) {
+        m_cur = row == i ? st[i].m : m_cur;
+        l_cur = row == i ? st[i].l : l_cur;
+    }
+    // The reference max moves only when a head's scores exceed it by more
+    // than kLazyLog2 (always on the first block), as in fold_rows.
+    if (__ballot(mx > m_cur + kLazyLog2) != 0) {
+        const float m_new = fmaxf(m_cur, mx);
+        const float alpha = fast_exp2(m_cur - m_new);    // 0 on the first block
+        l_cur *= alpha;
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            if (row == i) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) st[i].o[dt] *= alpha;
+            }
+        m_cur = m_new;
+    }
+    float pr[4][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[mt][i] = fast_exp2(fmaf(z[mt][i], scale_log2, -m_cur));
+            // the first weight starts the sum (0 + w == w for every w >= +0)
+            psum = mt == 0 && i == 0 ? pr[0][0] : psum + pr[mt][i];
+        }
+    l_cur += psum;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        st[i].m = row == i ? m_cur : st[i].m;
+        st[i].l = row == i ? l_cur : st[i].l;
+    }
+    // P^T operand of half h: keys 32*h + 4*lg + 0..3 and 32*h + 16 + 4*lg + 0..3
+    // (the k-order of a chunk's P^T in fold_rows).
+    u32x4 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        pb[h] = u32x4{pack_bf16x2(pr[2 * h][0], pr[2 * h][1]), pack_bf16x2(pr[2 * h][2], pr[2 * h][3]),
+                      pack_bf16x2(pr[2 * h + 1][0], pr[2 * h + 1][1]),
+                      pack_bf16x2(pr[2 * h + 1][2], pr[2 * h + 1][3])};
+    u32x4 va[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if constexpr (kVR) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) va[h][dt] = vr[h][dt];
+        } else {
+            const int vkey = 4 * lg + (lr >> 2);
+            const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int rd = 8192 * h + (rd0 ^ (dt << 5));
+                const uint2 lo = lds_read_tr16(vt + rd);
+                const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
+                va[h][dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+        if (row == i) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                st[i].o[dt] = mfma_16x16x32(va[0][dt], pb[0], st[i].o[dt]);
+                st[i].o[dt] = mfma_16x16x32(va[1][dt], pb[1], st[i].o[dt]);
+            }
+        }
+}
+
+// Clear the V elements of keys past `last` (an offset within one 32-key half;
+// below 0: the whole half) in that half's V^T operands from a tiled cache:
+// such keys may never have been written, and 0 times an unwritten NaN would
+// not be 0.
+__device__ __forceinline__ void clear_tail_v_half(u32x4 (&v)[8], int last) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    if (last < 31) {
+        // dword w of a V^T operand: keys k0 (low half) and k0 + 1 (high half)
+        uint32_t m[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int k0 = (w < 2 ? 4 * lg : 16 + 4 * lg) + 2 * (w & 1);
+            m[w] = (k0 <= last ? 0x0000ffffu : 0u) | (k0 + 1 <= last ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) v[dt][w] &= m[w];
+    }
+}
+
+// K operands of a block from a strided cache (kblk: its first key; tok:
+// elements between consecutive keys): tile mt holds keys 16*mt + lane%16,
+// dims 32*s + 8*(lane/16) (load_chunk's interleaved layout).  Keys past `last`
+// (the block's largest visible key offset, 0..63) read key `last` instead, so
+// every read stays inside the keys that exist.
+__device__ __forceinline__ void load_block_k(u32x4 (&ka)[4][4], const uint16_t *kblk, int64_t tok, int last) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
+    const uint32_t tok_bytes = (uint32_t)tok * 2u;
+    const char *kb = reinterpret_cast<const char *>(kblk);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t off = (uint32_t)min(16 * mt + lr, last) * tok_bytes + 16u * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[mt][s] = *reinterpret_cast<const u32x4 *>(kb + off + 64 * s);
+    }
+}
+
+// V rows of a block from a strided cache, half h in v[h] as load_chunk's vr
+// (keys 32*h + 4*(lane/8) + kk in v[h][2*kk + 0/1], 16-byte units lane%8 and
+// lane%8 + 8); keys past `last` read key `last`.
+__device__ __forceinline__ void load_block_v(u32x4 (&v)[2][8], const uint16_t *vblk, int64_t tok, int last) {
+    const int lane = threadIdx.x & 63, kg = lane >> 3, dc = lane & 7;
+    const uint32_t tok_bytes = (uint32_t)tok * 2u;
+    const char *vb = reinterpret_cast<const char *>(vblk);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t off = (uint32_t)min(32 * h + 4 * kg + kk, last) * tok_bytes + 16u * dc;
+            v[h][2 * kk] = *reinterpret_cast<const u32x4 *>(vb + off);
+            v[h][2 * kk + 1] = *reinterpret_cast<const u32x4 *>(vb + off + 128);
+        }
+}
+
 // Fold one loaded 32-key chunk into a single state st (stage V, fold,
 // release the tile).
 __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
@@ -621,104 +804,179 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
         return rest ? k + 1 + __builtin_ctzll(rest) : n_ent;
     };
 
-    // A chunk of the walk: half hh of the block of the group opened by entry
-    // k (wave-uniform values); p_max: the largest position among its rows.
-    struct Chunk {
-        int kb, k, end, p_max;
-        int64_t tok;      // token of the chunk's first key
-    };
-    auto chunk_at = [&](int k, int hh) -> Chunk {
-        Chunk c;
-        c.k = k;
-        c.end = group_end(k);
-        c.kb = (__builtin_amdgcn_readlane(e_key, k) >> 2) * kBlock + 32 * hh;
-        c.tok = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) + 32 * hh;
-        int pm = __builtin_amdgcn_readlane(e_p, k);
-        for (int j = k + 1; j < c.end; ++j) pm = max(pm, __builtin_amdgcn_readlane(e_p, j));
-        c.p_max = pm;
-        return c;
-    };
-    int k = 0, half = 0;
-    auto next_chunk = [&](Chunk &c) -> bool {   // advances (k, half) to the next chunk some row sees
-        for (;;) {
-            if (half == 0) {
-                half = 1;
-            } else {
-                half = 0;
-                k = group_end(k);
-                if (k >= n_ent) return false;
-            }
-            c = chunk_at(k, half);
-            if (c.kb <= c.p_max) return true;
-        }
-    };
-    using Regs = typename std::conditional<KV8, ChunkRegs8, ChunkRegs>::type;
-    auto load = [&](Regs &r, const Chunk &c) {
-        if constexpr (kTiled) {   // block c.tok / 64, half (c.tok / 32) % 2
-            const int64_t off = (c.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head + ((c.tok >> 5) & 1) * 4096;
-            load_chunk_tiled(r, a.k + off, a.v + off);
-            return;
-        }
-        const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
-        if constexpr (KV8) {
-            const int64_t soff = c.tok * a.s_tok + (int64_t)g * a.s_head;
-            load_chunk8(r, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, c.p_max - c.kb);
-        } else {
-            load_chunk(r, a.k + off, a.v + off, a.kv_tok, 0, c.p_max - c.kb);
-        }
-    };
-    // Fold one loaded chunk into every row of its group that sees it (keys
-    // past a row's own position are masked in its fold).
-    auto fold = [&](Regs &r, const Chunk &c) {
-        u32x4 ka8[2][4];
-        if constexpr (kTiled) clear_tail_v_tiled(r, c.p_max - c.kb);
-        if constexpr (KV8) {
-            stage_v8(r, vt, sct);
-            k_operands8(r, ka8);
-        } else if constexpr (!kTiled) {
-            stage_v(r, vt);
-        }
-        if constexpr (!kTiled) wave_lds_sync();
-        for (int j = c.k; j < c.end; ++j) {
-            const int row = __builtin_amdgcn_readlane(e_key, j) & 3;
-            const int p = __builtin_amdgcn_readlane(e_p, j);
-            if (c.kb > p) continue;
-            u32x4 qb[4];
-            read_q<KV8>(qb, qt + row * kQTileBytes);
-            if constexpr (KV8) fold_rows<RW, true>(st, row, qb, ka8, c.kb, p, a.scale_log2, vt, sct);
-            else if constexpr (kTiled)
-                fold_rows<RW, false, true>(st, row, qb, r.ka, c.kb, p, a.scale_log2, nullptr, nullptr, r.vr);
-            else fold_rows<RW, false>(st, row, qb, r.ka, c.kb, p, a.scale_log2, vt, nullptr);
-        }
-        if constexpr (!kTiled) wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
-    };
-
     force_ready(e_key);
     force_ready(e_p);
     force_ready(e_lo);
     force_ready(e_hi);
-    // The prefetch is unconditional (past the last chunk it re-reads the chunk
-    // being folded), so every path through the loop has the same loads in
-    // flight and a fold waits only for its own chunk, never for the prefetch.
-    Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
-    Regs ca, cb;
-    if (n_ent > 0) load(ca, c0);
+
+    if constexpr (!KV8) {
+        // bf16 caches: one fold per (block, row) over the block's 64 keys.
+        // The walk moves from run to run (a run: the entries that read one
+        // block's K/V, usually one row).  K of the next run is requested as
+        // soon as this run's last QK^T products are issued, V as soon as this
+        // run's V is no longer needed in registers (tiled: after its last PV
+        // products; strided: once staged in LDS), so each load has most of a
+        // fold to arrive.  Past the last run the requests re-read it, so
+        // every path has the same loads in flight.
+        struct Run {
+            int k, end, kb, p_max;    // entries [k, end); first key; largest position among its rows
+            int64_t tok;              // token of the block's first key
+        };
+        auto run_at = [&](int k) -> Run {
+            Run r;
+            r.k = k;
+            r.end = group_end(k);
+            r.kb = (__builtin_amdgcn_readlane(e_key, k) >> 2) * kBlock;
+            r.tok = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane(e_lo, k));
+            int pm = __builtin_amdgcn_readlane(e_p, k);
+            for (int j = k + 1; j < r.end; ++j) pm = max(pm, __builtin_amdgcn_readlane(e_p, j));
+            r.p_max = pm;
+            return r;
+        };
+        u32x4 kreg[4][4];   // K operands of the block's 4 key tiles
+        u32x4 vreg[2][8];   // V of each 32-key half: tiled, its 8 V^T operands; strided, its rows (load_chunk's vr)
+        auto load_k = [&](const Run &r) {
+            if constexpr (kTiled) {
+                const uint16_t *kt = a.k + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head;
 #pragma unroll
-    for (int i = 0; i < RW; ++i) store_q_tile(qt + i * kQTileBytes, qv[i]);
-    wave_lds_sync();   // q tiles written before the first fold reads them
-    if (n_ent > 0) {
-        for (;;) {
-            const bool have1 = next_chunk(c1);
-            if (!have1) c1 = c0;
-            load(cb, c1);
-            fold(ca, c0);
-            if (!have1) break;
-            const bool have0 = next_chunk(c0);
-            if (!have0) c0 = c1;
-            load(ca, c0);
-            fold(cb, c1);
-            if (!have0) break;
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            kreg[2 * h + mt][s] = load16(kt + 4096 * h + 8 * ((4 * mt + s) * kWave + lane));
+            } else {
+                load_block_k(kreg, a.k + r.tok * a.kv_tok + (int64_t)g * a.kv_head, a.kv_tok, r.p_max - r.kb);
+            }
+        };
+        auto load_v = [&](const Run &r) {
+            if constexpr (kTiled) {
+                const uint16_t *vtl = a.v + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) vreg[h][dt] = load16(vtl + 4096 * h + 8 * (dt * kWave + lane));
+            } else {
+                load_block_v(vreg, a.v + r.tok * a.kv_tok + (int64_t)g * a.kv_head, a.kv_tok, r.p_max - r.kb);
+            }
+        };
+        Run r = run_at(0);
+        if (n_ent > 0) {
+            load_k(r);
+            load_v(r);
+        }
+#pragma unroll
+        for (int i = 0; i < RW; ++i) store_q_tile(qt + i * kQTileBytes, qv[i]);
+        wave_lds_sync();   // q tiles written before the first fold reads them
+        if (n_ent > 0) {
+            for (;;) {
+                const bool have = r.end < n_ent;
+                const Run nx = have ? run_at(r.end) : r;
+                if constexpr (kTiled) {
+                    clear_tail_v_half(vreg[0], r.p_max - r.kb);
+                    clear_tail_v_half(vreg[1], r.p_max - r.kb - 32);
+                } else {
+                    stage_v_rows(vreg[0], vt);
+                    stage_v_rows(vreg[1], vt + 8192);
+                    wave_lds_sync();
+                    load_v(nx);
+                }
+                for (int j = r.k; j < r.end; ++j) {
+                    const int row = __builtin_amdgcn_readlane(e_key, j) & 3;
+                    const int p = __builtin_amdgcn_readlane(e_p, j);
+                    u32x4 qb[4];
+                    read_q<false>(qb, qt + row * kQTileBytes);
+                    floatx4 sacc[4];
+                    qk_block(sacc, qb, kreg);
+                    if (j == r.end - 1) load_k(nx);
+                    softmax_pv_block<RW, kTiled>(st, row, sacc, vreg, vt, r.kb, p, a.scale_log2);
+                }
+                if constexpr (kTiled) load_v(nx);
+                else wave_lds_sync();   // PV reads finish before the next run's V overwrites the tile
+                if (!have) break;
+                r = nx;
+            }
+        }
+    } else {
+        // int8 cache: one fold per (32-key chunk, row), the chunk's codes
+        // staged and converted in LDS.  A chunk: half hh of the block of the
+        // run opened by entry k (wave-uniform values); p_max: the largest
+        // position among its rows.
+        struct Chunk {
+            int kb, k, end, p_max;
+            int64_t tok;      // token of the chunk's first key
+        };
+        auto chunk_at = [&](int k, int hh) -> Chunk {
+            Chunk c;
+            c.k = k;
+            c.end = group_end(k);
+            c.kb = (__builtin_amdgcn_readlane(e_key, k) >> 2) * kBlock + 32 * hh;
+            c.tok = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(e_hi, k) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane(e_lo, k)) + 32 * hh;
+            int pm = __builtin_amdgcn_readlane(e_p, k);
+            for (int j = k + 1; j < c.end; ++j) pm = max(pm, __builtin_amdgcn_readlane(e_p, j));
+            c.p_max = pm;
+            return c;
+        };
+        int k = 0, half = 0;
+        auto next_chunk = [&](Chunk &c) -> bool {   // advances (k, half) to the next chunk some row sees
+            for (;;) {
+                if (half == 0) {
+                    half = 1;
+                } else {
+                    half = 0;
+                    k = group_end(k);
+                    if (k >= n_ent) return false;
+                }
+                c = chunk_at(k, half);
+                if (c.kb <= c.p_max) return true;
+            }
+        };
+        auto load = [&](ChunkRegs8 &r, const Chunk &c) {
+            const int64_t off = c.tok * a.kv_tok + (int64_t)g * a.kv_head;
+            const int64_t soff = c.tok * a.s_tok + (int64_t)g * a.s_head;
+            load_chunk8(r, a.k8 + off, a.v8 + off, a.ks + soff, a.vs + soff, a.kv_tok, a.s_tok, c.p_max - c.kb);
+        };
+        // Fold one loaded chunk into every row of its run that sees it (keys
+        // past a row's own position are masked in its fold).
+        auto fold = [&](ChunkRegs8 &r, const Chunk &c) {
+            u32x4 ka8[2][4];
+            stage_v8(r, vt, sct);
+            k_operands8(r, ka8);
+            wave_lds_sync();
+            for (int j = c.k; j < c.end; ++j) {
+                const int row = __builtin_amdgcn_readlane(e_key, j) & 3;
+                const int p = __builtin_amdgcn_readlane(e_p, j);
+                if (c.kb > p) continue;
+                u32x4 qb[4];
+                read_q<true>(qb, qt + row * kQTileBytes);
+                fold_rows<RW, true>(st, row, qb, ka8, c.kb, p, a.scale_log2, vt, sct);
+            }
+            wave_lds_sync();   // reads finish before the next chunk overwrites the tiles
+        };
+        // The prefetch is unconditional (past the last chunk it re-reads the
+        // chunk being folded), so every path through the loop has the same
+        // loads in flight and a fold waits only for its own chunk.
+        Chunk c0 = chunk_at(0, 0), c1;      // an entry's first half is always visible
+        ChunkRegs8 ca, cb;
+        if (n_ent > 0) load(ca, c0);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) store_q_tile(qt + i * kQTileBytes, qv[i]);
+        wave_lds_sync();   // q tiles written before the first fold reads them
+        if (n_ent > 0) {
+            for (;;) {
+                const bool have1 = next_chunk(c1);
+                if (!have1) c1 = c0;
+                load(cb, c1);
+                fold(ca, c0);
+                if (!have1) break;
+                const bool have0 = next_chunk(c0);
+                if (!have0) c0 = c1;
+                load(ca, c0);
+                fold(cb, c1);
+                if (!have0) break;
+            }
         }
     }
 
@@ -744,7 +1002,9 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
 // in the order of their 64-row windows), one per wave.
 template <int RW, bool KV8, bool kTiled>
 __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled ? 16 : 8192];
+    // V tile per wave: a block's two 32-key halves (strided bf16), one chunk
+    // (int8), none (tiled: V^T operands come straight from the cache)
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled ? 16 : KV8 ? 8192 : 16384];
     __shared__ __attribute__((aligned(16))) uint8_t qt_all[4][RW * kQTileBytes];
     __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
     const int wave = uniform(threadIdx.x >> 6);
