@@ -620,10 +620,11 @@ def main():
     ap.add_argument("--ik-layout", choices=("token-major", "head-major"), default="token-major",
                     help="the index-key cache: [tokens, heads, 64] (token-major) or [heads, tokens, 64] "
                          "(head-major, passed as a strided [tokens, heads, 64] view)")
-    ap.add_argument("--overlap", choices=("indexer", "free", "none"), default="indexer",
+    ap.add_argument("--overlap", choices=("indexer", "attention", "free", "none"), default="indexer",
                     help="the long row's calls: on a second stream starting when the chunk's cache write of "
-                         "each step is done (indexer, the default: beside the chunk's indexer and selection), on "
-                         "a free-running second stream (free), or after the chunk's on one stream (none)")
+                         "each step is done (indexer, the default: beside the chunk's indexer and selection), "
+                         "when the chunk's selection is done (attention: beside the chunk attention), on a "
+                         "free-running second stream (free), or after the chunk's on one stream (none)")
     ap.add_argument("--separate-write", action="store_true",
                     help="decode workloads: write the new keys with their own launch "
                          "(msa_pack_kv_tiled_rows / msa_pack_kv_tiled) instead of inside the selection's "
@@ -685,12 +686,15 @@ def main():
         --overlap indexer: the long row's calls start once the chunk's cache
         write is done, beside the chunk's indexer and selection."""
         chunk_calls = wl["chunk"].calls(i)
-        if side is not None and args.overlap == "indexer":
-            head = [c for c in chunk_calls if c[0] == "write_cache"]
-            run_calls("chunk", head, timed)
-            chunk_calls = [c for c in chunk_calls if c[0] != "write_cache"]
+        if side is not None and args.overlap in ("indexer", "attention"):
+            # the chunk's calls before the long row's start: its cache write
+            # (indexer), or everything before its attention (attention)
+            n_head = (int(chunk_calls[0][0] == "write_cache") if args.overlap == "indexer"
+                      else len(chunk_calls) - 1)
+            run_calls("chunk", chunk_calls[:n_head], timed)
+            chunk_calls = chunk_calls[n_head:]
             mk = marks[i % len(marks)]
-            mk.record()                  # after the chunk's cache write
+            mk.record()
             side.wait_event(mk)
         with torch.cuda.stream(side) if side is not None else contextlib.nullcontext():
             run_calls("long", wl["long"].calls(i), timed)
@@ -773,6 +777,8 @@ def main():
                             f"steps, on its launch stream; algorithmic work of one launch over that mean"),
         "streams": {"none": "one: the long row's calls after the chunk's",
                     "free": "two (default priority): the long row's calls on a free-running second stream",
+                    "attention": "two (default priority): each step's long row on a second stream, starting "
+                                 "when the chunk's selection of the same step is done (beside its attention)",
                     "indexer": "two (default priority): each step's long row on a second stream, starting when "
                                "the chunk's cache write of the same step is done (beside its indexer and "
                                "selection)"}[args.overlap],
