@@ -112,41 +112,8 @@ __device__ __forceinline__ void read_q(u32x4 (&qb)[4], const uint8_t *qt) {
     for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const u32x4 *>(src + (kBlocked ? 16 : 64) * s);
 }
 
-// Registers of one 32-key chunk: K as MFMA A operands (key kbase + 16*mt +
-// lane%16, dims 32*s + 8*(lane/16): the interleaved layout) and V pieces (keys kbase + 4*(lane/8) +
-// kk, 16-byte units lane%8 and lane%8 + 8).  A key past p is read from key p
-// instead (always in bounds): its score is masked to -inf, so its weight is 0.
-struct ChunkRegs {
-    u32x4 ka[2][4];
-    u32x4 vr[4][2];
-};
-
-// Addressing: the chunk's first key is a wave-uniform base; each lane adds a
-// 32-bit byte offset (a chunk spans 32 tokens, so offsets stay small).
-__device__ __forceinline__ void load_chunk(ChunkRegs &c, const uint16_t *kseq, const uint16_t *vseq,
-                                           int64_t tok, int kbase, int p) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-    const int last = p - kbase;                       // keys past it read key p instead
-    const uint32_t tok_bytes = (uint32_t)tok * 2u;
-    const char *kb = reinterpret_cast<const char *>(kseq + (int64_t)kbase * tok);
-    const char *vb = reinterpret_cast<const char *>(vseq + (int64_t)kbase * tok);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const uint32_t off = (uint32_t)min(16 * mt + lr, last) * tok_bytes + 16u * lg;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) c.ka[mt][s] = *reinterpret_cast<const u32x4 *>(kb + off + 64 * s);
-    }
-    const int kg = lane >> 3, dc = lane & 7;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t off = (uint32_t)min(4 * kg + kk, last) * tok_bytes + 16u * dc;
-        c.vr[kk][0] = *reinterpret_cast<const u32x4 *>(vb + off);
-        c.vr[kk][1] = *reinterpret_cast<const u32x4 *>(vb + off + 128);
-    }
-}
-
-// Write 32 keys' V rows (load_chunk's vr, here flattened: v[2*kk + hf]) into
-// an 8 KiB LDS tile.
+// Write 32 keys' V rows into an 8 KiB LDS tile: v[2*kk + hf] holds key
+// 4*(lane/8) + kk, 16-byte unit lane%8 + 8*hf (load_block_v's half).
 __device__ __forceinline__ void stage_v_rows(const u32x4 (&v)[8], uint8_t *vt) {
     const int lane = threadIdx.x & 63;
     const int kg = lane >> 3, dc = lane & 7;
@@ -156,50 +123,6 @@ __device__ __forceinline__ void stage_v_rows(const u32x4 (&v)[8], uint8_t *vt) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
             *reinterpret_cast<u32x4 *>(vt + key * 256 + 16 * v_unit(key, dc + 8 * hf)) = v[2 * kk + hf];
-    }
-}
-
-// Write one loaded chunk's V rows into this wave's 8 KiB LDS tile.
-__device__ __forceinline__ void stage_v(const ChunkRegs &c, uint8_t *vt) {
-    stage_v_rows(*reinterpret_cast<const u32x4(*)[8]>(&c.vr[0][0]), vt);
-}
-
-// Registers of one 32-key chunk from a tiled cache (kt, vt: the chunk's 4,096
-// elements of its block's K and V tiles).  The K tile holds the 8 operands
-// ka[mt][s] in order and the V tile the 8 V^T operands of fold_rows' PV
-// product (d-tile dt in vr[dt / 2][dt % 2]), each as 64 lane-ordered 16-byte
-// pieces, so every load reads 1 KiB of contiguous memory.  Keys past the
-// chunk's largest visible key offset may never have been written: their scores
-// are masked in fold_rows, and their V elements are cleared by
-// clear_tail_v_tiled before the fold (their weight is 0, but 0 times an
-// unwritten NaN would not be) -- at fold time, so that the prefetch of a chunk
-// never waits for its own loads.
-__device__ __forceinline__ void load_chunk_tiled(ChunkRegs &c, const uint16_t *kt, const uint16_t *vt) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) c.ka[mt][s] = load16(kt + 8 * ((4 * mt + s) * kWave + lane));
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) c.vr[dt >> 1][dt & 1] = load16(vt + 8 * (dt * kWave + lane));
-}
-
-// Clear the V elements of keys past `last` (the chunk's largest visible key
-// offset) in a tiled chunk's registers.
-__device__ __forceinline__ void clear_tail_v_tiled(ChunkRegs &c, int last) {
-    const int lane = threadIdx.x & 63, lg = lane >> 4;
-    if (last < 31) {
-        // dword w of a V^T operand: keys k0 (low half) and k0 + 1 (high half)
-        uint32_t m[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int k0 = (w < 2 ? 4 * lg : 16 + 4 * lg) + 2 * (w & 1);
-            m[w] = (k0 <= last ? 0x0000ffffu : 0u) | (k0 + 1 <= last ? 0xffff0000u : 0u);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) c.vr[dt >> 1][dt & 1][w] &= m[w];
     }
 }
 
@@ -275,16 +198,15 @@ __device__ __forceinline__ void stage_v8(const ChunkRegs8 &c, uint8_t *vt, float
 // (wave-uniform) of a group of RW rows' states: K operands from registers,
 // V^T from the LDS tile (already staged and synced).  The scores and softmax
 // run once, with the row's max and sum picked by selects; only the rare
-// rescale and the 8 PV MFMAs sit under a branch on the row.
+// rescale and the 8 PV MFMAs sit under a branch on the row.  (The int8 cache's
+// fold; the bf16 caches fold whole blocks, softmax_pv_block below.)
 // KV8 (int8 cache): every key's score is scaled by its key scale and every
 // weight by its value scale before the PV product (the sum of weights is
 // unscaled), with the scales from the wave's scale tile `sct`.
-// kVR (tiled cache): the V^T operands come ready from registers (vr, as
-// load_chunk_tiled leaves them) instead of the LDS tile.
-template <int RW, bool KV8, bool kVR = false>
+template <int RW, bool KV8>
 __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x4 (&qb)[4],
                                           const u32x4 (&ka)[2][4], int kbase, int p, float scale_log2,
-                                          const uint8_t *vt, const float *sct, const u32x4 (*vr)[2] = nullptr) {
+                                          const uint8_t *vt, const float *sct) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
     floatx4 sacc[2];
 #pragma unroll
@@ -376,19 +298,14 @@ __device__ __forceinline__ void fold_rows(Softmax (&st)[RW], int row, const u32x
     // (and key + 16); the swizzle only flips address bits 5..7, so the piece
     // for d-tile dt sits at the dt = 0 offset XOR (dt << 5).
     u32x4 va[8];
-    if constexpr (kVR) {
+    const int vkey = 4 * lg + (lr >> 2);
+    const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) va[dt] = vr[dt >> 1][dt & 1];
-    } else {
-        const int vkey = 4 * lg + (lr >> 2);
-        const int rd0 = vkey * 256 + 8 * (lr & 3) + 32 * (vkey & 7);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const int rd = rd0 ^ (dt << 5);
-            const uint2 lo = lds_read_tr16(vt + rd);
-            const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
-            va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+    for (int dt = 0; dt < 8; ++dt) {
+        const int rd = rd0 ^ (dt << 5);
+        const uint2 lo = lds_read_tr16(vt + rd);
+        const uint2 hi = lds_read_tr16(vt + rd + 16 * 256);
+        va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i)
@@ -541,9 +458,36 @@ __device__ __forceinline__ void clear_tail_v_half(u32x4 (&v)[8], int last) {
     }
 }
 
+// K operands and V^T operands of a block from a tiled cache (kt, vt: the
+// block's 8,192-element K and V tiles of one key head; 32-key half h at
+// 4096 * h).  A half's K tile holds its 8 QK^T A operands (key tile mt, k-step
+// s) in order and its V tile the 8 V^T operands of the PV product (d-tile dt),
+// each as 64 lane-ordered 16-byte pieces, so every load reads 1 KiB of
+// contiguous memory.  Keys past the block's largest position may never have
+// been written: their scores are masked and their V elements cleared
+// (clear_tail_v_half) before the PV products, at fold time, so that a
+// prefetch never waits for its own loads.
+__device__ __forceinline__ void load_block_k_tiled(u32x4 (&ka)[4][4], const uint16_t *kt) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ka[2 * h + mt][s] = load16(kt + 4096 * h + 8 * ((4 * mt + s) * kWave + lane));
+}
+
+__device__ __forceinline__ void load_block_v_tiled(u32x4 (&v)[2][8], const uint16_t *vt) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) v[h][dt] = load16(vt + 4096 * h + 8 * (dt * kWave + lane));
+}
+
 // K operands of a block from a strided cache (kblk: its first key; tok:
 // elements between consecutive keys): tile mt holds keys 16*mt + lane%16,
-// dims 32*s + 8*(lane/16) (load_chunk's interleaved layout).  Keys past `last`
+// dims 32*s + 8*(lane/16) (the interleaved layout q's operands share).  Keys past `last`
 // (the block's largest visible key offset, 0..63) read key `last` instead, so
 // every read stays inside the keys that exist.
 __device__ __forceinline__ void load_block_k(u32x4 (&ka)[4][4], const uint16_t *kblk, int64_t tok, int last) {
@@ -558,9 +502,9 @@ __device__ __forceinline__ void load_block_k(u32x4 (&ka)[4][4], const uint16_t *
     }
 }
 
-// V rows of a block from a strided cache, half h in v[h] as load_chunk's vr
-// (keys 32*h + 4*(lane/8) + kk in v[h][2*kk + 0/1], 16-byte units lane%8 and
-// lane%8 + 8); keys past `last` read key `last`.
+// V rows of a block from a strided cache, half h in v[h] (keys 32*h +
+// 4*(lane/8) + kk in v[h][2*kk + 0/1], 16-byte units lane%8 and lane%8 + 8:
+// stage_v_rows' input); keys past `last` read key `last`.
 __device__ __forceinline__ void load_block_v(u32x4 (&v)[2][8], const uint16_t *vblk, int64_t tok, int last) {
     const int lane = threadIdx.x & 63, kg = lane >> 3, dc = lane & 7;
     const uint32_t tok_bytes = (uint32_t)tok * 2u;
@@ -575,23 +519,8 @@ __device__ __forceinline__ void load_block_v(u32x4 (&v)[2][8], const uint16_t *v
         }
 }
 
-// Fold one loaded 32-key chunk into a single state st (stage V, fold,
+// Fold one loaded int8 chunk into a single state st (stage and convert V, fold,
 // release the tile).
-__device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
-                                           int kbase, int p, float scale_log2, uint8_t *vt, float *) {
-    stage_v(c, vt);
-    wave_lds_sync();
-    fold_rows<1, false>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, c.ka, kbase, p, scale_log2, vt, nullptr);
-    wave_lds_sync();   // reads finish before the next chunk overwrites the tile
-}
-
-// The same from a tiled cache's registers (no V tile, no LDS).
-__device__ __forceinline__ void fold_chunk_tiled(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs &c,
-                                                 int kbase, int p, float scale_log2) {
-    fold_rows<1, false, true>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, qb, c.ka, kbase, p, scale_log2, nullptr,
-                              nullptr, c.vr);
-}
-
 __device__ __forceinline__ void fold_chunk(Softmax &st, const u32x4 (&qb)[4], const ChunkRegs8 &c,
                                            int kbase, int p, float scale_log2, uint8_t *vt, float *sct) {
     stage_v8(c, vt, sct);
@@ -835,28 +764,17 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
             return r;
         };
         u32x4 kreg[4][4];   // K operands of the block's 4 key tiles
-        u32x4 vreg[2][8];   // V of each 32-key half: tiled, its 8 V^T operands; strided, its rows (load_chunk's vr)
+        u32x4 vreg[2][8];   // V of each 32-key half: tiled, its 8 V^T operands; strided, its rows (load_block_v)
         auto load_k = [&](const Run &r) {
             if constexpr (kTiled) {
-                const uint16_t *kt = a.k + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            kreg[2 * h + mt][s] = load16(kt + 4096 * h + 8 * ((4 * mt + s) * kWave + lane));
+                load_block_k_tiled(kreg, a.k + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head);
             } else {
                 load_block_k(kreg, a.k + r.tok * a.kv_tok + (int64_t)g * a.kv_head, a.kv_tok, r.p_max - r.kb);
             }
         };
         auto load_v = [&](const Run &r) {
             if constexpr (kTiled) {
-                const uint16_t *vtl = a.v + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) vreg[h][dt] = load16(vtl + 4096 * h + 8 * (dt * kWave + lane));
+                load_block_v_tiled(vreg, a.v + (r.tok >> 6) * a.kv_tok + (int64_t)g * a.kv_head);
             } else {
                 load_block_v(vreg, a.v + r.tok * a.kv_tok + (int64_t)g * a.kv_head, a.kv_tok, r.p_max - r.kb);
             }
@@ -1032,17 +950,30 @@ __device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit 
     const int kb0 = b * kBlock, kb1 = kb0 + 32;
     if (b < 0 || kb0 > u.p) return;
     const int64_t t0 = block_token0(a.b, u.s, kv0, b);     // the block's first key
-    if constexpr (kTiled) {   // the tile of block t0 / 64
-        const int64_t off = (t0 >> 6) * a.kv_tok + (int64_t)u.g * a.kv_head;
-        ChunkRegs ca, cb;
-        load_chunk_tiled(ca, a.k + off, a.v + off);
-        if (kb1 <= u.p) load_chunk_tiled(cb, a.k + off + 4096, a.v + off + 4096);
-        clear_tail_v_tiled(ca, u.p - kb0);
-        fold_chunk_tiled(st, qb, ca, kb0, u.p, a.scale_log2);
-        if (kb1 <= u.p) {
-            clear_tail_v_tiled(cb, u.p - kb1);
-            fold_chunk_tiled(st, qb, cb, kb1, u.p, a.scale_log2);
+    if constexpr (!KV8) {
+        // bf16 caches: the block's 64 keys in one fold, as the prefill walk
+        // folds a block (so decode and prefill share the fold's arithmetic)
+        u32x4 kreg[4][4], vreg[2][8];
+        const int last = min(u.p - kb0, 63);    // the block's largest visible key offset
+        if constexpr (kTiled) {   // the tile of block t0 / 64 (whole: its keys past p are masked / cleared)
+            const int64_t off = (t0 >> 6) * a.kv_tok + (int64_t)u.g * a.kv_head;
+            load_block_k_tiled(kreg, a.k + off);
+            load_block_v_tiled(vreg, a.v + off);
+            clear_tail_v_half(vreg[0], last);
+            clear_tail_v_half(vreg[1], last - 32);
+        } else {
+            const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
+            load_block_k(kreg, a.k + off, a.kv_tok, last);
+            load_block_v(vreg, a.v + off, a.kv_tok, last);
+            stage_v_rows(vreg[0], vt);
+            stage_v_rows(vreg[1], vt + 8192);
+            wave_lds_sync();
         }
+        floatx4 sacc[4];
+        qk_block(sacc, qb, kreg);
+        softmax_pv_block<1, kTiled>(*reinterpret_cast<Softmax(*)[1]>(&st), 0, sacc, vreg, vt, kb0, u.p,
+                                    a.scale_log2);
+        if constexpr (!kTiled) wave_lds_sync();   // reads finish before the tile is reused
         return;
     }
     const int64_t off = t0 * a.kv_tok + (int64_t)u.g * a.kv_head;
@@ -1055,13 +986,6 @@ __device__ __forceinline__ void decode_fold_block(const AttnArgs &a, const Unit 
             load_chunk8(cb, a.k8 + off1, a.v8 + off1, a.ks + soff1, a.vs + soff1, a.kv_tok, a.s_tok, u.p - kb1);
         fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt, sct);
         if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt, sct);
-    } else {
-        const uint16_t *kblk = a.k + off, *vblk = a.v + off;
-        ChunkRegs ca, cb;
-        load_chunk(ca, kblk, vblk, a.kv_tok, 0, u.p - kb0);
-        if (kb1 <= u.p) load_chunk(cb, kblk, vblk, a.kv_tok, 32, u.p - kb0);
-        fold_chunk(st, qb, ca, kb0, u.p, a.scale_log2, vt, nullptr);
-        if (kb1 <= u.p) fold_chunk(st, qb, cb, kb1, u.p, a.scale_log2, vt, nullptr);
     }
 }
 
@@ -1082,9 +1006,9 @@ __device__ __forceinline__ void decode_stash(const Softmax &st, float *wm, float
 // The partial of the 4 stashed states w0..w0+3 (slot order) for head h, dims
 // d0..d0+N-1.  Empty states (no visible key, or no slot) have max -inf and
 // weight 0.
-template <int N>
+template <int N, int kTileBytes>
 __device__ __forceinline__ void combine_group(const float (*wm)[16], const float (*wl)[16],
-                                              const uint8_t (*vt)[8192], int w0, int h, int d0, float &M,
+                                              const uint8_t (*vt)[kTileBytes], int w0, int h, int d0, float &M,
                                               float &Ls, float (&acc)[N]) {
     M = fmaxf(fmaxf(wm[w0][h], wm[w0 + 1][h]), fmaxf(wm[w0 + 2][h], wm[w0 + 3][h]));
     Ls = 0.f;
@@ -1139,7 +1063,9 @@ __device__ __forceinline__ void decode_write(const AttnArgs &a, const Unit &u, i
 // last to arrive (a per-unit counter) merges them.
 template <bool KV8, bool kTiled>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit) {
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][8192];
+    // per wave: a block's V (strided bf16: both halves), a chunk's (int8), or
+    // only the combine's stash (tiled)
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled || KV8 ? 8192 : 16384];
     __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
     __shared__ float wm[4][16], wl[4][16];
     __shared__ int is_last;
@@ -1248,7 +1174,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
 template <bool KV8, bool kTiled>
 __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
     constexpr int kW = 8;
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[kW][8192];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[kW][kTiled || KV8 ? 8192 : 16384];
     __shared__ __attribute__((aligned(16))) float sc_all[kW][KV8 ? 64 : 4];
     __shared__ float wm[kW][16], wl[kW][16];
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
