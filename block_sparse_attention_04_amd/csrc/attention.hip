@@ -467,22 +467,28 @@ __device__ __forceinline__ void clear_tail_v_half(u32x4 (&v)[8], int last) {
 // been written: their scores are masked and their V elements cleared
 // (clear_tail_v_half) before the PV products, at fold time, so that a
 // prefetch never waits for its own loads.
+// Addressing: each load's 1 KiB piece has a wave-uniform base and every load
+// shares one per-lane byte offset, 16 * lane.
+__device__ __forceinline__ u32x4 load_tile_piece(const uint16_t *piece, uint32_t lane_bytes) {
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(piece) + lane_bytes);
+}
+
 __device__ __forceinline__ void load_block_k_tiled(u32x4 (&ka)[4][4], const uint16_t *kt) {
-    const int lane = threadIdx.x & 63;
+    const uint32_t lb = 16u * (uint32_t)(threadIdx.x & 63);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ka[2 * h + mt][s] = load16(kt + 4096 * h + 8 * ((4 * mt + s) * kWave + lane));
+            for (int s = 0; s < 4; ++s) ka[2 * h + mt][s] = load_tile_piece(kt + 4096 * h + 512 * (4 * mt + s), lb);
 }
 
 __device__ __forceinline__ void load_block_v_tiled(u32x4 (&v)[2][8], const uint16_t *vt) {
-    const int lane = threadIdx.x & 63;
+    const uint32_t lb = 16u * (uint32_t)(threadIdx.x & 63);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) v[h][dt] = load16(vt + 4096 * h + 8 * (dt * kWave + lane));
+        for (int dt = 0; dt < 8; ++dt) v[h][dt] = load_tile_piece(vt + 4096 * h + 512 * dt, lb);
 }
 
 // K operands of a block from a strided cache (kblk: its first key; tok:
