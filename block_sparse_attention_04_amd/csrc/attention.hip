@@ -6,21 +6,22 @@
 // The 16 query heads of a key head share the row's selection, so a wave holds
 // all 16 heads of one (row, key head) and reads every kept key/value once for
 // all of them (TensorFold pull request 1388, commit on 4,096-row prompt
-// chunks).  Decode splits the kept keys into partials of 32-key pieces merged
-// by a log-sum-exp combine (same pull request, commit adding the minimax_m3
-// family).
+// chunks).  Decode splits the kept keys into partials merged by a log-sum-exp
+// combine (same pull request, commit adding the minimax_m3 family, which cuts
+// them in 32-key pieces; here a partial covers 4 kept blocks).
 //
-// Per 32-key chunk, on v_mfma_f32_16x16x32_bf16:
-//   S^T[key][head] = K Q^T      2 key tiles x 4 k-steps over the 128 dims
-//   O^T[d][head]  += V^T P^T    8 d-tiles x one 32-key k-step
-// With S^T, a lane holds one head's scores for 8 keys, which is exactly the
-// P^T operand layout of the second product, so probabilities go from the
+// Per kept 64-key block (bf16 caches), on v_mfma_f32_16x16x32_bf16:
+//   S^T[key][head] = K Q^T      4 key tiles x 4 k-steps over the 128 dims
+//   O^T[d][head]  += V^T P^T    8 d-tiles x two 32-key k-steps
+// (the int8 cache folds 32-key chunks: 2 key tiles, one k-step).  With S^T, a
+// lane holds one head's scores for 4 keys of each key tile, which is exactly
+// the P^T operand layout of the second product, so probabilities go from the
 // softmax straight into the MFMA without leaving registers, and the running
-// max / sum / rescale of a head stay inside its 4 lanes.  V is written to LDS
-// row-major (one 256-byte row per key, 32-byte column blocks XOR-swizzled by
-// key mod 8) and each V^T operand is gathered by two transposing LDS reads
-// (ds_read_b64_tr_b16), with no repacking in registers.
-// Softmax runs in base 2 on scale*log2(e)-prescaled scores.
+// max / sum / rescale of a head stay inside its 4 lanes.  A strided cache's V
+// is written to LDS row-major (one 256-byte row per key, 32-byte column blocks
+// XOR-swizzled by key mod 8) and each V^T operand is gathered by two
+// transposing LDS reads (ds_read_b64_tr_b16); a tiled cache stores the
+// operands ready.  Softmax runs in base 2 on scale*log2(e)-prescaled scores.
 #include <type_traits>
 
 #include "msa_device.h"
@@ -130,7 +131,8 @@ __device__ __forceinline__ void stage_v_rows(const u32x4 (&v)[8], uint8_t *vt) {
 // 16*mt + lane%16, dims 32*(lane/16) + 16*h .. +15), V codes (key kbase +
 // 4*(lane/8) + kk, dims 8*(lane%8 + 8*hf) .. +7) and one scale per lane:
 // lanes 0..31 the key scale of key kbase + lane, lanes 32..63 the value scale
-// of key kbase + lane - 32.  Keys past p read key p, as in load_chunk.
+// of key kbase + lane - 32.  Keys past p read key p instead (always in
+// bounds): their scores are masked, so their weights are 0.
 struct ChunkRegs8 {
     u32x4 ka[2][2];
     uint2 vr[4][2];
@@ -566,8 +568,8 @@ __device__ __forceinline__ Unit make_unit(const AttnArgs &a, int64_t unit) {
 // group_rows below).  For each row it holds the 16 query heads (so every
 // kept block is fetched once for the whole group) and an online-softmax state.  The
 // rows' kept blocks are merged into one list sorted by block index and walked
-// 32 keys at a time, the next chunk's K/V loads in flight while the current
-// one is folded.  A block kept by several of the rows (their shared local
+// one block at a time (32-key chunks with the int8 cache), the next block's
+// K/V loads in flight while the current one is folded.  A block kept by several of the rows (their shared local
 // block, or any block on correlated rows) is loaded once and folded into each
 // of them.  Each row still sees its own blocks in ascending order, so its bits
 // depend only on its blocks.  Walking the merged
