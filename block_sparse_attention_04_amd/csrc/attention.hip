@@ -1179,6 +1179,19 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int wg_per_unit
 // own; after each pass the workgroup forms that pass's two partials, kept in
 // registers, and merges all partials at the end.  Nothing leaves the CU until
 // the output, and the arithmetic is decode_kernel's, step for step.
+// Workgroups are dispatched to the chip's 8 XCDs in turn (workgroup i to XCD
+// i mod 8), each XCD with its own L2.  Workgroup i takes unit base(i mod 8) +
+// i / 8, so every XCD gets one contiguous run of units -- consecutive rows of
+// one key head, which in a verify window keep mostly the same blocks, so their
+// K/V is fetched into one L2 rather than into all eight.  A bijection of
+// [0, n): the first n mod 8 XCDs take one unit more.  A unit's result does not
+// depend on which workgroup computes it.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_unit(int64_t i, int64_t n) {
+    const int64_t q = n / kXcds, r = n % kXcds, x = i % kXcds, k = i / kXcds;
+    return x * q + min(x, r) + k;
+}
+
 template <bool KV8, bool kTiled>
 __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
     constexpr int kW = 8;
@@ -1186,8 +1199,9 @@ __global__ __launch_bounds__(512) void decode_unit_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float sc_all[kW][KV8 ? 64 : 4];
     __shared__ float wm[kW][16], wl[kW][16];
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int64_t unit = blockIdx.x;
-    if (unit >= (int64_t)a.b.total_rows * a.H) return;
+    const int64_t n_units = (int64_t)a.b.total_rows * a.H;
+    if ((int64_t)blockIdx.x >= n_units) return;
+    const int64_t unit = xcd_unit(blockIdx.x, n_units);
     const Unit u = make_unit(a, unit);
     const int hq = a.H * kGroup;
     const int64_t kv0 = seq_token0(a.b, u.s);
