@@ -342,3 +342,29 @@ def test_prefill_row_grouping(name):
     o_ref, l_ref = oracle.attention(case, sel.cpu().numpy())
     check_out(o_s.cpu(), o_ref, f"{name}/all rows")
     check_lse(l_s.cpu(), l_ref, f"{name}/all rows")
+
+
+@pytest.mark.gpu
+def test_decode_unit_order_ragged():
+    """100 (row, key head) units (not a multiple of the 8 XCDs) take the
+    one-workgroup-per-unit decode, whose workgroups pick units in an
+    XCD-aware order: every unit must be computed once and equal the same
+    rows run a sequence at a time (the split kernel), bit for bit, and pass
+    the oracle checks."""
+    case = make_case("dk_ragged", [9000, 5000, 700], [9, 9, 7], 4, seed=190)
+    assert case.total_rows * case.n_kv_heads == 100
+    full_check(case, "decode")
+    t = device_tensors(case)
+    shape = shape_of(case)
+    big = msa.run_path(shape, msa.Batch(case.seq_lens, case.rows), t, "decode")
+    for s in range(case.n_seqs):
+        r0, r1 = case.cu_rows[s], case.cu_rows[s + 1]
+        k0, L = case.kv_start[s], case.seq_lens[s]
+        sub = {"q": t["q"][r0:r1].contiguous(), "iq": t["iq"][r0:r1].contiguous(),
+               "k": t["k"][k0:k0 + L].contiguous(), "v": t["v"][k0:k0 + L].contiguous(),
+               "ik": t["ik"][k0:k0 + L].contiguous()}
+        one = msa.run_path(shape, msa.Batch([L], [r1 - r0]), sub, "decode")
+        torch.cuda.synchronize()
+        assert torch.equal(big["block_idx"][r0:r1], one["block_idx"]), s
+        assert torch.equal(big["out"][r0:r1], one["out"]), s
+        assert torch.equal(big["lse"][r0:r1], one["lse"]), s
