@@ -730,7 +730,10 @@ __device__ __forceinline__ void window_select_tail(const float *scores, const fl
 // batch's own keys into the tiled cache, one (row, key head) per wave
 // (msa_index_select_pack_rows): nothing in this launch reads the tiles, and
 // the attention that does comes after it on the stream.
-template <bool kSelect>
+// kDeep: a wave requests all 4 of its blocks at once (4 register sets), for
+// launches small enough that every workgroup is resident together: its walk
+// then waits for one round trip to memory instead of three.
+template <bool kSelect, bool kDeep>
 __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTail t, PackRowsArgs pk,
                                                            int x_index) {
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -782,16 +785,29 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
                 const int bq = b_begin + min(q, nblk - 1);
                 window_load_block(av, ik_g, block_token0(a.b, s, kv0, bq), a.ik_tok, bq, L, lr);
             };
-            u32x4 ra[4][2], rb[4][2];
-            ld(0, ra);
-            ld(1, rb);
-            static_assert(kWindowBlocks == 4, "the two-set ring below covers four blocks");
-            const float m0 = window_lane_max(ra, bq0, bq1, b_begin, prow, p_first);
-            ld(2, ra);
-            const float m1 = window_lane_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
-            ld(3, rb);
-            const float m2 = window_lane_max(ra, bq0, bq1, b_begin + 2, prow, p_first);
-            const float m3 = window_lane_max(rb, bq0, bq1, b_begin + 3, prow, p_first);
+            static_assert(kWindowBlocks == 4, "the register sets below cover four blocks");
+            float m0, m1, m2, m3;
+            if constexpr (kDeep) {
+                u32x4 ra[4][2], rb[4][2], rc[4][2], rd[4][2];
+                ld(0, ra);
+                ld(1, rb);
+                ld(2, rc);
+                ld(3, rd);
+                m0 = window_lane_max(ra, bq0, bq1, b_begin, prow, p_first);
+                m1 = window_lane_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
+                m2 = window_lane_max(rc, bq0, bq1, b_begin + 2, prow, p_first);
+                m3 = window_lane_max(rd, bq0, bq1, b_begin + 3, prow, p_first);
+            } else {
+                u32x4 ra[4][2], rb[4][2];
+                ld(0, ra);
+                ld(1, rb);
+                m0 = window_lane_max(ra, bq0, bq1, b_begin, prow, p_first);
+                ld(2, ra);
+                m1 = window_lane_max(rb, bq0, bq1, b_begin + 1, prow, p_first);
+                ld(3, rb);
+                m2 = window_lane_max(ra, bq0, bq1, b_begin + 2, prow, p_first);
+                m3 = window_lane_max(rb, bq0, bq1, b_begin + 3, prow, p_first);
+            }
             // lane group lg ends with block b_begin + lg (past the visible
             // blocks: a re-read, discarded)
             const float v = max_scatter_lane_groups(m0, m1, m2, m3);
@@ -848,6 +864,11 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
 // index_scores_window's grid: with heads in fours, a workgroup per (4-block
 // key range, group of 4 heads); else per (16-block range, head).  With a
 // batch writer `pk`, one more column per 4 (row, key head) units.
+// The deep variant while the index workgroups fit the chip at once: 3 per
+// compute unit at its register use, 256 compute units.
+constexpr int64_t kDeepWindowWgs = 3 * 256;
+static bool window_deep(int x_index, int n_seqs) { return (int64_t)x_index * n_seqs <= kDeepWindowWgs; }
+
 static dim3 window_grid(const IndexArgs &a, const PackRowsArgs *pk, int *x_index) {
     int x = 0;
     if (a.H % 4 == 0) {
@@ -866,8 +887,12 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st, const PackRow
     if (a.b.max_rows <= 16) {
         int x_index = 0;
         const dim3 grid = window_grid(a, pk, &x_index);
-        hipLaunchKernelGGL(index_scores_window<false>, grid, dim3(256), 0, st, a, SelectTail{},
-                           pk ? *pk : PackRowsArgs{}, x_index);
+        if (window_deep(x_index, a.b.n_seqs))
+            hipLaunchKernelGGL((index_scores_window<false, true>), grid, dim3(256), 0, st, a, SelectTail{},
+                               pk ? *pk : PackRowsArgs{}, x_index);
+        else
+            hipLaunchKernelGGL((index_scores_window<false, false>), grid, dim3(256), 0, st, a, SelectTail{},
+                               pk ? *pk : PackRowsArgs{}, x_index);
     } else {
         constexpr int NT = 4;
         const int rows_wg = 16 * NT * kTiledWaves;
@@ -904,7 +929,12 @@ hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, h
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st, const PackRowsArgs *pk) {
     int x_index = 0;
     const dim3 grid = window_grid(a, pk, &x_index);
-    hipLaunchKernelGGL(index_scores_window<true>, grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{}, x_index);
+    if (window_deep(x_index, a.b.n_seqs))
+        hipLaunchKernelGGL((index_scores_window<true, true>), grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{},
+                           x_index);
+    else
+        hipLaunchKernelGGL((index_scores_window<true, false>), grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{},
+                           x_index);
     return hipGetLastError();
 }
 
