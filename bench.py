@@ -18,9 +18,9 @@ value = rows per second of the headline step (4,097 rows).  Inputs are
 resident in HBM before timing; the timed region enqueues K steps back to
 back, bracketed by a device synchronisation on both sides.  Inputs rotate
 over replicas so the 256 MB Infinity Cache cannot hold a step's working set.
-The long row's calls run on a second stream, each step's starting when the
-chunk's part of the same step starts (beside the chunk's cache write,
-indexer and selection, not its attention).
+A second stream runs each step's chunk cache write and then the long row's
+calls, beside the chunk's indexer and selection; the chunk attention waits
+for the write and runs alone.
 
 Per configuration (`configs`): each of the five named workloads (2,048-row
 prefill, batched decode, the chunk, the long row, the verify windows) alone,
@@ -620,11 +620,13 @@ def main():
     ap.add_argument("--ik-layout", choices=("token-major", "head-major"), default="token-major",
                     help="the index-key cache: [tokens, heads, 64] (token-major) or [heads, tokens, 64] "
                          "(head-major, passed as a strided [tokens, heads, 64] view)")
-    ap.add_argument("--overlap", choices=("indexer", "attention", "free", "none"), default="indexer",
-                    help="the long row's calls: on a second stream starting when the chunk's cache write of "
-                         "each step is done (indexer, the default: beside the chunk's indexer and selection), "
-                         "when the chunk's selection is done (attention: beside the chunk attention), on a "
-                         "free-running second stream (free), or after the chunk's on one stream (none)")
+    ap.add_argument("--overlap", choices=("write", "indexer", "attention", "free", "none"), default="write",
+                    help="the long row's calls: on a second stream after the chunk's cache write (write, "
+                         "the default: the write and the long row beside the chunk's indexer and selection; "
+                         "the chunk attention waits for the write), on a second stream starting when the "
+                         "chunk's cache write on the first stream is done (indexer), when the chunk's "
+                         "selection is done (attention: beside the chunk attention), on a free-running second "
+                         "stream (free), or after the chunk's on one stream (none)")
     ap.add_argument("--separate-write", action="store_true",
                     help="decode workloads: write the new keys with their own launch "
                          "(msa_pack_kv_tiled_rows / msa_pack_kv_tiled) instead of inside the selection's "
@@ -671,6 +673,7 @@ def main():
     timer = Timed(torch)
     bracket = set()
     marks = [torch.cuda.Event() for _ in range(8)]
+    write_marks = [torch.cuda.Event() for _ in range(8)]
 
     def run_calls(name, calls, timed):
         for kname, fn in calls:
@@ -686,6 +689,22 @@ def main():
         --overlap indexer: the long row's calls start once the chunk's cache
         write is done, beside the chunk's indexer and selection."""
         chunk_calls = wl["chunk"].calls(i)
+        if side is not None and args.overlap == "write" and chunk_calls[0][0] == "write_cache":
+            # second stream: the chunk's cache write, then the long row, once
+            # everything enqueued before this step on the first stream is
+            # done (a replica's tiles are rewritten only after the attention
+            # that read them); the chunk attention waits for the write
+            mk, wk = marks[i % len(marks)], write_marks[i % len(write_marks)]
+            mk.record()
+            side.wait_event(mk)
+            with torch.cuda.stream(side):
+                run_calls("chunk", chunk_calls[:1], timed)
+                wk.record()
+                run_calls("long", wl["long"].calls(i), timed)
+            run_calls("chunk", chunk_calls[1:-1], timed)
+            torch.cuda.current_stream().wait_event(wk)
+            run_calls("chunk", chunk_calls[-1:], timed)
+            return
         if side is not None and args.overlap in ("indexer", "attention"):
             # the chunk's calls before the long row's start: its cache write
             # (indexer), or everything before its attention (attention)
@@ -776,6 +795,9 @@ def main():
         "roofline_timing": (f"{dominant}: HIP event pair around each of its launches in the {args.steps} timed "
                             f"steps, on its launch stream; algorithmic work of one launch over that mean"),
         "streams": {"none": "one: the long row's calls after the chunk's",
+                    "write": "two (default priority): each step's chunk cache write and then its long row on a "
+                             "second stream, beside the chunk's indexer and selection; the chunk attention "
+                             "waits for the write",
                     "free": "two (default priority): the long row's calls on a free-running second stream",
                     "attention": "two (default priority): each step's long row on a second stream, starting "
                                  "when the chunk's selection of the same step is done (beside its attention)",
