@@ -647,7 +647,7 @@ def main():
         args.kv_layout = "strided"   # their own layouts of the strided cache
     tiled = args.kv_layout == "tiled"
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(sharding by key head is described in the design notes)", file=sys.stderr)
         sys.exit(2)
 

@@ -80,7 +80,7 @@ extern "C" {
 typedef enum msa_status {
     MSA_OK = 0,
     MSA_ERR_INVALID = -1,      /* null pointer, negative size, inconsistent sizes */
-    MSA_ERR_UNSUPPORTED = -2,  /* a shape this build has no kernel for */
+    MSA_ERR_UNSUPPORTED = -2,  /* a shape the library has no kernel for */
     MSA_ERR_WORKSPACE = -3,    /* decode workspace missing or too small */
     MSA_ERR_HIP = -4           /* HIP runtime error (no device, launch failure) */
 } msa_status;
