@@ -599,12 +599,35 @@ __device__ __forceinline__ float window_lane_max(const u32x4 (&av)[4][2], u32x4 
 // score T: the top_k-1 largest range maxima belong to distinct ranges, each
 // holding a candidate at least that large.  Every candidate >= T then lies in
 // a range whose maximum is >= T0, so only those ranges' scores are read
-// (usually top_k-1 of them, at most 64 here), in ascending block order, and
-// the top top_k-1 among them -- ties to the lower block -- are the selection.
-// More than 64 such ranges (mass ties) take an exact search over every
-// candidate score instead, streamed from memory.
+// (usually top_k-1 of them, at most 64 here).  Among their blocks only those
+// >= T0 can be kept (at least top_k-1 blocks reach T0): they are listed in
+// ascending block order, one per lane, and each one's rank -- the keys above
+// it, plus equal keys earlier in the list -- decides it: kept if the rank is
+// below top_k-1, which is the top top_k-1 with ties to the lower block.  More
+// than 64 candidate ranges, or more than 64 blocks at or above T0 (mass
+// ties), take an exact search over every candidate score instead, streamed
+// from memory.
+struct WindowTailLds {
+    int32_t cr[2 * kWave];    // candidate ranges; [kWave, 2 kWave): per-lane discard slots
+    uint2 kb[2 * kWave];      // blocks >= T0: (order key, block); discard slots as above
+};
+
+// Exclusive prefix over the lanes of cnt (0 <= cnt < 2^kBits), and the total.
+template <int kBits>
+__device__ __forceinline__ int lane_prefix(int cnt, int &total) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < kBits; ++bit) {
+        const uint64_t bm = __ballot((cnt >> bit) & 1);
+        pre += lanes_below(bm) << bit;
+        tot += (int)__popcll(bm) << bit;
+    }
+    total = tot;
+    return pre;
+}
+
 __device__ __forceinline__ void window_select_tail(const float *scores, const float *wmax, int n, int top_k,
-                                                   int32_t *out, int32_t *cr) {
+                                                   int32_t *out, WindowTailLds &sh) {
     const int lane = threadIdx.x & 63;
     const int nb = n + 1, need = top_k - 1;
     if (nb <= top_k || need == 0) {
@@ -631,7 +654,8 @@ __device__ __forceinline__ void window_select_tail(const float *scores, const fl
             if (w0 + lane + kWave * j < nw) lmax = max(lmax, order_key(x[j]));
     }
     const uint32_t t0 = kth_largest_wave<16>(lmax, need);
-    // pass 2: the ranges with a maximum >= T0, in ascending order
+    // pass 2: the ranges with a maximum >= T0 into cr[0, c) in ascending
+    // order: the 16 masks first, then each one's place from the running count
     int c = 0;
     for (int w0 = 0; w0 < nw; w0 += 16 * kWave) {
         float x[16];
@@ -642,59 +666,58 @@ __device__ __forceinline__ void window_select_tail(const float *scores, const fl
 #pragma unroll
             for (int j = 0; j < 16; ++j) x[j] = ld(wmax + min(w0 + lane + kWave * j, nw - 1));
         }
+        uint64_t bm[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bm[j] = __ballot(w0 + lane + kWave * j < nw && order_key(x[j]) >= t0);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int w = w0 + lane + kWave * j;
-            const bool f = w < nw && order_key(x[j]) >= t0;
-            const uint64_t mk = __ballot(f);
-            const int pos = c + lanes_below(mk);
-            if (f && pos < kWave) cr[pos] = w;
-            c += __popcll(mk);
+            const bool f = (bm[j] >> lane) & 1ull;
+            const int pos = c + lanes_below(bm[j]);
+            sh.cr[f && pos < kWave ? pos : kWave + lane] = w0 + lane + kWave * j;
+            c += (int)__popcll(bm[j]);
         }
     }
+    bool done = false;   // wave-uniform
     if (c <= kWave) {
         wave_lds_sync();
-        // lane l: the 4 blocks of candidate range l (keys 0 past the candidates)
-        const int w = lane < c ? cr[lane] : 0;
+        // lane l: the 4 blocks of candidate range l; those >= T0 into kb[0, m)
+        const int w = lane < c ? sh.cr[lane] : 0;
         float sv[kWindowBlocks];
 #pragma unroll
         for (int j = 0; j < kWindowBlocks; ++j) sv[j] = ld(scores + min(kWindowBlocks * w + j, n - 1));
-        uint32_t v[kWindowBlocks];
-#pragma unroll
-        for (int j = 0; j < kWindowBlocks; ++j) v[j] = lane < c && kWindowBlocks * w + j < n ? order_key(sv[j]) : 0u;
-        // T: the need-th largest key (the candidates hold >= need real keys)
-        uint32_t t = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cb = t | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < kWindowBlocks; ++j) cnt += __popcll(__ballot(v[j] >= cb));
-            t = cnt >= need ? cb : t;
-        }
-        int gt = 0;
-#pragma unroll
-        for (int j = 0; j < kWindowBlocks; ++j) gt += __popcll(__ballot(v[j] > t));
-        const int need_eq = need - gt;
-        // index order is lane-major here (range l's blocks come before range l+1's)
-        int eq_before = 0;
-#pragma unroll
-        for (int j = 0; j < kWindowBlocks; ++j) eq_before += lanes_below(__ballot(v[j] == t));
-        bool take[kWindowBlocks];
-        int within = 0;
-#pragma unroll
-        for (int j = 0; j < kWindowBlocks; ++j) {
-            const bool eq = v[j] == t;
-            take[j] = v[j] > t || (eq && eq_before + within < need_eq);
-            within += eq ? 1 : 0;
-        }
-        int pos = 0;
-#pragma unroll
-        for (int j = 0; j < kWindowBlocks; ++j) pos += lanes_below(__ballot(take[j]));
+        uint32_t fb = 0u;
 #pragma unroll
         for (int j = 0; j < kWindowBlocks; ++j)
-            if (take[j]) out[pos++] = kWindowBlocks * w + j;
-    } else {
-        // exact fallback: bitwise search for T over every candidate score
+            fb |= (lane < c && kWindowBlocks * w + j < n && order_key(sv[j]) >= t0 ? 1u : 0u) << j;
+        int m;
+        int pos = lane_prefix<3>(__popc(fb), m);
+#pragma unroll
+        for (int j = 0; j < kWindowBlocks; ++j) {
+            const bool f = (fb >> j) & 1u;
+            sh.kb[f && pos < kWave ? pos : kWave + lane] =
+                make_uint2(order_key(sv[j]), (uint32_t)(kWindowBlocks * w + j));
+            pos += f ? 1 : 0;
+        }
+        if (m <= kWave) {
+            wave_lds_sync();
+            // lane l: block l of the list (ascending blocks) and its rank:
+            // the keys above it, and equal keys earlier in the list
+            const uint2 me = lane < m ? sh.kb[lane] : make_uint2(0u, 0u);
+            int rank = 0;
+            for (int i = 0; i < m; ++i) {
+                const uint32_t k = (uint32_t)__builtin_amdgcn_readlane((int)me.x, i);
+                rank += k > me.x || (k == me.x && i < lane) ? 1 : 0;
+            }
+            const bool take = lane < m && rank < need;
+            const uint64_t tm = __ballot(take);
+            if (take) out[lanes_below(tm)] = (int32_t)me.y;
+            done = true;
+        }
+    }
+    if (!done) {
+        // exact fallback (more than 64 candidate ranges, or more than 64
+        // blocks at or above T0: ties): bitwise search for T over every
+        // candidate score, then one pass in block order
         uint32_t t = 0u;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cb = t | (1u << bit);
@@ -839,7 +862,7 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         // agent-scope loads (sc1: not served from a copy in its own L2).  The
         // language's model orders none of this; an agent-scope release fence
         // would, but writes back the whole L2 in each of the many workgroups.
-        __shared__ int32_t cr_all[4][kWave];
+        __shared__ WindowTailLds tail_lds[4];
         __shared__ int is_last;
         const int unit = s * n_groups + (heads_wg ? g0 / 4 : g0);   // (sequence, head group)
         __builtin_amdgcn_s_waitcnt(0);
@@ -857,7 +880,7 @@ __global__ __launch_bounds__(256) void index_scores_window(IndexArgs a, SelectTa
         const int gs = heads_wg ? g0 + wave : g0;
         const int64_t u = (int64_t)row0 * a.H + gs;
         window_select_tail(a.scores + u * a.bs_stride, t.wmax + ((int64_t)s * a.H + gs) * t.ranges, p_first / kBlock,
-                           t.top_k, t.idx + u * t.top_k, cr_all[wave]);
+                           t.top_k, t.idx + u * t.top_k, tail_lds[wave]);
     }
 }
 
