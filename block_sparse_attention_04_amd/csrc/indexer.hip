@@ -700,15 +700,9 @@ __device__ __forceinline__ void window_select_tail(const float *scores, const fl
         }
         if (m <= kWave) {
             wave_lds_sync();
-            // lane l: block l of the list (ascending blocks) and its rank:
-            // the keys above it, and equal keys earlier in the list
+            // lane l: block l of the list (ascending blocks)
             const uint2 me = lane < m ? sh.kb[lane] : make_uint2(0u, 0u);
-            int rank = 0;
-            for (int i = 0; i < m; ++i) {
-                const uint32_t k = (uint32_t)__builtin_amdgcn_readlane((int)me.x, i);
-                rank += k > me.x || (k == me.x && i < lane) ? 1 : 0;
-            }
-            const bool take = lane < m && rank < need;
+            const bool take = top_keep(me.x, m, need);
             const uint64_t tm = __ballot(take);
             if (take) out[lanes_below(tm)] = (int32_t)me.y;
             done = true;
