@@ -15,13 +15,14 @@
 //   1. T0 = the (top_k-1)-th largest of the 64 per-lane maxima, decided on
 //      their top 16 bits -- a lower bound on T, since top_k-1 lanes hold a
 //      value >= T0;
-//   2. the candidates >= T0 (usually a few dozen) are compacted into LDS and
-//      T is found among them by a 32-step bitwise search over one key per
-//      lane; if more than 64 candidates tie above T0, the same search runs
-//      over all scores instead;
-//   3. one pass in ascending block order keeps every key > T and the first
-//      (lowest-index) keys == T until top_k-1 are kept; the local block
-//      closes the list.
+//   2. the candidates >= T0 (usually a few dozen) are compacted into LDS, one
+//      key per lane in block order; up to 16 of them are kept by their rank
+//      (keys above, plus equal keys earlier in the list), more by a 32-step
+//      bitwise search for T and then every key > T and the first
+//      (lowest-index) keys == T; if more than 64 candidates tie above T0, the
+//      search runs over all scores instead;
+//   3. the kept blocks are written in ascending block order until top_k-1 are
+//      kept; the local block closes the list.
 #include "msa_launch.h"
 #include "msa_select.h"
 
