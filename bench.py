@@ -670,6 +670,11 @@ def main():
     torch.cuda.synchronize()
 
     side = None if args.overlap == "none" else torch.cuda.Stream()
+    # --overlap write moves the chunk's cache write to the second stream; a
+    # chunk that writes nothing (strided cache, packed paged pool) starts its
+    # long row with the step instead (the indexer placement)
+    overlap = ("indexer" if args.overlap == "write" and "write_cache" not in wl["chunk"].steps
+               else args.overlap)
     timer = Timed(torch)
     bracket = set()
     marks = [torch.cuda.Event() for _ in range(8)]
@@ -686,10 +691,12 @@ def main():
     def step(i, timed):
         """One headline step: the long row (second stream unless --overlap
         none) and the chunk; `timed`: bracket the calls named in `bracket`.
-        --overlap indexer: the long row's calls start once the chunk's cache
-        write is done, beside the chunk's indexer and selection."""
+        --overlap write (the default): the chunk's cache write and then the
+        long row on the second stream, beside the chunk's indexer and
+        selection; indexer: the long row's calls start once the chunk's cache
+        write on the first stream is done."""
         chunk_calls = wl["chunk"].calls(i)
-        if side is not None and args.overlap == "write" and chunk_calls[0][0] == "write_cache":
+        if side is not None and overlap == "write":
             # second stream: the chunk's cache write, then the long row, once
             # everything enqueued before this step on the first stream is
             # done (a replica's tiles are rewritten only after the attention
@@ -705,10 +712,10 @@ def main():
             torch.cuda.current_stream().wait_event(wk)
             run_calls("chunk", chunk_calls[-1:], timed)
             return
-        if side is not None and args.overlap in ("indexer", "attention"):
+        if side is not None and overlap in ("indexer", "attention"):
             # the chunk's calls before the long row's start: its cache write
             # (indexer), or everything before its attention (attention)
-            n_head = (int(chunk_calls[0][0] == "write_cache") if args.overlap == "indexer"
+            n_head = (int(chunk_calls[0][0] == "write_cache") if overlap == "indexer"
                       else len(chunk_calls) - 1)
             run_calls("chunk", chunk_calls[:n_head], timed)
             chunk_calls = chunk_calls[n_head:]
@@ -803,7 +810,7 @@ def main():
                                  "when the chunk's selection of the same step is done (beside its attention)",
                     "indexer": "two (default priority): each step's long row on a second stream, starting when "
                                "the chunk's cache write of the same step is done (beside its indexer and "
-                               "selection)"}[args.overlap],
+                               "selection)"}[overlap],
     }
     print(f"[bench] headline {ms_step:.4f} ms/step ({res['value'] / 1e6:.3f} M rows/s)", file=sys.stderr,
           flush=True)
