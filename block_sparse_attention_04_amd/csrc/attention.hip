@@ -931,17 +931,34 @@ __device__ __forceinline__ void prefill_group(const AttnArgs &a, int g, int r0, 
 }
 
 // Groups are enumerated head-major (consecutive groups: groups of one key head,
-// in the order of their 64-row windows), one per wave.
-template <int RW, bool KV8, bool kTiled>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int groups_per_head) {
+// in the order of their 64-row windows), one per wave.  kW waves per
+// workgroup: 4 for the 4-row walk, whose four waves start together and keep
+// their walks in step (L2 hits: one-wave workgroups took the chunk attention
+// from ~375 to ~390-420 us); 1 for the shorter walks of small batches, where a
+// SIMD then starts its next group as soon as its wave ends instead of waiting
+// for the slowest of four (the 2,048-row prefill 50.4 -> 46.3 us a step).
+// Workgroups go to the 8 XCDs in turn, so with one wave each, workgroup j
+// takes group 32 (j / 32) + 4 (j % 8) + (j / 8) % 4: each XCD keeps the same
+// 4 consecutive groups of every 32 as with four-wave workgroups (in a last
+// partial 32, group j).
+__device__ __forceinline__ int64_t prefill_group_of(int64_t j, int64_t n) {
+    const int64_t base = j & ~int64_t(31);
+    if (base + 32 > n) return j;
+    return base + 4 * (j & 7) + ((j >> 3) & 3);
+}
+
+template <int RW, bool KV8, bool kTiled, int kW>
+__global__ __launch_bounds__(64 * kW) void prefill_kernel(AttnArgs a, int groups_per_head) {
     // V tile per wave: a block's two 32-key halves (strided bf16), one chunk
     // (int8), none (tiled: V^T operands come straight from the cache)
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[4][kTiled ? 16 : KV8 ? 8192 : 16384];
-    __shared__ __attribute__((aligned(16))) uint8_t qt_all[4][RW * kQTileBytes];
-    __shared__ __attribute__((aligned(16))) float sc_all[4][KV8 ? 64 : 4];
-    const int wave = uniform(threadIdx.x >> 6);
-    const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
-    if (grp >= (int64_t)groups_per_head * a.H) return;
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[kW][kTiled ? 16 : KV8 ? 8192 : 16384];
+    __shared__ __attribute__((aligned(16))) uint8_t qt_all[kW][RW * kQTileBytes];
+    __shared__ __attribute__((aligned(16))) float sc_all[kW][KV8 ? 64 : 4];
+    const int wave = kW == 1 ? 0 : uniform(threadIdx.x >> 6);
+    const int64_t n = (int64_t)groups_per_head * a.H;
+    const int64_t j = (int64_t)blockIdx.x * kW + wave;
+    if (j >= n) return;
+    const int64_t grp = kW == 1 ? prefill_group_of(j, n) : j;
     const int g = (int)(grp / groups_per_head);
     const int r0 = (int)(grp % groups_per_head) * RW;
     prefill_group<RW, KV8, kTiled>(a, g, r0, vt_all[wave], qt_all[wave], sc_all[wave]);
@@ -1263,8 +1280,9 @@ template <int RW, bool KV8, bool kTiled>
 static void launch_prefill_rw(const AttnArgs &a, hipStream_t st) {
     const int gph = (a.b.total_rows + RW - 1) / RW;
     const int64_t waves = (int64_t)gph * a.H;
-    hipLaunchKernelGGL((prefill_kernel<RW, KV8, kTiled>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a,
-                       gph);
+    constexpr int kW = RW == 4 ? 4 : 1;   // waves per workgroup
+    hipLaunchKernelGGL((prefill_kernel<RW, KV8, kTiled, kW>), dim3((unsigned)((waves + kW - 1) / kW)), dim3(64 * kW),
+                       0, st, a, gph);
 }
 
 template <bool KV8, bool kTiled>
