@@ -601,12 +601,11 @@ __device__ __forceinline__ float window_lane_max(const u32x4 (&av)[4][2], u32x4 
 // a range whose maximum is >= T0, so only those ranges' scores are read
 // (usually top_k-1 of them, at most 64 here).  Among their blocks only those
 // >= T0 can be kept (at least top_k-1 blocks reach T0): they are listed in
-// ascending block order, one per lane, and each one's rank -- the keys above
-// it, plus equal keys earlier in the list -- decides it: kept if the rank is
-// below top_k-1, which is the top top_k-1 with ties to the lower block.  More
-// than 64 candidate ranges, or more than 64 blocks at or above T0 (mass
-// ties), take an exact search over every candidate score instead, streamed
-// from memory.
+// ascending block order, one per lane, and top_keep keeps the top top_k-1 of
+// the list with ties to the lower block (by rank for short lists, by a
+// bitwise search for the cut otherwise).  More than 64 candidate ranges, or
+// more than 64 blocks at or above T0 (mass ties), take an exact search over
+// every candidate score instead, streamed from memory.
 struct WindowTailLds {
     int32_t cr[2 * kWave];    // candidate ranges; [kWave, 2 kWave): per-lane discard slots
     uint2 kb[2 * kWave];      // blocks >= T0: (order key, block); discard slots as above
