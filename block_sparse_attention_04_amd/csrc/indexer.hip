@@ -942,15 +942,18 @@ hipError_t launch_index_select_chunk(const IndexArgs &a, const ChunkSelect &c, h
     return hipGetLastError();
 }
 
+// The fused one-row selection always takes the deep variant: beside a
+// prompt chunk's indexer (the chunk's workgroups leave no room for a scan
+// wave on their SIMDs, so the scan takes compute units as they free up) a
+// workgroup that waits for one round trip instead of three holds its unit
+// for less time (262,144-key row beside the chunk: step 564.0 -> 562.6 us;
+// alone 41.3 -> 41.2 us).  The scores-only launch keeps the residency rule
+// (verify windows: 62.1 us, 63.4 us with the deep variant).
 hipError_t launch_index_select(const IndexArgs &a, SelectTail t, hipStream_t st, const PackRowsArgs *pk) {
     int x_index = 0;
     const dim3 grid = window_grid(a, pk, &x_index);
-    if (window_deep(x_index, a.b.n_seqs))
-        hipLaunchKernelGGL((index_scores_window<true, true>), grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{},
-                           x_index);
-    else
-        hipLaunchKernelGGL((index_scores_window<true, false>), grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{},
-                           x_index);
+    hipLaunchKernelGGL((index_scores_window<true, true>), grid, dim3(256), 0, st, a, t, pk ? *pk : PackRowsArgs{},
+                       x_index);
     return hipGetLastError();
 }
 
