@@ -220,6 +220,9 @@ def quantiles(xs):
     return at(0.1), at(0.5), at(0.9)
 
 
+SMALL_PROMPT_UNITS = 4096   # prompt steps up to this many (row, key head) units carry their cache write
+
+
 class Workload:
     """One named workload on the device: input replicas (rotated so the
     Infinity Cache cannot hold a step's working set), the tiled cache of each
@@ -262,12 +265,16 @@ class Workload:
         self.new_keys = [(k0 + L - n, k0 + L) for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows)]
         self.o = msa.run_path(self.shape, self.batch, self.inputs[0], mode, fused=fused,
                               kv8=self.inputs[0].get("kv8"), kvt=self.inputs[0].get("kvt"))
-        # decode steps: the new keys' write rides in the selection's launch
-        # (msa_index_select_pack_rows) unless fold_write is off.  Prompt
+        # The new keys' write rides in the selection's first launch
+        # (msa_index_select_pack_rows) unless fold_write is off: for decode
+        # steps, and for prompt steps of at most SMALL_PROMPT_UNITS (row, key
+        # head) units, whose indexer leaves the chip partly idle (the 2,048-row
+        # prefill's is 256 workgroups: 46.4 -> 42.9 us a step).  Larger prompt
         # chunks write their token range with msa_pack_kv_tiled: beside a
         # chip-filling indexer the carried writer measured slower (headline
         # step 679-680 against 675-676 us)
-        self.fold = self.write and fold_write and mode == "decode"
+        small_prompt = mode == "prefill" and case.total_rows * case.n_kv_heads <= SMALL_PROMPT_UNITS
+        self.fold = self.write and fold_write and (mode == "decode" or small_prompt)
         if self.fold:
             self.steps = ("write_index_select" if fused else "write_index_scores_select", "attention")
             if "select_workspace" not in self.o:

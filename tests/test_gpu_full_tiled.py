@@ -1,10 +1,10 @@
 """The benchmarked path at full size: the five named workloads through exactly
 the calls the benchmark times over the tiled bf16 cache -- the step's new
 keys written into the tiles (msa_pack_kv_tiled over one token range for the
-prompt chunk and the 2,048-token prefill; for decode batches the write rides
-in the selection's launch, msa_index_select_pack_rows; every other key is
-packed first and the row keys are left NaN until the step writes them), the
-selection (msa_index_scores + msa_select_blocks for prompt chunks) and
+prompt chunk; for decode batches and the 2,048-token prefill the write rides
+in the selection's first launch, msa_index_select_pack_rows; every other key
+is packed first and the row keys are left NaN until the step writes them),
+the selection (msa_index_scores + msa_select_blocks for the prompt chunk) and
 msa_prefill_tiled / msa_decode_tiled.
 
 Each is checked two ways: bit for bit against the strided cache's path on
@@ -17,6 +17,7 @@ import torch
 import block_sparse_attention_04_amd as msa
 import oracle
 from gpu_helpers import check_lse, check_out, check_scores, check_selection, device_tensors, say, shape_of
+from bench import SMALL_PROMPT_UNITS
 from test_gpu_parity import FULL_ROWS
 from workloads import config
 
@@ -30,11 +31,17 @@ def bench_calls(case, t, batch, o, kvt):
     new keys into kvt and the results into o."""
     shape = shape_of(case)
     mode = MODE[case.name]
-    if mode == "prefill":
+    if mode == "prefill" and case.total_rows * case.n_kv_heads > SMALL_PROMPT_UNITS:
         for k0, L, n in zip(case.kv_start, case.seq_lens, case.rows):   # one token range per sequence
             msa.msa_pack_kv_tiled(shape, t["k"], t["v"], kvt, k0 + L - n, k0 + L)
         msa.msa_index_scores(shape, batch, t["iq"], t["ik"], o["block_scores"])
         msa.msa_select_blocks(shape, batch, o["block_scores"], o["block_idx"])
+        msa.msa_prefill_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"])
+    elif mode == "prefill":
+        # a small prompt step: the new keys' write rides in the indexer's launch
+        ws = msa.index_select_workspace(shape, batch)
+        msa.msa_index_select_pack_rows(shape, batch, t["iq"], t["ik"], o["block_scores"], o["block_idx"],
+                                       t["k"], t["v"], kvt, ws)
         msa.msa_prefill_tiled(shape, batch, t["q"], kvt, o["block_idx"], o["out"], o["lse"])
     else:
         # the new keys' write rides in the selection's launch
